@@ -1,0 +1,350 @@
+"""Benchmark of the sparse MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+Headline workload: batch-1 decode, one token row through 40 MoE layers with
+distinct weights (H=2048, 256 experts top-8 + 1 shared, I=512, bf16; 64.7 GB
+of weights, so every layer streams from HBM).  One step = one token through
+all 40 layers, replayed from a captured HIP graph; the input row rotates
+through a pool of 64 rows.  Alongside: prefill of M=4096 tokens through one
+layer (same shapes), one step = one layer call.
+
+Inputs are seeded synthetic tensors generated on the device before timing.
+Printed: one JSON line with throughput, the dominant kernel's roofline
+position (per-launch algorithmic bytes over its event-timed duration), and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, datasheet
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, datasheet
+METRIC = "MoE-layer tokens/s: prefill M=4096 & decode M=1; % of MFMA / HBM roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--layers", type=int, default=40, help=argparse.SUPPRESS)
+    ap.add_argument("--trace-steps", type=int, default=10)
+    return ap.parse_args()
+
+
+class Hip:
+    """hipEvent helpers through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so.7")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            assert self.L.hipEventCreate(ctypes.byref(ev)) == 0
+            arr[i] = ev
+        return arr
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.L.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, rc
+        return ms.value
+
+    def destroy(self, arr):
+        for e in arr:
+            self.L.hipEventDestroy(e)
+
+
+class LayerCall:
+    """Pre-marshalled moe_layer_forward arguments for one layer."""
+
+    def __init__(self, moe, x, r, ex, sh, k, out, ws, bias=None, routing=None):
+        import torch
+        M, H = x.shape
+        E = r.shape[0]
+        I = ex.numel() // (3 * E * H)
+        Is = 0 if sh is None else sh.numel() // (3 * H)
+        self.lib = moe.lib()
+        self.desc = moe.make_desc(M, H, E, I, Is, 0, bias)
+        self.routing = moe._routing_struct(routing)
+        self.args = [ctypes.byref(self.desc), x.data_ptr(), r.data_ptr(), ex.data_ptr(),
+                     None if sh is None else sh.data_ptr(), k, out.data_ptr(), ws.data_ptr(), ws.numel(), None,
+                     None if self.routing is None else ctypes.byref(self.routing)]
+        self.torch = torch
+
+    def __call__(self, trace=None):
+        self.args[9] = self.torch.cuda.current_stream().cuda_stream
+        if trace is None:
+            st = self.lib.moe_layer_forward(*self.args)
+        else:
+            st = self.lib.moe_layer_forward_traced(*self.args, ctypes.byref(trace))
+        if st != 0:
+            raise RuntimeError(f"moe_layer_forward failed with status {st}")
+
+
+def kernel_times(hip, moe, calls_fn, n_calls_per_step, steps, kernels_per_call):
+    """Run `steps` eager steps with per-kernel events; returns {kernel name: [ms per launch]}."""
+    import torch
+    cap = steps * n_calls_per_step * kernels_per_call
+    begin, end = hip.events(cap), hip.events(cap)
+    kid = (ctypes.c_int32 * cap)()
+    tr = moe.MoeTrace(ctypes.cast(begin, ctypes.POINTER(ctypes.c_void_p)),
+                      ctypes.cast(end, ctypes.POINTER(ctypes.c_void_p)), kid, cap, 0)
+    for s in range(steps):
+        calls_fn(s, tr)
+    torch.cuda.synchronize()
+    res = {}
+    for i in range(tr.count):
+        res.setdefault(moe.KERNELS[kid[i]], []).append(hip.elapsed_ms(begin[i], end[i]))
+    hip.destroy(begin)
+    hip.destroy(end)
+    return res
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+# ------------------------------------------------------------------ decode
+
+def bench_decode(args, hip, moe, SD, S):
+    import torch
+    w = S.DECODE
+    L = args.layers
+    dev = "cuda"
+    H, E, I, k = w.H, w.E, w.I, w.k
+    t0 = time.time()
+    xpool = torch.empty(w.x_pool, H, dtype=torch.bfloat16, device=dev)
+    SD.fill(xpool, S.x_key(w, 0), 0, w.x_sigma)
+    layers = []
+    for l in range(L):
+        r = torch.empty(E, H, dtype=torch.bfloat16, device=dev)
+        SD.fill(r, S.router_key(w, l), 0, w.router_sigma)
+        ex = torch.empty(E, w.expert_elems(), dtype=torch.bfloat16, device=dev)
+        for e in range(E):
+            SD.fill(ex[e], S.expert_key(w, l, e), 0, w.w_sigma)
+        sh = torch.empty(w.shared_elems(), dtype=torch.bfloat16, device=dev)
+        SD.fill(sh, S.shared_key(w, l), 0, w.w_sigma)
+        layers.append((r, ex, sh))
+    out = torch.empty(L, H, dtype=torch.bfloat16, device=dev)
+    wsn = moe.workspace_size(1, H, E, I, w.I_shared, k)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=dev)  # layers run in stream order: one workspace
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+
+    xs = [xpool[i:i + 1] for i in range(w.x_pool)]
+    calls = [[LayerCall(moe, xs[i], r, ex, sh, k, out[l:l + 1], ws) for l, (r, ex, sh) in enumerate(layers)]
+             for i in range(w.x_pool)]
+
+    # eager reference for row 0, then one captured graph per pool row
+    for c in calls[0]:
+        c()
+    torch.cuda.synchronize()
+    eager0 = out.clone()
+    graphs = []
+    cap_stream = torch.cuda.Stream()
+    for i in range(w.x_pool):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for c in calls[i]:
+                c()
+        graphs.append(g)
+    for rep in range(3):  # replays must reproduce the eager result bit for bit
+        out.zero_()
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager0.view(torch.int16)), "graph replay differs from eager"
+
+    for s in range(args.warmup):
+        graphs[s % w.x_pool].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(args.steps):
+        graphs[s % w.x_pool].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations (eager, traced)
+    def step(s, tr):
+        for c in calls[s % w.x_pool]:
+            c(tr)
+    kt = kernel_times(hip, moe, step, L, args.trace_steps, 3)
+
+    # algorithmic bytes
+    layer_bytes = (k + 1) * w.expert_elems() * 2 + E * H * 2 + 2 * H * 2
+    gateup_bytes = k * 2 * I * H * 2 + H * 2 + E * 4 + k * I * 4
+    dom = "dec_gateup"
+    avg_ms = sum(kt[dom]) / len(kt[dom])
+    achieved = gateup_bytes / (avg_ms * 1e-3) / 1e9
+    res = dict(
+        value=1000.0 / ms, ms_per_step=ms, gen_s=gen_s,
+        layer_us=ms * 1000.0 / L,
+        layer_hbm_frac=layer_bytes * L / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        kernels_us={n: round(1000.0 * sum(v) / len(v), 3) for n, v in kt.items()},
+        roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel="k_dec_gateup",
+                      bytes_per_launch=gateup_bytes, avg_us=round(avg_ms * 1000, 3)),
+    )
+    return res, (layers, xpool)
+
+
+def cpu_decode(S, O, layers_sample=4):
+    """Oracle on a bounded sample: one token row through `layers_sample` layers."""
+    import numpy as np
+    w = S.DECODE
+    f = S.bf16_bits_to_f32
+    x = f(S.x_rows(w, 0, 1, 0))
+    t_total = 0.0
+    for l in range(layers_sample):
+        r = f(S.router_weight(w, l))
+        sh = f(S.shared_weight(w, l))
+        ids = O.topk_ids(O.selection_logits(O.router_logits(x, r)), w.k)
+        cache = {int(e): O.unpack_expert(f(S.expert_weight(w, l, int(e))), w.I, w.H) for e in ids.ravel()}
+        t = time.perf_counter()
+        O.moe_forward(x, r, lambda e: cache[e], sh, w.k, w.I)
+        t_total += time.perf_counter() - t
+    per_layer = t_total / layers_sample
+    return dict(value=1.0 / (per_layer * w.layers), unit="tok/s", cores=blas_threads(), kind="oracle",
+                sample=f"1 token row x {layers_sample} of the 40 layers (fp64 NumPy oracle; selected experts "
+                       f"regenerated outside the timing); tok/s = 1 / (mean layer time x 40)",
+                seconds=round(t_total, 3))
+
+
+# ------------------------------------------------------------------ prefill
+
+def bench_prefill(args, hip, moe, SD, S, w):
+    import torch
+    x, r, ex, sh = SD.layer_tensors(w)
+    bias = None
+    if w.zipf_s:
+        bias = torch.from_numpy(S.zipf_router_bias(w)).cuda()
+    out = torch.empty_like(x)
+    ws = torch.empty(moe.workspace_size(w.M, w.H, w.E, w.I, w.I_shared, w.k), dtype=torch.uint8, device="cuda")
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    call = LayerCall(moe, x, r, ex, sh, w.k, out, ws, bias=bias, routing={"counts": counts})
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    steps = max(10, args.steps // 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kt = kernel_times(hip, moe, lambda s, tr: call(tr), 1, args.trace_steps, 7)
+    c = counts.cpu()
+    nonempty = int((c > 0).sum())
+    M, H, E, I, k = w.M, w.H, w.E, w.I, w.k
+    layer_bytes = (nonempty + 1) * w.expert_elems() * 2 + E * H * 2 + 2 * M * H * 2
+    flops = M * (2 * H * E + (k + 1) * 3 * 2 * H * I)
+    gu_bytes = (nonempty + 1) * 2 * I * H * 2 + M * H * 2 + (M * k + M) * I * 2
+    gu_flops = (M * k + M) * 2 * I * H * 2
+    avg = sum(kt["gemm_gateup"]) / len(kt["gemm_gateup"])
+    ach = gu_bytes / (avg * 1e-3) / 1e9
+    res = dict(
+        value=M / (ms * 1e-3), unit="tok/s", ms_per_step=ms, steps=steps,
+        config=dict(workload=f"{w.name}: {w.describe()}, bf16", nonempty_experts=nonempty,
+                    max_group=int(c.max()), empty_groups=int((c == 0).sum())),
+        hbm_frac=layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        kernels_us={n: round(1000.0 * sum(v) / len(v), 2) for n, v in kt.items()},
+        roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None, kernel="k_grouped_gemm<gate/up>",
+                      bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
+                      mfma_frac=round(gu_flops / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)),
+    )
+    del x, r, ex, sh, ws
+    return res
+
+
+def cpu_prefill(S, O, w, m_sample=512):
+    """Oracle on a bounded sample: the first m_sample tokens of the workload through the layer."""
+    import concurrent.futures as cf
+    f = S.bf16_bits_to_f32
+    x = f(S.x_rows(w, 0, m_sample))
+    r = f(S.router_weight(w))
+    sh = f(S.shared_weight(w))
+    bias = S.zipf_router_bias(w)
+    ids = O.topk_ids(O.selection_logits(O.router_logits(x, r, bias)), w.k)
+    need = sorted(set(int(e) for e in ids.ravel()))
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+        blocks = dict(zip(need, ex.map(lambda e: O.unpack_expert(f(S.expert_weight(w, 0, e)), w.I, w.H), need)))
+    t = time.perf_counter()
+    O.moe_forward(x, r, lambda e: blocks[e], sh, w.k, w.I, bias=bias)
+    dt = time.perf_counter() - t
+    return dict(value=m_sample / dt, unit="tok/s", cores=blas_threads(), kind="oracle",
+                sample=f"first {m_sample} of the {w.M} tokens through the layer (fp64 NumPy oracle; "
+                       f"{len(need)} experts' weights regenerated outside the timing)",
+                seconds=round(dt, 3))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the layer's multi-GPU sharding is a design, not a build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_moe_router_amd import moe
+    from synth import device as SD
+    from synth import inputs as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    hip = Hip()
+    dec, keep = bench_decode(args, hip, moe, SD, S)
+    del keep
+    torch.cuda.empty_cache()
+    pre = bench_prefill(args, hip, moe, SD, S, S.PREFILL)
+    skew = bench_prefill(args, hip, moe, SD, S, S.SKEW)
+    cpu_d = cpu_p = None
+    if not args.no_cpu:
+        import oracle.moe_oracle as O
+        cpu_d = cpu_decode(S, O)
+        cpu_p = cpu_prefill(S, O, S.PREFILL)
+        pre["cpu_baseline"] = cpu_p
+    w = S.DECODE
+    line = {
+        "metric": METRIC, "value": round(dec["value"], 2), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dec["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; weights ~N(0,0.02), x ~N(0,1), generated on device)",
+        "config": {"workload": f"decode batch-1: 1 token row x {args.layers} MoE layers, "
+                               f"H={w.H} E={w.E} top-{w.k} + 1 shared, I={w.I}, bf16 weights "
+                               f"({args.layers * (w.E + 1) * w.expert_elems() * 2 / 1e9:.1f} GB), "
+                               f"HIP-graph replay", "layers": args.layers},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu_d,
+        "decode_layer": {"us_per_layer": round(dec["layer_us"], 3), "hbm_frac": round(dec["layer_hbm_frac"], 4),
+                         "kernels_us": dec["kernels_us"]},
+        "prefill": pre,
+        "prefill_skew": skew,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * moe_layer.h -- C ABI of the sparse mixture-of-experts FFN layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources: "Optimizing on-device inference for Apple Silicon",
+ * Perplexity 2026):
+ *   - the router scores every routed expert and each token keeps its top k,
+ *     plus one shared expert that every token passes through
+ *     (section "Qwen creates three distinct workload shapes");
+ *   - routing stays on the GPU: a histogram of assignments per expert, a
+ *     prefix scan to group offsets, a scatter into expert groups and a block
+ *     map of fixed-size row tiles for the grouped GEMM, with no host
+ *     synchronisation inside the layer (section "Keep expert routing on the
+ *     GPU");
+ *   - each expert applies two input projections with a gated activation,
+ *     then an output projection combined with its routing score and the
+ *     shared expert's result (section "Reduce intermediate and state
+ *     traffic"); products accumulate in fp32 and write bf16 (section
+ *     "Dequantize weights during matrix multiplication");
+ *   - prefill (many rows) runs as grouped matrix-matrix products, batch-1
+ *     decode as bandwidth-bound matrix-vector products over the selected
+ *     experts only (sections "Apple silicon offers different paths for
+ *     different workloads" and "Optimize the single-row weight path").
+ *
+ * Definitions fixed by this library where the pages are silent:
+ *   scores     L[t,e] = x[t] . Wr[e] (+ bias[e]), fp32;
+ *   selection  the top_k largest L[t,.], descending, equal scores -> lower
+ *              expert index first; slot j of a token holds its rank-j expert;
+ *   weights    w[t,j] = softmax over the selected scores (equal to the full
+ *              softmax probabilities renormalised over the selection);
+ *   expert     F(x) = Wd . (silu(Wg . x) * (Wu . x)), silu(z) = z*sigmoid(z);
+ *   output     out[t] = S(x[t]) + sum_j w[t,j] * F_{ids[t,j]}(x[t]), with S the
+ *              shared expert (weight 1), no capacity limit, no dropped token;
+ *   groups     assignments of one expert are stored in ascending token order.
+ *
+ * Conventions for every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library allocates nothing, keeps no state between calls and never
+ *     frees caller memory.  Pointers must be 16-byte aligned.
+ *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the default stream) and the call returns without waiting.
+ *     Buffers must stay valid until that work completes.  The library never
+ *     synchronises the stream and never launches host callbacks.
+ *   - Arguments are checked before anything is enqueued; a failed check
+ *     returns a status and enqueues nothing.  A failed launch returns
+ *     MOE_ERR_HIP (the hipError_t is available from moe_last_hip_error()).
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - Calls on distinct workspaces are independent (re-entrant); two calls
+ *     sharing one workspace must be ordered (same stream, or synchronised).
+ *
+ * Layouts (row-major, bf16 = IEEE bfloat16 bits):
+ *   x          bf16 [M][H]
+ *   router_w   bf16 [E][H]
+ *   expert_w   bf16 [E][3*I*H]; expert e = gate [I][H], up [I][H], down [H][I]
+ *   shared_w   bf16 [3*I_shared*H], same packing, or NULL when I_shared == 0
+ *   out        bf16 [M][H]; must not overlap any input
+ *   router_bias fp32 [E] or NULL
+ *
+ * Supported shapes: M >= 0 (M == 0 is a no-op returning MOE_OK),
+ * H % 64 == 0 and 64 <= H <= 16384, I % 64 == 0 and 64 <= I <= 16384,
+ * I_shared == 0 or (I_shared % 64 == 0 and I_shared <= 16384),
+ * 1 <= E <= 1024, 1 <= top_k <= min(E, 32), M * top_k < 2^31.
+ */
+#ifndef MOE_LAYER_H
+#define MOE_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,         /* null pointer, negative size, aliasing */
+  MOE_ERR_UNSUPPORTED_SHAPE = 2,   /* outside the supported shapes above */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < moe_workspace_size() */
+  MOE_ERR_MISALIGNED = 4,          /* a pointer is not 16-byte aligned */
+  MOE_ERR_HIP = 5                  /* a HIP launch failed */
+} moe_status_t;
+
+/* Path selection.  Default: the decode path when M == 1, else the grouped path. */
+#define MOE_FLAG_FORCE_GEMV 0x1u /* decode (matrix-vector) path; requires M == 1 */
+#define MOE_FLAG_FORCE_GEMM 0x2u /* grouped (matrix-matrix) path, also at M == 1 */
+
+typedef struct {
+  int64_t M;                /* token rows in this call */
+  int32_t H;                /* hidden size */
+  int32_t E;                /* routed experts */
+  int32_t I;                /* routed expert intermediate size */
+  int32_t I_shared;         /* shared expert intermediate size; 0 = no shared expert */
+  uint32_t flags;           /* MOE_FLAG_* */
+  const float* router_bias; /* device fp32 [E] added to the scores, or NULL */
+} moe_desc_t;
+
+/* Optional routing outputs (device pointers; any may be NULL = not wanted). */
+typedef struct {
+  int32_t* topk_ids; /* [M][top_k] selected experts, slot order = rank order */
+  float* topk_w;     /* [M][top_k] routing weights */
+  float* logits;     /* [M][E] fp32 router scores (bias included) */
+  int32_t* counts;   /* [E] assignments per expert (grouped path only) */
+  int32_t* offsets;  /* [E+1] exclusive prefix sum of counts (grouped path only) */
+  int32_t* perm;     /* [M*top_k] perm[p] = t*top_k + j of the assignment at group
+                        position p (grouped path only) */
+} moe_routing_t;
+
+/* Bytes of device workspace moe_layer_forward / moe_route need for this
+ * descriptor and top_k on the path the descriptor selects; 0 when the
+ * arguments are invalid.  Pure host computation. */
+size_t moe_workspace_size(const moe_desc_t* d, int top_k);
+
+/* The whole layer: out = shared expert + weighted top-k routed experts.
+ * x, router_w, expert_w, shared_w, top_k, out as documented above;
+ * workspace: device buffer of workspace_bytes >= moe_workspace_size(d, top_k),
+ * 256-byte aligned, contents undefined on entry and exit;
+ * routing: NULL, or buffers that receive the routing decisions. */
+moe_status_t moe_layer_forward(const moe_desc_t* d, const void* x, const void* router_w,
+                               const void* expert_w, const void* shared_w, int top_k, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               const moe_routing_t* routing);
+
+/* Routing only (scores, top-k, weights and, on the grouped path, the
+ * histogram / scan / scatter tables), written to `routing` (non-NULL). */
+moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w, int top_k,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       const moe_routing_t* routing);
+
+/* Kernels of the layer, as reported by moe_layer_forward_traced. */
+typedef enum {
+  MOE_K_ROUTER_SCORES = 1,     /* grouped path: router scores (MFMA) */
+  MOE_K_TOPK = 2,              /* grouped path: top-k, weights, per-chunk histograms */
+  MOE_K_ROUTE_SCAN = 3,        /* grouped path: prefix scan and block map */
+  MOE_K_ROUTE_SCATTER = 4,     /* grouped path: scatter into expert groups */
+  MOE_K_GEMM_GATEUP = 5,       /* grouped path: gate/up GEMM + gated activation */
+  MOE_K_GEMM_DOWN = 6,         /* grouped path: down GEMM */
+  MOE_K_COMBINE = 7,           /* grouped path: weighted combine + shared expert */
+  MOE_K_DEC_ROUTER_SHARED = 8, /* decode: router scores and shared expert gate/up */
+  MOE_K_DEC_GATEUP = 9,        /* decode: top-k and routed experts' gate/up */
+  MOE_K_DEC_DOWN = 10          /* decode: down projections + combine */
+} moe_kernel_t;
+
+/* Instrumentation for moe_layer_forward_traced: caller-created hipEvent_t
+ * handles (timing enabled).  Each kernel launch i of the call is bracketed by
+ * hipEventRecord(begin[count], stream) / hipEventRecord(end[count], stream)
+ * and kernel[count] = its moe_kernel_t; count advances.  Launches beyond
+ * capacity run unrecorded. */
+typedef struct {
+  void* const* begin;
+  void* const* end;
+  int32_t* kernel;
+  int32_t capacity;
+  int32_t count;
+} moe_trace_t;
+
+/* moe_layer_forward with per-kernel event records (same arguments and
+ * results; trace may be NULL, which is exactly moe_layer_forward). */
+moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const void* router_w,
+                                      const void* expert_w, const void* shared_w, int top_k,
+                                      void* out, void* workspace, size_t workspace_bytes,
+                                      void* stream, const moe_routing_t* routing,
+                                      moe_trace_t* trace);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status_t s);
+
+/* hipError_t (as int) behind the last MOE_ERR_HIP returned on this thread, 0 if none. */
+int moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_H */

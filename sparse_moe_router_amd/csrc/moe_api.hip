@@ -1,0 +1,320 @@
+// C ABI of the sparse MoE layer: argument checks, workspace plan and the
+// launch sequence on the caller's stream.  No allocation, no host
+// synchronisation, no state kept between calls.
+#include <stdint.h>
+#include <string.h>
+
+#include "moe_internal.h"
+#include "moe_layer.h"
+
+namespace moe {
+
+namespace {
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// place `bytes` at the running offset; false on overflow
+inline bool place(size_t* off, size_t* slot, uint64_t bytes) {
+  *off = align256(*off);
+  if (bytes > ((uint64_t)1 << 48)) return false;
+  *slot = *off;
+  *off += (size_t)bytes;
+  return true;
+}
+
+thread_local int g_last_hip_error = 0;
+
+moe_status_t hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return MOE_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+
+bool make_plan(Plan* p, int64_t M, int H, int E, int I, int Is, int k, bool gemv) {
+  memset(p, 0, sizeof(*p));
+  p->M = M;
+  p->H = H;
+  p->E = E;
+  p->I = I;
+  p->Is = Is;
+  p->k = k;
+  p->shared = Is > 0;
+  p->gemv = gemv;
+  p->A = M * (int64_t)k;
+  p->nchunk = (M + kChunk - 1) / kChunk;
+  p->max_tiles = (p->A + kTileM - 1) / kTileM + E + (p->shared ? (M + kTileM - 1) / kTileM : 0);
+  size_t off = 0;
+  bool ok = true;
+  if (gemv) {
+    ok &= place(&off, &p->logits, (uint64_t)E * 4);
+    ok &= place(&off, &p->ids, (uint64_t)k * 4);
+    ok &= place(&off, &p->w, (uint64_t)k * 4);
+    ok &= place(&off, &p->h_r, ((uint64_t)k * I + (uint64_t)Is) * 4);  // fp32 [k][I] then [Is]
+  } else {
+    const uint64_t A = (uint64_t)p->A;
+    ok &= place(&off, &p->logits, (uint64_t)M * E * 4);
+    ok &= place(&off, &p->ids, A * 4);
+    ok &= place(&off, &p->w, A * 4);
+    ok &= place(&off, &p->cmask, (uint64_t)p->nchunk * E * 8);
+    ok &= place(&off, &p->cbase, (uint64_t)p->nchunk * E * 4);
+    ok &= place(&off, &p->counts, (uint64_t)E * 4);
+    ok &= place(&off, &p->offsets, (uint64_t)(E + 1) * 4);
+    ok &= place(&off, &p->perm, A * 4);
+    ok &= place(&off, &p->inv, A * 4);
+    ok &= place(&off, &p->tiles, (uint64_t)p->max_tiles * sizeof(Tile));
+    ok &= place(&off, &p->ntiles, 4);
+    ok &= place(&off, &p->h_r, A * I * 2);
+    ok &= place(&off, &p->h_s, (uint64_t)M * Is * 2);
+    ok &= place(&off, &p->y_r, A * H * 2);
+    ok &= place(&off, &p->y_s, (uint64_t)M * H * 2);
+  }
+  p->total = align256(off);
+  return ok;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+// Shape / flag checks shared by every entry point.
+moe_status_t check_desc(const moe_desc_t* d, int top_k, bool* gemv) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->M < 0) return MOE_ERR_INVALID_ARG;
+  const uint32_t known = MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GEMM;
+  if (d->flags & ~known) return MOE_ERR_INVALID_ARG;
+  if ((d->flags & MOE_FLAG_FORCE_GEMV) && (d->flags & MOE_FLAG_FORCE_GEMM)) return MOE_ERR_INVALID_ARG;
+  if (d->H < 64 || d->H > 16384 || d->H % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (d->I < 64 || d->I > 16384 || d->I % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (d->I_shared < 0 || d->I_shared > 16384 || d->I_shared % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (d->E < 1 || d->E > kMaxE) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (top_k < 1 || top_k > d->E || top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (d->M * (int64_t)top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if ((d->flags & MOE_FLAG_FORCE_GEMV) && d->M != 1) return MOE_ERR_UNSUPPORTED_SHAPE;
+  *gemv = (d->flags & MOE_FLAG_FORCE_GEMV) || (d->M == 1 && !(d->flags & MOE_FLAG_FORCE_GEMM));
+  if (d->router_bias && !aligned(d->router_bias, 16)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+moe_status_t check_routing(const moe_routing_t* r) {
+  if (!r) return MOE_OK;
+  const void* ps[] = {r->topk_ids, r->topk_w, r->logits, r->counts, r->offsets, r->perm};
+  for (const void* p : ps)
+    if (p && !aligned(p, 4)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+template <class T>
+T* ws_ptr(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+// Launches one kernel through `fn`, bracketed by the trace's events when a
+// trace slot is free.
+struct Tracer {
+  moe_trace_t* t;
+  hipStream_t s;
+  template <class F>
+  hipError_t run(moe_kernel_t id, F&& fn) {
+    const bool rec = t && t->count < t->capacity;
+    hipError_t e;
+    if (rec && (e = hipEventRecord((hipEvent_t)t->begin[t->count], s)) != hipSuccess) return e;
+    if ((e = fn()) != hipSuccess) return e;
+    if (rec) {
+      if ((e = hipEventRecord((hipEvent_t)t->end[t->count], s)) != hipSuccess) return e;
+      if (t->kernel) t->kernel[t->count] = (int32_t)id;
+      t->count++;
+    }
+    return hipSuccess;
+  }
+};
+
+// Routing on the grouped path: scores, top-k, chunk masks, scan + block map, scatter.
+moe_status_t run_routing_grouped(const Plan& p, const moe_desc_t* d, const void* x, const void* wr,
+                                 void* ws, const moe_routing_t* r, hipStream_t s, Tracer& tr) {
+  float* L = (r && r->logits) ? r->logits : ws_ptr<float>(ws, p.logits);
+  int32_t* ids = (r && r->topk_ids) ? r->topk_ids : ws_ptr<int32_t>(ws, p.ids);
+  float* w = (r && r->topk_w) ? r->topk_w : ws_ptr<float>(ws, p.w);
+  int32_t* counts = (r && r->counts) ? r->counts : ws_ptr<int32_t>(ws, p.counts);
+  int32_t* offsets = (r && r->offsets) ? r->offsets : ws_ptr<int32_t>(ws, p.offsets);
+  int32_t* perm = (r && r->perm) ? r->perm : ws_ptr<int32_t>(ws, p.perm);
+  hipError_t e;
+  if ((e = tr.run(MOE_K_ROUTER_SCORES, [&] {
+         return launch_router_logits((const uint16_t*)x, (const uint16_t*)wr, d->router_bias, L, p.M, p.H,
+                                     p.E, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  if ((e = tr.run(MOE_K_TOPK, [&] {
+         return launch_topk_chunks(L, ids, w, ws_ptr<uint64_t>(ws, p.cmask), ws_ptr<int32_t>(ws, p.cbase),
+                                   p.M, p.E, p.k, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  if ((e = tr.run(MOE_K_ROUTE_SCAN, [&] {
+         return launch_route_scan(ws_ptr<int32_t>(ws, p.cbase), counts, offsets, ws_ptr<Tile>(ws, p.tiles),
+                                  ws_ptr<int32_t>(ws, p.ntiles), p.M, p.E, p.k, p.shared, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  if ((e = tr.run(MOE_K_ROUTE_SCATTER, [&] {
+         return launch_route_scatter(ids, ws_ptr<uint64_t>(ws, p.cmask), ws_ptr<int32_t>(ws, p.cbase), perm,
+                                     ws_ptr<int32_t>(ws, p.inv), p.M, p.E, p.k, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_desc_t* d, int top_k) {
+  bool gemv = false;
+  if (check_desc(d, top_k, &gemv) != MOE_OK) return 0;
+  Plan p;
+  if (!make_plan(&p, d->M, d->H, d->E, d->I, d->I_shared, top_k, gemv)) return 0;
+  return p.total;
+}
+
+moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const void* router_w,
+                                      const void* expert_w, const void* shared_w, int top_k,
+                                      void* out, void* workspace, size_t workspace_bytes,
+                                      void* stream, const moe_routing_t* routing,
+                                      moe_trace_t* trace) {
+  bool gemv = false;
+  moe_status_t st = check_desc(d, top_k, &gemv);
+  if (st != MOE_OK) return st;
+  if (!x || !router_w || !expert_w || !out) return MOE_ERR_INVALID_ARG;
+  if ((d->I_shared > 0) != (shared_w != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(expert_w, 16) || !aligned(out, 16) ||
+      (shared_w && !aligned(shared_w, 16)))
+    return MOE_ERR_MISALIGNED;
+  if ((st = check_routing(routing)) != MOE_OK) return st;
+  const size_t xbytes = (size_t)d->M * d->H * 2;
+  if (overlap(x, xbytes, out, xbytes)) return MOE_ERR_INVALID_ARG;
+  if (d->M == 0) return MOE_OK;
+  Plan p;
+  if (!make_plan(&p, d->M, d->H, d->E, d->I, d->I_shared, top_k, gemv)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return MOE_ERR_MISALIGNED;
+  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (overlap(workspace, p.total, out, xbytes) || overlap(workspace, p.total, x, xbytes))
+    return MOE_ERR_INVALID_ARG;
+
+  if (trace && (trace->capacity < 0 || trace->count < 0 ||
+                (trace->capacity > 0 && (!trace->begin || !trace->end))))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  Tracer tr{trace, s};
+  const uint16_t* xb = (const uint16_t*)x;
+  const uint16_t* ew = (const uint16_t*)expert_w;
+  const uint16_t* sw = (const uint16_t*)shared_w;
+  hipError_t e;
+  if (gemv) {
+    float* L = (routing && routing->logits) ? routing->logits : ws_ptr<float>(workspace, p.logits);
+    int32_t* ids = (routing && routing->topk_ids) ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
+    float* w = (routing && routing->topk_w) ? routing->topk_w : ws_ptr<float>(workspace, p.w);
+    float* h = ws_ptr<float>(workspace, p.h_r);
+    if ((e = tr.run(MOE_K_DEC_ROUTER_SHARED, [&] {
+           return launch_decode_router_shared(xb, (const uint16_t*)router_w, d->router_bias, sw, L,
+                                              h + (int64_t)p.k * p.I, p, s);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = tr.run(MOE_K_DEC_GATEUP, [&] { return launch_decode_gateup(xb, ew, L, ids, w, h, p, s); })) !=
+        hipSuccess)
+      return hip_fail(e);
+    if ((e = tr.run(MOE_K_DEC_DOWN, [&] { return launch_decode_down(ew, sw, ids, w, h, (uint16_t*)out, p, s); })) !=
+        hipSuccess)
+      return hip_fail(e);
+    return MOE_OK;
+  }
+  if ((st = run_routing_grouped(p, d, x, router_w, workspace, routing, s, tr)) != MOE_OK) return st;
+  const int32_t* perm = (routing && routing->perm) ? routing->perm : ws_ptr<int32_t>(workspace, p.perm);
+  const float* w = (routing && routing->topk_w) ? routing->topk_w : ws_ptr<float>(workspace, p.w);
+  uint16_t* h_r = ws_ptr<uint16_t>(workspace, p.h_r);
+  uint16_t* h_s = ws_ptr<uint16_t>(workspace, p.h_s);
+  uint16_t* y_r = ws_ptr<uint16_t>(workspace, p.y_r);
+  uint16_t* y_s = ws_ptr<uint16_t>(workspace, p.y_s);
+  const Tile* tiles = ws_ptr<Tile>(workspace, p.tiles);
+  const int32_t* ntiles = ws_ptr<int32_t>(workspace, p.ntiles);
+  if ((e = tr.run(MOE_K_GEMM_GATEUP, [&] {
+         return launch_gemm_gateup(xb, ew, sw, perm, tiles, ntiles, h_r, h_s, p, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  if ((e = tr.run(MOE_K_GEMM_DOWN, [&] {
+         return launch_gemm_down(h_r, h_s, ew, sw, tiles, ntiles, y_r, y_s, p, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  if ((e = tr.run(MOE_K_COMBINE, [&] {
+         return launch_combine(y_r, y_s, w, ws_ptr<int32_t>(workspace, p.inv), (uint16_t*)out, p, s);
+       })) != hipSuccess)
+    return hip_fail(e);
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(const moe_desc_t* d, const void* x, const void* router_w,
+                               const void* expert_w, const void* shared_w, int top_k, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               const moe_routing_t* routing) {
+  return moe_layer_forward_traced(d, x, router_w, expert_w, shared_w, top_k, out, workspace,
+                                  workspace_bytes, stream, routing, nullptr);
+}
+
+moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w, int top_k,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       const moe_routing_t* routing) {
+  bool gemv = false;
+  moe_status_t st = check_desc(d, top_k, &gemv);
+  if (st != MOE_OK) return st;
+  if (!x || !router_w || !routing) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16)) return MOE_ERR_MISALIGNED;
+  if ((st = check_routing(routing)) != MOE_OK) return st;
+  if (d->M == 0) return MOE_OK;
+  Plan p;
+  if (!make_plan(&p, d->M, d->H, d->E, d->I, d->I_shared, top_k, gemv)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return MOE_ERR_MISALIGNED;
+  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = (hipStream_t)stream;
+  if (gemv) {
+    Plan q = p;  // selection only: no shared rows, no expert rows
+    q.shared = false;
+    q.Is = 0;
+    q.I = 0;
+    float* L = routing->logits ? routing->logits : ws_ptr<float>(workspace, p.logits);
+    int32_t* ids = routing->topk_ids ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
+    float* w = routing->topk_w ? routing->topk_w : ws_ptr<float>(workspace, p.w);
+    hipError_t e;
+    if ((e = launch_decode_router_shared((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias,
+                                         nullptr, L, nullptr, q, s)) != hipSuccess)
+      return hip_fail(e);
+    if ((e = launch_decode_gateup((const uint16_t*)x, nullptr, L, ids, w, nullptr, q, s)) != hipSuccess)
+      return hip_fail(e);
+    return MOE_OK;
+  }
+  Tracer none{nullptr, s};
+  return run_routing_grouped(p, d, x, router_w, workspace, routing, s, none);
+}
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_MISALIGNED: return "misaligned pointer";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Internal declarations shared by the kernels and the C-ABI host code of the
+// sparse MoE layer library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ----------------------------------------------------------------- constants
+
+constexpr int kChunk = 64;    // tokens per routing chunk: one bit per token in a 64-bit mask
+constexpr int kTileM = 256;   // rows per grouped-GEMM tile (block-map granularity)
+constexpr int kPanel1 = 64;   // gate/up GEMM: intermediate columns per tile (x2: gate and up)
+constexpr int kMaxE = 1024;
+constexpr int kMaxTopK = 32;
+
+// ----------------------------------------------------------------- vector types
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+// ----------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ----------------------------------------------------------------- workspace plan
+
+// One tile of the block map: rows [r0, r0+rows) of group g.  pos0 is the
+// first row's index into the group-ordered row space: for a routed group it
+// is offsets[g] + r0 (a position in perm order), for the shared group (g == E)
+// it is the token index r0.
+struct Tile {
+  int32_t g, r0, rows, pos0;
+};
+
+struct Plan {
+  // shapes
+  int64_t M;
+  int32_t H, E, I, Is, k;
+  bool shared;
+  bool gemv;  // decode path
+  int64_t A;  // assignments M*k
+  int64_t nchunk;
+  int64_t max_tiles;
+  // byte offsets into the workspace (all 256-aligned)
+  size_t logits, ids, w, cmask, cbase, counts, offsets, perm, inv, tiles, ntiles, h_r, h_s, y_r, y_s;
+  size_t total;
+};
+
+// Fills `p` for the given shapes; returns false on overflow.
+bool make_plan(Plan* p, int64_t M, int H, int E, int I, int Is, int k, bool gemv);
+
+// ----------------------------------------------------------------- launchers
+// All launchers enqueue on `s` and return hipGetLastError() of the launch.
+
+// Router scores L[M][E] = x Wr^T (+ bias), fp32 (MFMA).
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, float* L,
+                                int64_t M, int H, int E, hipStream_t s);
+// Top-k + weights per token, and per-chunk expert bitmasks / counts.
+hipError_t launch_topk_chunks(const float* L, int32_t* ids, float* w, uint64_t* cmask, int32_t* cbase,
+                              int64_t M, int E, int k, hipStream_t s);
+// counts, offsets, per-chunk bases, block map.
+hipError_t launch_route_scan(int32_t* cbase, int32_t* counts, int32_t* offsets, Tile* tiles,
+                             int32_t* ntiles, int64_t M, int E, int k, bool shared, hipStream_t s);
+// perm / inv from the chunk masks and bases.
+hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const int32_t* cbase,
+                                int32_t* perm, int32_t* inv, int64_t M, int E, int k, hipStream_t s);
+// Grouped gate/up GEMM + SwiGLU -> h (bf16).
+hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
+                              const int32_t* perm, const Tile* tiles, const int32_t* ntiles,
+                              uint16_t* h_r, uint16_t* h_s, const Plan& p, hipStream_t s);
+// Grouped down GEMM -> y (bf16).
+hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
+                            const uint16_t* shared_w, const Tile* tiles, const int32_t* ntiles,
+                            uint16_t* y_r, uint16_t* y_s, const Plan& p, hipStream_t s);
+// out[t] = y_s[t] + sum_j w[t,j] y_r[inv[t*k+j]]  (bf16 out)
+hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float* w, const int32_t* inv,
+                          uint16_t* out, const Plan& p, hipStream_t s);
+
+// Decode (M == 1) path.
+hipError_t launch_decode_router_shared(const uint16_t* x, const uint16_t* wr, const float* bias,
+                                       const uint16_t* shared_w, float* logits, float* h_dec,
+                                       const Plan& p, hipStream_t s);
+hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const float* logits,
+                                int32_t* ids, float* w, float* h_dec, const Plan& p, hipStream_t s);
+hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w, const int32_t* ids,
+                              const float* w, const float* h_dec, uint16_t* out, const Plan& p,
+                              hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,323 @@
+// Routing kernels of the sparse MoE layer (gfx950, wave64).
+//
+// "Optimizing on-device inference for Apple Silicon" (Perplexity 2026),
+// section "Keep expert routing on the GPU": after each token picks its
+// experts, a histogram counts assignments per expert, a prefix scan turns
+// counts into group offsets, a scatter places assignments in their expert's
+// group and a block map lists the fixed-size tiles the grouped GEMM works
+// on, all on the device with no host round trip.
+//
+// Design for CDNA4: tokens are handled in chunks of 64, one bit per token in
+// a 64-bit mask per (chunk, expert).  The masks are built with LDS atomicOr
+// (order-independent, so deterministic), counted with popcount, and a
+// token's position inside its expert group is its chunk base plus the
+// popcount of the mask bits below it -- a stable (ascending-token) scatter
+// with no atomics on global memory.
+#include "moe_internal.h"
+#include "wave_topk.h"
+
+namespace moe {
+namespace {
+
+// ------------------------------------------------------------------ router scores
+
+// L[t][e] = sum_h x[t][h] * Wr[e][h] (+ bias[e]); fp32 accumulate on MFMA.
+// Tile 64 tokens x 64 experts, 4 waves in 2x2, each wave one 32x32 block,
+// K in steps of 64 staged through LDS (double buffered, XOR-swizzled rows).
+__global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x,
+                                                       const uint16_t* __restrict__ wr,
+                                                       const float* __restrict__ bias,
+                                                       float* __restrict__ L, int64_t M, int H,
+                                                       int E) {
+  __shared__ u32x4_t sA[2][64 * 8];
+  __shared__ u32x4_t sB[2][64 * 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int e0 = blockIdx.y * 64;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // loader: 512 16-byte chunks per operand per stage, two per thread
+  const u32x4_t* srcA[2];
+  const u32x4_t* srcB[2];
+  bool okA[2], okB[2];
+  int dst[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i, row = c >> 3, q = c & 7;
+    const int64_t t = t0 + row;
+    const int e = e0 + row;
+    okA[i] = t < M;
+    okB[i] = e < E;
+    srcA[i] = (const u32x4_t*)(x + (okA[i] ? t : 0) * (int64_t)H) + q;
+    srcB[i] = (const u32x4_t*)(wr + (int64_t)(okB[i] ? e : 0) * H) + q;
+    dst[i] = row * 8 + (q ^ (row & 7));
+  }
+  const u32x4_t zero = {0, 0, 0, 0};
+  u32x4_t ra[2], rb[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ra[i] = okA[i] ? srcA[i][k0 >> 3] : zero;
+      rb[i] = okB[i] ? srcB[i][k0 >> 3] : zero;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      sA[buf][dst[i]] = ra[i];
+      sB[buf][dst[i]] = rb[i];
+    }
+  };
+
+  f32x16_t acc = {};
+  const int arow = wm * 32 + (lane & 31), brow = wn * 32 + (lane & 31), half = lane >> 5;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int nsteps = H / 64;
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nsteps) gload((s + 1) * 64);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int q = 2 * kk + half;
+      const u32x4_t a = sA[buf][arow * 8 + (q ^ (arow & 7))];
+      const u32x4_t b = sB[buf][brow * 8 + (q ^ (brow & 7))];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                     __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+    }
+    if (s + 1 < nsteps) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  // D layout of the 32x32 block: lane -> column, register r -> row 8(r/4) + 4(lane/32) + r%4
+  const int e = e0 + wn * 32 + (lane & 31);
+  if (e < E) {
+    const float bv = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = t0 + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (t < M) L[t * E + e] = acc[r] + bv;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ top-k
+
+// One workgroup per chunk of 64 tokens, 4 waves x 16 tokens.  Writes ids and
+// weights per token, and per (chunk, expert) the token bitmask and its count.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk_chunks(const float* __restrict__ L,
+                                                     int32_t* __restrict__ ids,
+                                                     float* __restrict__ w,
+                                                     uint64_t* __restrict__ cmask,
+                                                     int32_t* __restrict__ ccount, int64_t M, int E,
+                                                     int k) {
+  __shared__ uint32_t mlo[kMaxE], mhi[kMaxE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c = blockIdx.x;
+  for (int e = tid; e < E; e += 256) mlo[e] = mhi[e] = 0;
+  __syncthreads();
+  for (int i = 0; i < 16; ++i) {
+    const int tl = wave * 16 + i;  // token within the chunk
+    const int64_t t = c * kChunk + tl;
+    if (t >= M) break;
+    uint64_t top;
+    const uint64_t mine = wave_topk<EPL>(L + t * E, E, k, lane, &top);
+    const float l0 = from_orderable((uint32_t)(top >> 32));
+    const float lj = from_orderable((uint32_t)(mine >> 32));
+    const int ej = (int)(0xFFFFFFFFu - (uint32_t)mine);
+    const float ex = lane < k ? expf(lj - l0) : 0.0f;
+    const float sum = wave_sum(ex);
+    if (lane < k) {
+      ids[t * k + lane] = ej;
+      w[t * k + lane] = ex / sum;
+      if (tl < 32)
+        atomicOr(&mlo[ej], 1u << tl);
+      else
+        atomicOr(&mhi[ej], 1u << (tl - 32));
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    const uint32_t lo = mlo[e], hi = mhi[e];
+    cmask[c * E + e] = ((uint64_t)hi << 32) | lo;
+    ccount[c * E + e] = __popc(lo) + __popc(hi);
+  }
+}
+
+// ------------------------------------------------------------------ scan + block map
+
+// Exclusive scan of one int per thread over a 1024-thread block.
+__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int wv = lane < 16 ? s_wave[lane] : 0;
+    int wi = wv;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int o = __shfl_up(wi, d, 64);
+      if (lane >= d) wi += o;
+    }
+    if (lane < 16) s_wave[16 + lane] = wi - wv;  // exclusive prefix of wave totals
+    if (lane == 15) s_wave[32] = wi;
+  }
+  __syncthreads();
+  const int r = s_wave[16 + wave] + incl - v;
+  *total = s_wave[32];
+  __syncthreads();
+  return r;
+}
+
+// Single workgroup.  cbase holds per-(chunk, expert) counts on entry and the
+// group position of the chunk's first assignment to that expert on exit.
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cbase,
+                                                     int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
+                                                     Tile* __restrict__ tiles,
+                                                     int32_t* __restrict__ ntiles, int64_t M, int E,
+                                                     int k, int shared) {
+  __shared__ int s_part[1024];
+  __shared__ int s_wave[40];
+  const int tid = threadIdx.x;
+  const int64_t nchunk = (M + kChunk - 1) / kChunk;
+  const int P = 1024 / E;  // threads per expert (E <= 1024)
+  const int e = tid % E, part = tid / E;
+  const bool active = part < P;
+  const int64_t cpp = (nchunk + P - 1) / P;
+  const int64_t c0 = active ? (int64_t)part * cpp : 0;
+  const int64_t c1 = active ? (c0 + cpp < nchunk ? c0 + cpp : nchunk) : 0;
+
+  // pass 1: partial counts per (part, expert)
+  int psum = 0;
+  for (int64_t c = c0; c < c1; ++c) psum += cbase[c * E + e];
+  s_part[tid] = active ? psum : 0;
+  __syncthreads();
+  // expert totals (thread e < E), exclusive scan over experts
+  int total = 0;
+  if (tid < E)
+    for (int p = 0; p < P; ++p) total += s_part[p * E + tid];
+  int routed_total;
+  const int off = block_exclusive_scan(tid < E ? total : 0, s_wave, &routed_total);
+  // tile counts per group, scan
+  const int nt = tid < E ? (total + kTileM - 1) / kTileM : 0;
+  int routed_tiles;
+  const int tstart = block_exclusive_scan(nt, s_wave, &routed_tiles);
+  if (tid < E) {
+    counts[tid] = total;
+    offsets[tid] = off;
+    for (int i = 0; i < nt; ++i) {
+      const int r0 = i * kTileM;
+      Tile tl;
+      tl.g = tid;
+      tl.r0 = r0;
+      tl.rows = total - r0 < kTileM ? total - r0 : kTileM;
+      tl.pos0 = off + r0;
+      tiles[tstart + i] = tl;
+    }
+  }
+  if (tid == 0) offsets[E] = routed_total;
+  // shared group after the routed tiles
+  const int nts = shared ? (int)((M + kTileM - 1) / kTileM) : 0;
+  for (int i = tid; i < nts; i += 1024) {
+    Tile tl;
+    tl.g = E;
+    tl.r0 = i * kTileM;
+    tl.rows = (int)(M - tl.r0 < kTileM ? M - tl.r0 : kTileM);
+    tl.pos0 = tl.r0;
+    tiles[routed_tiles + i] = tl;
+  }
+  if (tid == 0) *ntiles = routed_tiles + nts;
+  // pass 2: chunk bases.  s_part[part*E + e] -> start of the part within expert e
+  __syncthreads();
+  if (tid < E) {
+    int run = off;
+    for (int p = 0; p < P; ++p) {
+      const int v = s_part[p * E + tid];
+      s_part[p * E + tid] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  if (active) {
+    int run = s_part[tid];
+    for (int64_t c = c0; c < c1; ++c) {
+      const int v = cbase[c * E + e];
+      cbase[c * E + e] = run;
+      run += v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ scatter
+
+// perm[p] = t*k + j and inv[t*k + j] = p for every assignment, where p is the
+// chunk base of (chunk, expert) plus the number of earlier tokens of the chunk
+// routed to that expert.
+__global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict__ ids,
+                                                       const uint64_t* __restrict__ cmask,
+                                                       const int32_t* __restrict__ cbase,
+                                                       int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ inv, int64_t M, int E,
+                                                       int k) {
+  const int64_t c = blockIdx.x;
+  for (int idx = threadIdx.x; idx < kChunk * k; idx += 256) {
+    const int tl = idx & (kChunk - 1), j = idx >> 6;
+    const int64_t t = c * kChunk + tl;
+    if (t >= M) continue;
+    const int64_t a = t * k + j;
+    const int e = ids[a];
+    const uint64_t m = cmask[c * E + e];
+    const int p = cbase[c * E + e] + __popcll(m & ((1ull << tl) - 1ull));
+    perm[p] = (int32_t)a;
+    inv[a] = p;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, float* L,
+                                int64_t M, int H, int E, hipStream_t s) {
+  dim3 grid((unsigned)((M + 63) / 64), (unsigned)((E + 63) / 64));
+  hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, wr, bias, L, M, H, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_chunks(const float* L, int32_t* ids, float* w, uint64_t* cmask, int32_t* cbase,
+                              int64_t M, int E, int k, hipStream_t s) {
+  dim3 grid((unsigned)((M + kChunk - 1) / kChunk));
+  if (E <= 64)
+    hipLaunchKernelGGL(k_topk_chunks<1>, grid, dim3(256), 0, s, L, ids, w, cmask, cbase, M, E, k);
+  else if (E <= 128)
+    hipLaunchKernelGGL(k_topk_chunks<2>, grid, dim3(256), 0, s, L, ids, w, cmask, cbase, M, E, k);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_topk_chunks<4>, grid, dim3(256), 0, s, L, ids, w, cmask, cbase, M, E, k);
+  else if (E <= 512)
+    hipLaunchKernelGGL(k_topk_chunks<8>, grid, dim3(256), 0, s, L, ids, w, cmask, cbase, M, E, k);
+  else
+    hipLaunchKernelGGL(k_topk_chunks<16>, grid, dim3(256), 0, s, L, ids, w, cmask, cbase, M, E, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scan(int32_t* cbase, int32_t* counts, int32_t* offsets, Tile* tiles,
+                             int32_t* ntiles, int64_t M, int E, int k, bool shared, hipStream_t s) {
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, cbase, counts, offsets, tiles, ntiles, M,
+                     E, k, shared ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const int32_t* cbase,
+                                int32_t* perm, int32_t* inv, int64_t M, int E, int k, hipStream_t s) {
+  dim3 grid((unsigned)((M + kChunk - 1) / kChunk));
+  hipLaunchKernelGGL(k_route_scatter, grid, dim3(256), 0, s, ids, cmask, cbase, perm, inv, M, E, k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,137 @@
+"""Helpers for the GPU parity tests: host-side oracle inputs regenerated from the
+seeded generator, GPU calls through the C ABI, and the comparison rules.
+
+Comparison rules (the layer's parity bar):
+  - expert ids: bit-exact, except tokens the oracle flags as near-ties
+    (adjacent fp32 score gap <= 1e-5 among ranks 0..k); there the GPU's
+    choice must be a valid top-k, and the oracle is re-run with that choice;
+  - counts, offsets, perm: bit-exact (against the oracle for the GPU's ids);
+  - routing weights: |w_gpu - w_oracle| <= 1e-5;
+  - outputs: per token, max|y - y_ref| / max|y_ref| <= 1e-2.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import functools
+import os
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle.moe_oracle as O  # noqa: E402
+from sparse_moe_router_amd import moe  # noqa: E402
+from synth import device as SD  # noqa: E402
+from synth import inputs as S  # noqa: E402
+
+OUT_TOL = 1e-2
+W_TOL = 1e-5
+
+
+def f32(bits):
+    return S.bf16_bits_to_f32(bits)
+
+
+class HostLayer:
+    """Oracle-side copy of one layer's inputs, regenerated on the host."""
+
+    def __init__(self, w: S.Workload, layer: int = 0):
+        self.w, self.layer = w, layer
+        self.router = f32(S.router_weight(w, layer))
+        self.shared = f32(S.shared_weight(w, layer)) if w.I_shared else None
+        b = S.zipf_router_bias(w, layer)
+        self.bias = b
+        self._experts = {}
+
+    def x(self, row0, n):
+        return f32(S.x_rows(self.w, row0, n, self.layer))
+
+    def _gen(self, e):
+        blk = f32(S.expert_weight(self.w, self.layer, e))
+        return O.unpack_expert(blk, self.w.I, self.w.H)
+
+    def prefetch(self, experts):
+        todo = sorted(set(int(e) for e in experts) - set(self._experts))
+        if not todo:
+            return
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+            for e, v in zip(todo, ex.map(self._gen, todo)):
+                self._experts[e] = v
+
+    def expert(self, e):
+        if e not in self._experts:
+            self._experts[e] = self._gen(e)
+        return self._experts[e]
+
+
+def device_layer(w: S.Workload, layer=0, x_row0=0, x_rows=None):
+    return SD.layer_tensors(w, layer, x_rows=x_rows, x_row0=x_row0)
+
+
+def routing_buffers(M, E, k, dev="cuda", grouped=True):
+    r = dict(topk_ids=torch.empty(M, k, dtype=torch.int32, device=dev),
+             topk_w=torch.empty(M, k, dtype=torch.float32, device=dev),
+             logits=torch.empty(M, E, dtype=torch.float32, device=dev))
+    if grouped:
+        r.update(counts=torch.empty(E, dtype=torch.int32, device=dev),
+                 offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                 perm=torch.empty(M * k, dtype=torch.int32, device=dev))
+    return r
+
+
+def run_gpu(x, r, ex, sh, k, bias=None, flags=0):
+    """One moe_layer_forward call; returns numpy out (fp32 of bf16) and routing outputs."""
+    M, E = x.shape[0], r.shape[0]
+    grouped = not (M == 1 and not (flags & moe.FLAG_FORCE_GEMM))
+    rb = routing_buffers(M, E, k, grouped=grouped)
+    out = moe.forward(x, r, ex, sh, k, routing=rb, flags=flags, router_bias=bias)
+    torch.cuda.synchronize()
+    res = {name: t.cpu().numpy() for name, t in rb.items()}
+    res["out"] = out.float().cpu().numpy()
+    return res
+
+
+def check(gpu, orc_fn, k, E, rows=None, grouped=True, label=""):
+    """Compare one GPU result with the oracle.  orc_fn(force_ids) runs the oracle."""
+    orc = orc_fn(None)
+    ids_g = gpu["topk_ids"].astype(np.int64)
+    same = (ids_g == orc["ids"]).all(axis=1)
+    flagged = orc["flagged"]
+    bad = ~same & ~flagged
+    assert not bad.any(), f"{label}: ids differ on {bad.sum()} unflagged tokens, first {np.nonzero(bad)[0][:5]}"
+    diff = ~same
+    if diff.any():
+        ok = O.valid_topk(orc["logits32"][diff], ids_g[diff])
+        assert ok.all(), f"{label}: invalid top-k at flagged tokens {np.nonzero(diff)[0][~ok][:5]}"
+        orc = orc_fn(ids_g)  # the oracle for the GPU's (valid) selection
+    Lerr = np.abs(gpu["logits"].astype(np.float64) - orc["logits"]).max()
+    assert Lerr < 1e-4, f"{label}: router scores differ by {Lerr}"
+    werr = np.abs(gpu["topk_w"].astype(np.float64) - orc["w"]).max()
+    assert werr <= W_TOL, f"{label}: routing weights differ by {werr}"
+    if grouped:
+        assert np.array_equal(gpu["counts"], orc["counts"]), f"{label}: counts"
+        assert np.array_equal(gpu["offsets"], orc["offsets"]), f"{label}: offsets"
+        assert np.array_equal(gpu["perm"], orc["perm"]), f"{label}: perm"
+    rows = np.arange(gpu["out"].shape[0]) if rows is None else np.asarray(rows)
+    rel = O.rel_err_per_token(gpu["out"][rows], orc["out"][rows])
+    assert rel.max() <= OUT_TOL, f"{label}: output rel err {rel.max():.3e} at token {rows[rel.argmax()]}"
+    return dict(flagged=int(flagged.sum()), swapped=int(diff.sum()), max_rel=float(rel.max()),
+                L_err=float(Lerr), w_err=float(werr))
+
+
+def oracle_fn(hl: HostLayer, x_host, tokens=None):
+    w = hl.w
+
+    def fn(force):
+        return O.moe_forward(x_host, hl.router, hl.expert, hl.shared, w.k, w.I, bias=hl.bias,
+                             force_ids=force, tokens=tokens, I_shared=w.I_shared)
+    return fn
+
+
+@functools.lru_cache(maxsize=None)
+def gpu_ok():
+    return torch.cuda.is_available()

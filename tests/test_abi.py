@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects invalid
+arguments with the documented status before launching anything (CPU only:
+no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_router_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_layer.h")
+
+OK, INVALID, SHAPE, WS, MISALIGNED = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = moe.lib()
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = moe.lib()
+    for code in range(6):
+        s = L.moe_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert L.moe_status_string(0) == b"ok"
+    assert L.moe_last_hip_error() == 0
+
+
+def _desc(M=64, H=256, E=16, I=128, Is=128, flags=0, bias=None):
+    return moe.MoeDesc(M, H, E, I, Is, flags, bias)
+
+
+def ws_size(d, k):
+    return moe.lib().moe_workspace_size(ctypes.byref(d), k)
+
+
+def test_workspace_size_valid_and_invalid():
+    assert ws_size(_desc(), 2) > 0
+    big = ws_size(_desc(M=4096, H=2048, E=256, I=512, Is=512), 8)
+    # y_r alone is M*k*H bf16
+    assert big > 4096 * 8 * 2048 * 2
+    gemv = ws_size(_desc(M=1, H=2048, E=256, I=512, Is=512), 8)
+    gemm = ws_size(_desc(M=1, H=2048, E=256, I=512, Is=512, flags=moe.FLAG_FORCE_GEMM), 8)
+    assert 0 < gemv < gemm  # the decode path needs no permutation tables or y rows
+    for bad in [_desc(H=100), _desc(I=96), _desc(E=0), _desc(E=2000), _desc(Is=32), _desc(M=-1),
+                _desc(flags=3), _desc(flags=0x10)]:
+        assert ws_size(bad, 2) == 0
+    assert ws_size(_desc(), 0) == 0
+    assert ws_size(_desc(), 17) == 0  # top_k > E
+    assert ws_size(_desc(E=64), 33) == 0  # top_k > 32
+    assert ws_size(_desc(M=1 << 28), 8) == 0  # M*k >= 2^31
+    assert ws_size(_desc(M=5, flags=moe.FLAG_FORCE_GEMV), 2) == 0
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails its checks first
+
+
+def fwd(d, k=2, x=FAKE, r=FAKE + (1 << 24), ex=FAKE + (2 << 24), sh=FAKE + (3 << 24), out=FAKE + (4 << 24),
+        ws=FAKE + (5 << 24), wsb=1 << 40, routing=None):
+    return moe.lib().moe_layer_forward(ctypes.byref(d), x, r, ex, sh, k, out, ws, wsb, None,
+                                       None if routing is None else ctypes.byref(routing))
+
+
+def test_forward_rejects_bad_arguments():
+    d = _desc()
+    assert fwd(d, x=None) == INVALID
+    assert fwd(d, r=None) == INVALID
+    assert fwd(d, ex=None) == INVALID
+    assert fwd(d, out=None) == INVALID
+    assert fwd(d, sh=None) == INVALID  # I_shared > 0 needs shared weights
+    assert fwd(_desc(Is=0)) == INVALID  # shared weights given but I_shared == 0
+    assert fwd(d, ws=None) == INVALID
+    assert fwd(d, out=FAKE) == INVALID  # out aliases x
+    assert fwd(d, ws=FAKE + 1024) == INVALID  # workspace overlaps x
+    assert fwd(d, x=FAKE + 2) == MISALIGNED
+    assert fwd(d, ex=FAKE + (2 << 24) + 8) == MISALIGNED
+    assert fwd(d, ws=FAKE + (5 << 24) + 16) == MISALIGNED
+    assert fwd(d, wsb=ws_size(d, 2) - 1) == WS
+    assert fwd(_desc(H=100)) == SHAPE
+    assert fwd(d, k=0) == SHAPE
+    assert fwd(d, k=17) == SHAPE
+    assert fwd(_desc(M=3, flags=moe.FLAG_FORCE_GEMV)) == SHAPE
+    assert fwd(_desc(flags=3)) == INVALID
+    bad_bias = _desc(bias=FAKE + (6 << 24) + 4)
+    assert fwd(bad_bias) == MISALIGNED
+    r = moe.MoeRouting(FAKE + (7 << 24) + 2, None, None, None, None, None)
+    assert fwd(d, routing=r) == MISALIGNED
+    assert moe.lib().moe_layer_forward(None, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 0, None, None) == INVALID
+
+
+def test_forward_empty_batch_is_noop():
+    # M == 0: nothing to compute, returns OK without touching memory
+    assert fwd(_desc(M=0), ws=None, wsb=0) == OK
+
+
+def test_route_rejects_bad_arguments():
+    L = moe.lib()
+    d = _desc()
+    r = moe.MoeRouting(None, None, None, None, None, None)
+    assert L.moe_route(ctypes.byref(d), FAKE, FAKE + (1 << 24), 2, FAKE + (5 << 24), 1 << 40, None, None) == INVALID
+    assert L.moe_route(ctypes.byref(d), None, FAKE + (1 << 24), 2, FAKE + (5 << 24), 1 << 40, None,
+                       ctypes.byref(r)) == INVALID
+    assert L.moe_route(ctypes.byref(d), FAKE + 8, FAKE + (1 << 24), 2, FAKE + (5 << 24), 1 << 40, None,
+                       ctypes.byref(r)) == MISALIGNED
+    assert L.moe_route(ctypes.byref(d), FAKE, FAKE + (1 << 24), 2, FAKE + (5 << 24), 16, None,
+                       ctypes.byref(r)) == WS
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    r = torch.zeros(16, 256, dtype=torch.bfloat16)
+    ex = torch.zeros(16, 3 * 128 * 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.forward(x, r, ex, None, 2)

@@ -1,0 +1,221 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the
+seeded synthetic workloads (full sizes with sampled outputs, reduced sizes
+with every output) and on the layer's edge and degenerate cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from gpu_util import (HostLayer, check, device_layer, moe, oracle_fn, run_gpu, S, SD, f32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    moe.lib()
+    yield
+
+
+def upload(a, dtype=torch.bfloat16):
+    """Host fp32 array holding bf16-representable values -> device bf16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dtype).cuda()
+
+
+def bits_to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+# ------------------------------------------------------------------ generator
+
+def test_device_generator_matches_host():
+    for key, start, n, sigma in [(S.stream_key(1, 2, 3, 4), 0, 100_003, 0.02), (12345, 777, 4096, 1.0),
+                                 (S.x_key(S.PREFILL), 4095 * 2048, 2048, 1.0)]:
+        t = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        SD.fill(t, key, start, sigma)
+        got = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, S.normal_bf16(key, start, n, sigma))
+
+
+# ------------------------------------------------------------------ tiny workload
+
+def test_tiny_grouped_all_tokens():
+    w = S.TINY
+    hl = HostLayer(w)
+    x, r, ex, sh = device_layer(w)
+    g = run_gpu(x, r, ex, sh, w.k)
+    check(g, oracle_fn(hl, hl.x(0, w.M)), w.k, w.E, label="tiny")
+
+
+@pytest.mark.parametrize("flags", [0, moe.FLAG_FORCE_GEMM])
+def test_tiny_single_rows(flags):
+    w = S.TINY
+    hl = HostLayer(w)
+    _, r, ex, sh = device_layer(w)
+    for t in [0, 1, 17, 63]:
+        x1 = bits_to_dev(S.x_rows(w, t, 1))
+        g = run_gpu(x1, r, ex, sh, w.k, flags=flags)
+        check(g, oracle_fn(hl, hl.x(t, 1)), w.k, w.E, grouped=bool(flags), label=f"tiny row {t} flags {flags}")
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _full_case(w, layer=0, x_row0=0, nsample=8, extra_tokens=()):
+    hl = HostLayer(w, layer)
+    xh = hl.x(x_row0, w.M)
+    x, r, ex, sh = device_layer(w, layer, x_row0=x_row0)
+    bias = None if hl.bias is None else torch.from_numpy(hl.bias).cuda()
+    g = run_gpu(x, r, ex, sh, w.k, bias=bias)
+    del ex
+    rng = np.random.default_rng(w.seed + layer)
+    sample = sorted(set(rng.choice(w.M, nsample, replace=False).tolist()) | {0, w.M - 1} | set(extra_tokens))
+    ids_o = O.topk_ids(O.selection_logits(O.router_logits(xh, hl.router, hl.bias)), w.k)
+    hl.prefetch(np.concatenate([ids_o[sample].ravel(), g["topk_ids"][sample].ravel()]))
+    stats = check(g, oracle_fn(hl, xh, tokens=sample), w.k, w.E, rows=sample, label=w.name)
+    return g, stats
+
+
+def test_prefill_full():
+    g, st = _full_case(S.PREFILL)
+    assert g["counts"].sum() == S.PREFILL.M * S.PREFILL.k
+    print("prefill", st)
+
+
+def test_skew_full():
+    w = S.SKEW
+    # also sample tokens of the hottest expert, including the last rows of its group
+    hl = HostLayer(w)
+    L = O.router_logits(hl.x(0, w.M), hl.router, hl.bias)
+    ids = O.topk_ids(O.selection_logits(L), w.k)
+    hot = np.bincount(ids.ravel(), minlength=w.E).argmax()
+    hot_tokens = np.nonzero((ids == hot).any(axis=1))[0]
+    g, st = _full_case(w, extra_tokens=[int(hot_tokens[-1]), int(hot_tokens[len(hot_tokens) // 2])])
+    counts = g["counts"]
+    assert counts.max() > 1000 and (counts == 0).sum() > 50, "skewed routing expected"
+    print("skew", st, "max group", counts.max(), "empty", (counts == 0).sum())
+
+
+def test_long_prefill_chunk():
+    w = S.LONG
+    g, st = _full_case(w, x_row0=5 * w.M, nsample=6)
+    print("long chunk 5", st)
+
+
+def test_decode_full_shape():
+    w = S.DECODE
+    for layer, row in [(0, 0), (7, 3), (39, 63)]:
+        hl = HostLayer(w, layer)
+        x1 = bits_to_dev(S.x_rows(w, row, 1, layer))
+        _, r, ex, sh = device_layer(w, layer, x_rows=1)
+        g = run_gpu(x1, r, ex, sh, w.k)
+        hl.prefetch(g["topk_ids"].ravel())
+        check(g, oracle_fn(hl, hl.x(row, 1)), w.k, w.E, grouped=False, label=f"decode layer {layer}")
+
+
+# ------------------------------------------------------------------ edge cases (every output checked)
+
+def _rand_case(M, H, E, k, I, Is, seed=0, bias=None, zero_router=False, hot=None):
+    rng = np.random.default_rng(seed)
+    q = lambda a: S.bf16_bits_to_f32(S.f32_to_bf16_bits(a.astype(np.float32)))
+    x = q(rng.standard_normal((M, H)))
+    r = np.zeros((E, H), np.float32) if zero_router else q(rng.standard_normal((E, H)) * 0.02)
+    ex = q(rng.standard_normal((E, 3 * I * H)) * 0.02)
+    sh = q(rng.standard_normal(3 * Is * H) * 0.02) if Is else None
+    if hot is not None:
+        bias = np.zeros(E, np.float32)
+        bias[hot] = 100.0
+    return x, r, ex, sh, bias
+
+
+def _edge(M, H, E, k, I, Is, flags=0, **kw):
+    x, r, ex, sh, bias = _rand_case(M, H, E, k, I, Is, **kw)
+    g = run_gpu(upload(x), upload(r), upload(ex), None if sh is None else upload(sh), k,
+                bias=None if bias is None else torch.from_numpy(bias).cuda(), flags=flags)
+
+    def fn(force):
+        return O.moe_forward(x, r, ex, sh, k, I, bias=bias, force_ids=force, I_shared=Is)
+    grouped = not (M == 1 and not (flags & moe.FLAG_FORCE_GEMM))
+    return g, check(g, fn, k, E, grouped=grouped, label=f"M={M} H={H} E={E} k={k} I={I} Is={Is} {kw}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 63, 64, 65, 257, 700])
+def test_ragged_token_counts(M):
+    _edge(M, 256, 32, 4, 128, 128, flags=moe.FLAG_FORCE_GEMM if M == 1 else 0, seed=M)
+
+
+def test_no_shared_expert():
+    _edge(130, 256, 16, 2, 128, 0, seed=1)
+    _edge(1, 256, 16, 2, 128, 0, seed=2)
+
+
+@pytest.mark.parametrize("k", [1, 16])
+def test_top1_and_all_experts(k):
+    _edge(96, 256, 16, k, 64, 64, seed=k)
+
+
+def test_single_expert_many_tiles():
+    g, _ = _edge(600, 128, 1, 1, 64, 64, seed=3)
+    assert g["counts"][0] == 600
+
+
+def test_zero_router_exact_ties():
+    g, _ = _edge(100, 256, 16, 4, 64, 64, zero_router=True)
+    assert (g["topk_ids"] == np.arange(4)[None, :]).all()
+    assert np.allclose(g["topk_w"], 0.25, rtol=0, atol=1e-7)
+
+
+def test_hot_expert_bias():
+    g, _ = _edge(520, 256, 32, 4, 64, 64, hot=5)
+    assert (g["topk_ids"][:, 0] == 5).all() and g["counts"][5] == 520
+
+
+@pytest.mark.parametrize("E", [100, 300, 1000])
+def test_expert_counts(E):
+    _edge(80, 128, E, 8, 64, 64, seed=E)
+    _edge(1, 128, E, 8, 64, 64, seed=E + 1)
+
+
+def test_shared_size_differs():
+    _edge(90, 256, 16, 2, 128, 256, seed=5)
+    _edge(90, 256, 16, 2, 256, 64, seed=6)
+    _edge(1, 256, 16, 2, 128, 256, seed=7)
+
+
+def test_hidden_not_multiple_of_128():
+    _edge(70, 192, 16, 2, 64, 64, seed=8)
+    _edge(1, 192, 16, 2, 64, 64, seed=9)
+
+
+def test_decode_topk_32():
+    _edge(1, 128, 64, 32, 64, 64, seed=10)
+    _edge(40, 128, 64, 32, 64, 64, seed=11)
+
+
+# ------------------------------------------------------------------ properties (bit-exact)
+
+def test_determinism_chunking_and_permutation():
+    w = S.reduced(S.PREFILL, M=512, E=64)
+    x, r, ex, sh = device_layer(w)
+    a = moe.forward(x, r, ex, sh, w.k).clone()
+    b = moe.forward(x, r, ex, sh, w.k).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run bits differ"
+    c1 = moe.forward(x[:200].contiguous(), r, ex, sh, w.k).clone()
+    c2 = moe.forward(x[200:].contiguous(), r, ex, sh, w.k).clone()
+    assert torch.equal(torch.cat([c1, c2]).view(torch.int16), a.view(torch.int16)), "chunking changed bits"
+    p = torch.randperm(w.M, generator=torch.Generator().manual_seed(0)).cuda()
+    d = moe.forward(x[p].contiguous(), r, ex, sh, w.k)
+    assert torch.equal(d.view(torch.int16), a[p].view(torch.int16)), "token permutation changed bits"
+
+
+def test_route_matches_forward_routing():
+    w = S.reduced(S.SKEW, M=300)
+    hl = HostLayer(w)
+    x, r, ex, sh = device_layer(w)
+    bias = torch.from_numpy(hl.bias).cuda()
+    g = run_gpu(x, r, ex, sh, w.k, bias=bias)
+    rb = {k: torch.empty_like(torch.from_numpy(v)).cuda() for k, v in g.items() if k != "out"}
+    moe.route(x, r, w.k, rb, router_bias=bias, I=w.I, I_shared=w.I_shared)
+    torch.cuda.synchronize()
+    for k, v in rb.items():
+        assert np.array_equal(v.cpu().numpy(), g[k]), k
