@@ -12,12 +12,18 @@
 //    up tiles share the A rows and SwiGLU runs on the accumulators), the
 //    output projection goes with its routing score and the shared expert.
 //
-// Tile: up to 256 rows of one expert group x 128 weight rows.  Four waves
-// split the rows (64 each); each wave holds a 64x128 fp32 accumulator
-// (2 x 4 blocks of 32x32) and needs all 128 weight rows, so the weight tile
-// is shared through LDS while each wave loads its own activation rows
-// straight into MFMA operand registers (the rows of a routed group are
-// gathered through the scatter permutation, never copied).
+// Tile: up to 256 rows of one expert group (eight 32-row blocks) x 256
+// weight rows, one 4-wave workgroup per CU.  Every wave covers all rows of
+// the tile and its own 64 weight rows (a 256x64 fp32 accumulator, 256
+// registers, in AGPRs).  The weights -- the HBM stream -- go straight from
+// global memory into MFMA operand registers, each byte loaded once per tile
+// and never through LDS; the activation tile (rows of a routed group
+// gathered through the scatter permutation, never copied) is staged once
+// per K-step in LDS and read by all four waves.  With tiles of 256 rows an
+// expert's weights are read once whenever it has at most 256 rows (all
+// experts at near-uniform routing).  The number of 32-row blocks is a
+// template parameter chosen per tile (rounded up to even), so the inner
+// loop has no branches and row blocks past the group's rows cost nothing.
 //
 // Launch order is XCD-aware: workgroup b runs on XCD b % 8, and consecutive
 // logical tiles (the panels of one row tile, then the next row tile of the
@@ -28,8 +34,10 @@
 namespace moe {
 namespace {
 
-constexpr int BK = 32;   // K per pipeline step
-constexpr int BNR = 128; // weight rows per tile
+constexpr int BM = 256;   // rows per tile (= kTileM)
+constexpr int WN = 64;    // weight rows per wave
+constexpr int NWR = 256;  // weight rows per workgroup
+static_assert(BM == kTileM, "block map tile height");
 
 struct GemmArgs {
   const uint16_t* a_x;    // gate/up: token rows [M][H]
@@ -48,12 +56,194 @@ struct GemmArgs {
   int max_tiles;
 };
 
-// MODE 0: h = silu(A Wg^T) * (A Wu^T) over a 64-column panel of I (weight
-//         rows 0..63 = gate rows, 64..127 = up rows of the same columns).
-// MODE 1: y = A Wd^T over a 128-column panel of H.
+constexpr int BK = 64;        // K per pipeline step
+constexpr int CPR = BK / 8;   // 16-byte chunks per row per step
+constexpr int KK = BK / 16;   // MFMA sub-steps per step
+constexpr int DB = 2;         // weight steps in flight
+constexpr int DA = 2;         // activation steps in flight
+constexpr int U = 2;          // unroll (ring slots are fixed registers)
+constexpr int LDS_A = 2 * BM * CPR;  // two activation buffers, 16-byte units (64 KB)
+
+__device__ __forceinline__ int swz(int row, int q) { return row * CPR + (q ^ (row & (CPR - 1))); }
+
+// One tile.  MODE 0: h = silu(A Wg^T) * (A Wu^T) over a 128-column panel of
+// I; wave w owns gate rows [n0+32w, +32) (col block 0) and the up rows of the
+// same columns (col block 1), so SwiGLU is lane-local.  MODE 1: y = A Wd^T
+// over a 256-column panel of H; wave w owns columns [n0+64w, +64).
+//
+// K runs in steps of BK with a register pipeline: the weight fragments of
+// step s+DB and the activation chunks of step s+DA are in flight while step
+// s multiplies; the activation chunks of step s+1 go to the other LDS buffer
+// at the end of step s.  Within a step, MFMA sub-step kk and lane half h
+// take the 8 K-values 32h+8kk .. 32h+8kk+7 on both operands, a consistent
+// permutation of K that lets each lane read 16 contiguous bytes.  Loads past
+// the last step re-read the last step (never out of bounds, never
+// conditional), so no control flow surrounds memory operations.
+template <int MODE, int NRB>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int panel, u32x4_t* smem) {
+  constexpr int ACH = NRB * 32 * CPR / 256;  // activation chunks per thread per step
+  const bool is_shared = tl.g >= p.E;
+  const int Ig = is_shared ? p.Is : p.I;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  u32x4_t(*sA)[BM * CPR] = (u32x4_t(*)[BM * CPR])smem;
+
+  const uint16_t* W = is_shared ? p.shared_w : p.expert_w + (int64_t)tl.g * 3 * p.I * p.H;
+  int K, N, ncol0, ldw;
+  if (MODE == 0) {
+    K = p.H;
+    N = Ig;
+    ncol0 = panel * (NWR / 2) + 32 * wave;
+    ldw = p.H;
+  } else {
+    K = Ig;
+    N = p.H;
+    ncol0 = panel * NWR + WN * wave;
+    ldw = Ig;
+  }
+  const bool wave_cols = ncol0 < N;  // wave-uniform: does this wave own any output column?
+
+  // ---- this wave's weight rows: col block cb -> one 16-byte chunk per lane per sub-step
+  const u32x4_t* bsrc[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    int wrow;
+    const uint16_t* base;
+    if (MODE == 0) {
+      wrow = ncol0 + l32;
+      base = cb == 0 ? W : W + (int64_t)Ig * p.H;  // gate, then up
+    } else {
+      wrow = ncol0 + 32 * cb + l32;
+      base = W + (int64_t)2 * Ig * p.H;  // down [H][Ig]
+    }
+    if (wrow >= N) wrow = 0;  // columns past N compute on row 0 and are never stored
+    bsrc[cb] = (const u32x4_t*)(base + (int64_t)wrow * ldw) + (CPR / 2) * half;
+  }
+
+  // ---- activation-tile loader: ACH chunks per thread per step (row-contiguous, coalesced)
+  const u32x4_t* asrc[ACH];
+  int adst[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int c = tid + 256 * i, row = c / CPR, q = c % CPR;
+    const int r = row < tl.rows ? row : 0;
+    const uint16_t* rowp;
+    if (MODE == 0) {
+      const int64_t tok = is_shared ? (int64_t)tl.pos0 + r : (int64_t)(p.perm[tl.pos0 + r] / p.k);
+      rowp = p.a_x + tok * p.H;
+    } else {
+      rowp = (is_shared ? p.a_s : p.a_r) + ((int64_t)tl.pos0 + r) * Ig;
+    }
+    asrc[i] = (const u32x4_t*)rowp + q;
+    adst[i] = swz(row, q);
+  }
+
+  const int nsteps = K / BK;
+  u32x4_t breg[DB][2][KK];
+  u32x4_t areg[DA][ACH];
+  auto load_b = [&](u32x4_t (&r)[2][KK], int st) {
+    const int c0 = (st < nsteps ? st : nsteps - 1) * CPR;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) r[cb][kk] = bsrc[cb][c0 + kk];
+  };
+  auto load_a = [&](u32x4_t (&r)[ACH], int st) {
+    const int c0 = (st < nsteps ? st : nsteps - 1) * CPR;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) r[i] = asrc[i][c0];
+  };
+  auto store_a = [&](const u32x4_t (&r)[ACH], int buf) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) sA[buf][adst[i]] = r[i];
+  };
+
+  f32x16_t acc[NRB][2];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = (f32x16_t){};
+
+  // prologue
+  load_a(areg[0], 0);
+  load_b(breg[0], 0);
+  load_a(areg[1], 1);
+  load_b(breg[1], 1);
+  store_a(areg[0], 0);
+  __syncthreads();
+
+  for (int s0 = 0; s0 < nsteps; s0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u;
+      // a step past the end (odd nsteps) only repeats the clamped loads and
+      // the barrier, so every wave runs the same barriers
+      if (wave_cols && s < nsteps) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          u32x4_t af[NRB];
+          const int q = (CPR / 2) * half + kk;
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) af[rb] = sA[u][swz(32 * rb + l32, q)];
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8_t, af[rb]), __builtin_bit_cast(bf16x8_t, breg[u][cb][kk]),
+                  acc[rb][cb], 0, 0, 0);
+        }
+      }
+      load_b(breg[u], s + DB);
+      load_a(areg[u], s + DA);
+      store_a(areg[u ^ 1], u ^ 1);
+      __syncthreads();
+    }
+  }
+  if (!wave_cols) return;
+
+  // ---- epilogue: per 32-row block, round to bf16, stage through this wave's
+  //      slice of the (now idle) LDS, write 16-byte chunks.
+  //      32x32 block D layout: lane -> column lane%32, register r -> row
+  //      8*(r/4) + 4*(lane/32) + r%4.
+  constexpr int OC = MODE == 0 ? 32 : 64;  // output columns per wave
+  constexpr int CPRO = OC / 8;             // 16-byte chunks per output row
+  uint16_t* stage = (uint16_t*)smem + wave * (32 * OC);
+  uint16_t* obase = is_shared ? p.out_s : p.out_r;
+  const int ldo = MODE == 0 ? Ig : p.H;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    if (32 * rb >= tl.rows) break;  // uniform; rb stays a constant
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+      if (MODE == 0) {
+        stage[row * OC + l32] = (uint16_t)f32_to_bf16(silu(acc[rb][0][r]) * acc[rb][1][r]);
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) stage[row * OC + 32 * cb + l32] = (uint16_t)f32_to_bf16(acc[rb][cb][r]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int c = lane; c < 32 * CPRO; c += 64) {
+      const int row = c / CPRO, q = c % CPRO;
+      const int grow = 32 * rb + row;
+      const int col = ncol0 + 8 * q;
+      if (grow < tl.rows && col < N)
+        *(u32x4_t*)(obase + ((int64_t)tl.pos0 + grow) * ldo + col) = *(const u32x4_t*)(stage + row * OC + 8 * q);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs p) {
-  __shared__ u32x4_t sB[2][BNR * (BK / 8)];  // 2 x 8 KB
+__global__ __launch_bounds__(256, 1) void k_grouped_gemm(GemmArgs p) {
+  __shared__ u32x4_t smem[LDS_A];
 
   // ---- logical tile from the XCD-aware launch order
   const int nt = *p.ntiles;
@@ -65,164 +255,17 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs p) {
   if (lid >= V) return;
   const Tile tl = p.tiles[lid / p.npan];
   const int panel = lid % p.npan;
-  const bool is_shared = tl.g >= p.E;
-  const int Ig = is_shared ? p.Is : p.I;
-
-  const uint16_t* W = is_shared ? p.shared_w : p.expert_w + (int64_t)tl.g * 3 * p.I * p.H;
-  int K, N, n0, ldw;
-  const uint16_t* Wbase;
   if (MODE == 0) {
-    n0 = panel * 64;
-    if (n0 >= Ig) return;
-    K = p.H;
-    N = Ig;
-    ldw = p.H;
-    Wbase = W;  // gate [Ig][H], then up [Ig][H]
-  } else {
-    n0 = panel * BNR;
-    K = Ig;
-    N = p.H;
-    ldw = Ig;
-    Wbase = W + (int64_t)2 * Ig * p.H;  // down [H][Ig]
+    const int Ig = tl.g >= p.E ? p.Is : p.I;
+    if (panel * (NWR / 2) >= Ig) return;
   }
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-
-  // ---- weight-tile loader: 512 chunks of 16 B per step, two per thread
-  const u32x4_t* bsrc[2];
-  bool bok[2];
-  int bdst[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i, br = c >> 2, q = c & 3;
-    int wrow;
-    if (MODE == 0) {
-      wrow = n0 + (br & 63);
-      bok[i] = wrow < N;
-      const uint16_t* base = br < 64 ? Wbase : Wbase + (int64_t)Ig * p.H;
-      bsrc[i] = (const u32x4_t*)(base + (int64_t)(bok[i] ? wrow : 0) * ldw) + q;
-    } else {
-      wrow = n0 + br;
-      bok[i] = wrow < N;
-      bsrc[i] = (const u32x4_t*)(Wbase + (int64_t)(bok[i] ? wrow : 0) * ldw) + q;
-    }
-    bdst[i] = br * 4 + (q ^ ((br >> 1) & 3));
-  }
-
-  // ---- activation rows of this wave: rows 64*wave + 32*rb + lane%32
-  const int wrow0 = 64 * wave;
-  const bool wave_active = wrow0 < tl.rows;
-  const u32x4_t* asrc[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    int r = wrow0 + 32 * rb + (lane & 31);
-    if (r >= tl.rows) r = 0;  // padding rows compute on row 0 and are never stored
-    const uint16_t* rowp;
-    if (MODE == 0) {
-      const int64_t tok = is_shared ? (int64_t)tl.pos0 + r : (int64_t)(p.perm[tl.pos0 + r] / p.k);
-      rowp = p.a_x + tok * p.H;
-    } else {
-      rowp = is_shared ? p.a_s + ((int64_t)tl.pos0 + r) * Ig : p.a_r + ((int64_t)tl.pos0 + r) * Ig;
-    }
-    asrc[rb] = (const u32x4_t*)rowp + half;
-  }
-
-  const u32x4_t zero = {0, 0, 0, 0};
-  u32x4_t breg[2];
-  u32x4_t acur[2][2], anxt[2][2];
-  auto load_b = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) breg[i] = bok[i] ? bsrc[i][k0 >> 3] : zero;
-  };
-  auto store_b = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) sB[buf][bdst[i]] = breg[i];
-  };
-  auto load_a = [&](int k0, u32x4_t (&a)[2][2]) {
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) a[rb][kk] = asrc[rb][(k0 >> 3) + 2 * kk];
-  };
-
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = (f32x16_t){};
-
-  load_b(0);
-  if (wave_active) load_a(0, acur);
-  store_b(0);
-  __syncthreads();
-  const int nsteps = K / BK;
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      load_b((s + 1) * BK);
-      if (wave_active) load_a((s + 1) * BK, anxt);
-    }
-    if (wave_active) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4_t bf[4];
-        const int q = 2 * kk + half;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const int br = 32 * cb + (lane & 31);
-          bf[cb] = sB[buf][br * 4 + (q ^ ((br >> 1) & 3))];
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, acur[rb][kk]), __builtin_bit_cast(bf16x8_t, bf[cb]),
-                acc[rb][cb], 0, 0, 0);
-      }
-    }
-    if (more) {
-      store_b(buf ^ 1);
-      if (wave_active) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) acur[rb][kk] = anxt[rb][kk];
-      }
-    }
-    __syncthreads();
-  }
-  if (!wave_active) return;
-
-  // ---- epilogue.  32x32 block D layout: lane -> column lane%32,
-  //      register r -> row 8*(r/4) + 4*(lane/32) + r%4.
-  const int col = lane & 31;
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wrow0 + 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (row >= tl.rows) continue;
-      if (MODE == 0) {
-        uint16_t* orow = is_shared ? p.out_s + ((int64_t)tl.pos0 + row) * Ig
-                                   : p.out_r + ((int64_t)tl.pos0 + row) * Ig;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const int n = n0 + 32 * cb + col;
-          const float g = acc[rb][cb][r], u = acc[rb][cb + 2][r];
-          if (n < N) orow[n] = (uint16_t)f32_to_bf16(silu(g) * u);
-        }
-      } else {
-        uint16_t* orow = is_shared ? p.out_s + ((int64_t)tl.pos0 + row) * p.H
-                                   : p.out_r + ((int64_t)tl.pos0 + row) * p.H;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const int n = n0 + 32 * cb + col;
-          if (n < N) orow[n] = (uint16_t)f32_to_bf16(acc[rb][cb][r]);
-        }
-      }
-    }
+  // row blocks of 32, rounded up to even: the inner loop is specialised per count
+  const int nrb2 = ((tl.rows + 63) >> 6) << 1;
+  switch (nrb2) {
+    case 2: gemm_tile<MODE, 2>(p, tl, panel, smem); break;
+    case 4: gemm_tile<MODE, 4>(p, tl, panel, smem); break;
+    case 6: gemm_tile<MODE, 6>(p, tl, panel, smem); break;
+    default: gemm_tile<MODE, 8>(p, tl, panel, smem); break;
   }
 }
 
@@ -291,7 +334,7 @@ hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const
   a.Is = pl.Is;
   a.k = pl.k;
   const int maxI = pl.I > pl.Is ? pl.I : pl.Is;
-  a.npan = maxI / 64;
+  a.npan = (maxI + NWR / 2 - 1) / (NWR / 2);
   a.max_tiles = (int)pl.max_tiles;
   hipLaunchKernelGGL(k_grouped_gemm<0>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -315,7 +358,7 @@ hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint
   a.I = pl.I;
   a.Is = pl.Is;
   a.k = pl.k;
-  a.npan = (pl.H + BNR - 1) / BNR;
+  a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
   hipLaunchKernelGGL(k_grouped_gemm<1>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -12,7 +12,6 @@ namespace moe {
 
 constexpr int kChunk = 64;    // tokens per routing chunk: one bit per token in a 64-bit mask
 constexpr int kTileM = 256;   // rows per grouped-GEMM tile (block-map granularity)
-constexpr int kPanel1 = 64;   // gate/up GEMM: intermediate columns per tile (x2: gate and up)
 constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 32;
 
