@@ -11,59 +11,57 @@
 //    weight reads, not arithmetic.
 //
 // Three kernels per layer, all streaming bf16 weight rows with 16-byte loads
-// (one wave per output row: 64 lanes x 16 B = 1 KB per load instruction,
-// contiguous) and fp32 wave reductions:
+// (64 lanes x 16 B = 1 KB contiguous per load instruction) and fp32 wave
+// reductions:
 //   1. router scores (one wave per expert) and, independent of routing, the
 //      shared expert's gate/up rows + SiLU gate (one wave per row);
 //   2. top-k (recomputed by each workgroup from the scores) and the selected
 //      experts' gate/up rows + SiLU gate;
-//   3. the down projection of all selected experts and the shared expert,
-//      weighted and summed in registers, one bf16 output per wave.
+//   3. the down projection: one wave per (expert slot, 4 output rows), the
+//      weighted slot partials summed in slot order through LDS.
 #include "moe_internal.h"
 #include "wave_topk.h"
 
 namespace moe {
 namespace {
 
-// dot(x[0:n], w[0:n]) for one wave, n % 8 == 0, both bf16 rows, fp32 result in all lanes
-__device__ __forceinline__ float wave_dot_bf16(const uint16_t* __restrict__ x,
-                                               const uint16_t* __restrict__ w, int n, int lane) {
-  float acc = 0.0f;
-  for (int c = lane * 8; c < n; c += 512) {
-    const u32x4_t a = *(const u32x4_t*)(x + c);
-    const u32x4_t b = *(const u32x4_t*)(w + c);
+// Every wave issues all of its loads before using any of them (fixed-size
+// register batches, addresses clamped in bounds, contributions masked), so
+// a wave costs one memory round trip, not one per loop iteration.
+constexpr int DB = 4;  // 16-byte chunks per lane per batch: 4 x 64 lanes x 8 = 2048 elements
+
+// dot(x[0:n], w[0:n]) and dot(x, w2) for one wave (n % 8 == 0), fp32 in all lanes.
+template <bool TWO>
+__device__ __forceinline__ void wave_dots(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                          const uint16_t* __restrict__ w2, int n, int lane, float* d1,
+                                          float* d2) {
+  float a1 = 0.0f, a2 = 0.0f;
+  for (int base = 0; base < n; base += DB * 512) {
+    u32x4_t xa[DB], wa[DB], wb[DB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc += bf16_lo(a[q]) * bf16_lo(b[q]);
-      acc += bf16_hi(a[q]) * bf16_hi(b[q]);
+    for (int i = 0; i < DB; ++i) {
+      const int c = base + 512 * i + lane * 8;
+      const int cc = c < n ? c : 0;
+      xa[i] = *(const u32x4_t*)(x + cc);
+      wa[i] = *(const u32x4_t*)(w + cc);
+      if (TWO) wb[i] = *(const u32x4_t*)(w2 + cc);
+    }
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      if (base + 512 * i + lane * 8 >= n) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a1 += bf16_lo(xa[i][q]) * bf16_lo(wa[i][q]) + bf16_hi(xa[i][q]) * bf16_hi(wa[i][q]);
+        if (TWO) a2 += bf16_lo(xa[i][q]) * bf16_lo(wb[i][q]) + bf16_hi(xa[i][q]) * bf16_hi(wb[i][q]);
+      }
     }
   }
-  return wave_sum(acc);
+  *d1 = wave_sum(a1);
+  if (TWO) *d2 = wave_sum(a2);
 }
 
-// Two rows (gate, up) against the same x, one pass over x.
-__device__ __forceinline__ void wave_dot2_bf16(const uint16_t* __restrict__ x,
-                                               const uint16_t* __restrict__ wg,
-                                               const uint16_t* __restrict__ wu, int n, int lane,
-                                               float* g, float* u) {
-  float ag = 0.0f, au = 0.0f;
-  for (int c = lane * 8; c < n; c += 512) {
-    const u32x4_t a = *(const u32x4_t*)(x + c);
-    const u32x4_t b = *(const u32x4_t*)(wg + c);
-    const u32x4_t d = *(const u32x4_t*)(wu + c);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ag += bf16_lo(a[q]) * bf16_lo(b[q]);
-      ag += bf16_hi(a[q]) * bf16_hi(b[q]);
-      au += bf16_lo(a[q]) * bf16_lo(d[q]);
-      au += bf16_hi(a[q]) * bf16_hi(d[q]);
-    }
-  }
-  *g = wave_sum(ag);
-  *u = wave_sum(au);
-}
-
-// Workgroups [0, nrouter) score experts, the rest compute the shared expert's gate.
+// Workgroups [0, nrouter) score experts (one wave per expert), the rest
+// compute the shared expert's gated activation (one wave per row).
 __global__ __launch_bounds__(256) void k_dec_router_shared(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wr,
                                                            const float* __restrict__ bias,
@@ -75,13 +73,14 @@ __global__ __launch_bounds__(256) void k_dec_router_shared(const uint16_t* __res
   if ((int)blockIdx.x < nrouter) {
     const int e = blockIdx.x * 4 + wave;
     if (e >= E) return;
-    const float v = wave_dot_bf16(x, wr + (int64_t)e * H, H, lane);
+    float v, unused;
+    wave_dots<false>(x, wr + (int64_t)e * H, nullptr, H, lane, &v, &unused);
     if (lane == 0) logits[e] = v + (bias ? bias[e] : 0.0f);
   } else {
     const int i = (blockIdx.x - nrouter) * 4 + wave;
     if (i >= Is) return;
     float g, u;
-    wave_dot2_bf16(x, shared_w + (int64_t)i * H, shared_w + ((int64_t)Is + i) * H, H, lane, &g, &u);
+    wave_dots<true>(x, shared_w + (int64_t)i * H, shared_w + ((int64_t)Is + i) * H, H, lane, &g, &u);
     if (lane == 0) h_s[i] = silu(g) * u;
   }
 }
@@ -98,10 +97,13 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
                                                     float* __restrict__ h_r, int H, int E, int I,
                                                     int k) {
   __shared__ int32_t s_ids[kMaxTopK];
+  __shared__ uint64_t s_keys[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
     uint64_t top;
-    const uint64_t mine = wave_topk<EPL>(logits, E, k, lane, &top);
+    float f[EPL];
+    load_scores<EPL>(logits, E, lane, f);
+    const uint64_t mine = wave_topk<EPL>(f, E, k, lane, &top, s_keys);
     const int ej = (int)(0xFFFFFFFFu - (uint32_t)mine);
     if (lane < k) s_ids[lane] = ej;
     if (blockIdx.x == 0) {
@@ -123,61 +125,77 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
   if (j >= k || i >= I) return;
   const uint16_t* W = expert_w + (int64_t)s_ids[j] * 3 * I * H;
   float g, u;
-  wave_dot2_bf16(x, W + (int64_t)i * H, W + ((int64_t)I + i) * H, H, lane, &g, &u);
+  wave_dots<true>(x, W + (int64_t)i * H, W + ((int64_t)I + i) * H, H, lane, &g, &u);
   if (lane == 0) h_r[(int64_t)j * I + i] = silu(g) * u;
 }
 
-// out[c] = sum_j w_j * (Wd_{ids[j]}[c] . h_r[j]) + Sd[c] . h_s, one wave per c.
-__global__ __launch_bounds__(256) void k_dec_down(const uint16_t* __restrict__ expert_w,
-                                                  const uint16_t* __restrict__ shared_w,
-                                                  const int32_t* __restrict__ ids,
-                                                  const float* __restrict__ wts,
-                                                  const float* __restrict__ h_r,
-                                                  const float* __restrict__ h_s,
-                                                  uint16_t* __restrict__ out, int H, int I, int Is,
-                                                  int k) {
-  __shared__ int32_t s_ids[kMaxTopK];
-  __shared__ float s_w[kMaxTopK];
-  if ((int)threadIdx.x < k) {
-    s_ids[threadIdx.x] = ids[threadIdx.x];
-    s_w[threadIdx.x] = wts[threadIdx.x];
+// out[c] = sum_j w_j * (Wd_{ids[j]}[c] . h_r[j]) + Sd[c] . h_s.
+// Workgroup = one wave per expert slot (slot k = shared expert), DR output
+// rows each; every wave loads its DR weight rows and its h slice at once,
+// reduces, and the slot partials are summed in slot order through LDS.
+constexpr int DR = 4;
+__global__ __launch_bounds__(1024) void k_dec_down(const uint16_t* __restrict__ expert_w,
+                                                   const uint16_t* __restrict__ shared_w,
+                                                   const int32_t* __restrict__ ids,
+                                                   const float* __restrict__ wts,
+                                                   const float* __restrict__ h_r,
+                                                   const float* __restrict__ h_s,
+                                                   uint16_t* __restrict__ out, int H, int I, int Is,
+                                                   int k, int nslot) {
+  __shared__ float s_part[kMaxTopK + 1][DR];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c0 = blockIdx.x * DR;
+  // slots wave, wave + nwaves, ... (one pass when k + 1 <= waves per workgroup)
+  for (int j = wave; j < nslot; j += blockDim.x >> 6) {
+    const bool sh = j == k;  // the shared expert
+    const int n = sh ? Is : I;
+    const uint16_t* wd;
+    const float* hj;
+    float wj = 1.0f;
+    if (sh) {
+      wd = shared_w + (int64_t)2 * Is * H;
+      hj = h_s;
+    } else {
+      wd = expert_w + (int64_t)ids[j] * 3 * I * H + (int64_t)2 * I * H;
+      hj = h_r + (int64_t)j * I;
+      wj = wts[j];
+    }
+    float part[DR];
+#pragma unroll
+    for (int r = 0; r < DR; ++r) part[r] = 0.0f;
+    for (int base = 0; base < n; base += 512) {
+      const int q0 = base + lane * 8;
+      const bool ok = q0 < n;
+      const int qq = ok ? q0 : 0;
+      u32x4_t b[DR];
+#pragma unroll
+      for (int r = 0; r < DR; ++r) {
+        const int c = c0 + r < H ? c0 + r : H - 1;
+        b[r] = *(const u32x4_t*)(wd + (int64_t)c * n + qq);
+      }
+      const f32x4_t h0 = *(const f32x4_t*)(hj + qq);
+      const f32x4_t h1 = *(const f32x4_t*)(hj + qq + 4);
+      if (ok) {
+#pragma unroll
+        for (int r = 0; r < DR; ++r)
+          part[r] += bf16_lo(b[r][0]) * h0[0] + bf16_hi(b[r][0]) * h0[1] + bf16_lo(b[r][1]) * h0[2] +
+                     bf16_hi(b[r][1]) * h0[3] + bf16_lo(b[r][2]) * h1[0] + bf16_hi(b[r][2]) * h1[1] +
+                     bf16_lo(b[r][3]) * h1[2] + bf16_hi(b[r][3]) * h1[3];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < DR; ++r) {
+      const float v = wave_sum(part[r]);
+      if (lane == 0) s_part[j][r] = wj * v;
+    }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = blockIdx.x * 4 + wave;
-  if (c >= H) return;
-  float total = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const uint16_t* wd = expert_w + (int64_t)s_ids[j] * 3 * I * H + (int64_t)2 * I * H + (int64_t)c * I;
-    const float* hj = h_r + (int64_t)j * I;
-    float acc = 0.0f;
-    for (int q0 = lane * 8; q0 < I; q0 += 512) {
-      const u32x4_t b = *(const u32x4_t*)(wd + q0);
-      const f32x4_t h0 = *(const f32x4_t*)(hj + q0);
-      const f32x4_t h1 = *(const f32x4_t*)(hj + q0 + 4);
-      acc += bf16_lo(b[0]) * h0[0] + bf16_hi(b[0]) * h0[1] + bf16_lo(b[1]) * h0[2] +
-             bf16_hi(b[1]) * h0[3];
-      acc += bf16_lo(b[2]) * h1[0] + bf16_hi(b[2]) * h1[1] + bf16_lo(b[3]) * h1[2] +
-             bf16_hi(b[3]) * h1[3];
-    }
-    total += s_w[j] * acc;
+  if (threadIdx.x < DR && c0 + (int)threadIdx.x < H) {
+    float v = 0.0f;
+    for (int j = 0; j < nslot; ++j) v += s_part[j][threadIdx.x];  // slot order, shared last
+    out[c0 + threadIdx.x] = (uint16_t)f32_to_bf16(v);
   }
-  if (shared_w) {
-    const uint16_t* wd = shared_w + (int64_t)2 * Is * H + (int64_t)c * Is;
-    float acc = 0.0f;
-    for (int q0 = lane * 8; q0 < Is; q0 += 512) {
-      const u32x4_t b = *(const u32x4_t*)(wd + q0);
-      const f32x4_t h0 = *(const f32x4_t*)(h_s + q0);
-      const f32x4_t h1 = *(const f32x4_t*)(h_s + q0 + 4);
-      acc += bf16_lo(b[0]) * h0[0] + bf16_hi(b[0]) * h0[1] + bf16_lo(b[1]) * h0[2] +
-             bf16_hi(b[1]) * h0[3];
-      acc += bf16_lo(b[2]) * h1[0] + bf16_hi(b[2]) * h1[1] + bf16_lo(b[3]) * h1[2] +
-             bf16_hi(b[3]) * h1[3];
-    }
-    total += acc;
-  }
-  total = wave_sum(total);
-  if (lane == 0) out[c] = (uint16_t)f32_to_bf16(total);
 }
 
 }  // namespace
@@ -215,8 +233,10 @@ hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w
                               hipStream_t s) {
   const float* h_r = h_dec;
   const float* h_s = h_dec + (int64_t)p.k * p.I;
-  hipLaunchKernelGGL(k_dec_down, dim3((p.H + 3) / 4), dim3(256), 0, s, expert_w,
-                     p.shared ? shared_w : nullptr, ids, w, h_r, h_s, out, p.H, p.I, p.Is, p.k);
+  const int nslot = p.k + (p.shared ? 1 : 0);
+  const int waves = nslot < 16 ? nslot : 16;
+  hipLaunchKernelGGL(k_dec_down, dim3((p.H + DR - 1) / DR), dim3(64 * waves), 0, s, expert_w,
+                     p.shared ? shared_w : nullptr, ids, w, h_r, h_s, out, p.H, p.I, p.Is, p.k, nslot);
   return hipGetLastError();
 }
 

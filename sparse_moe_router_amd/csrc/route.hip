@@ -24,6 +24,9 @@ namespace {
 // L[t][e] = sum_h x[t][h] * Wr[e][h] (+ bias[e]); fp32 accumulate on MFMA.
 // Tile 64 tokens x 64 experts, 4 waves in 2x2, each wave one 32x32 block,
 // K in steps of 64 staged through LDS (double buffered, XOR-swizzled rows).
+// Global loads run RD steps ahead in a register ring (loads past the end
+// re-read the last step: never conditional, never out of bounds).
+constexpr int RD = 4;
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ wr,
                                                        const float* __restrict__ bias,
@@ -36,7 +39,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   const int e0 = blockIdx.y * 64;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // loader: 512 16-byte chunks per operand per stage, two per thread
+  // loader: 512 16-byte chunks per operand per step, two per thread
   const u32x4_t* srcA[2];
   const u32x4_t* srcB[2];
   bool okA[2], okB[2];
@@ -52,42 +55,51 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
     srcB[i] = (const u32x4_t*)(wr + (int64_t)(okB[i] ? e : 0) * H) + q;
     dst[i] = row * 8 + (q ^ (row & 7));
   }
+  const int nsteps = H / 64;
   const u32x4_t zero = {0, 0, 0, 0};
-  u32x4_t ra[2], rb[2];
-  auto gload = [&](int k0) {
+  u32x4_t ra[RD][2], rb[RD][2];
+  auto gload = [&](u32x4_t (&a)[2], u32x4_t (&b)[2], int st) {
+    const int c0 = (st < nsteps ? st : nsteps - 1) * 8;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      ra[i] = okA[i] ? srcA[i][k0 >> 3] : zero;
-      rb[i] = okB[i] ? srcB[i][k0 >> 3] : zero;
+      const u32x4_t va = srcA[i][c0], vb = srcB[i][c0];
+      a[i] = okA[i] ? va : zero;
+      b[i] = okB[i] ? vb : zero;
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const u32x4_t (&a)[2], const u32x4_t (&b)[2], int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      sA[buf][dst[i]] = ra[i];
-      sB[buf][dst[i]] = rb[i];
+      sA[buf][dst[i]] = a[i];
+      sB[buf][dst[i]] = b[i];
     }
   };
 
   f32x16_t acc = {};
   const int arow = wm * 32 + (lane & 31), brow = wn * 32 + (lane & 31), half = lane >> 5;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int nsteps = H / 64;
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) gload((s + 1) * 64);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int q = 2 * kk + half;
-      const u32x4_t a = sA[buf][arow * 8 + (q ^ (arow & 7))];
-      const u32x4_t b = sB[buf][brow * 8 + (q ^ (brow & 7))];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                     __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  for (int st = 0; st < RD; ++st) gload(ra[st], rb[st], st);
+  lstore(ra[0], rb[0], 0);
+  __syncthreads();
+  for (int s0 = 0; s0 < nsteps; s0 += RD) {
+#pragma unroll
+    for (int u = 0; u < RD; ++u) {
+      const int s = s0 + u;
+      const int buf = u & 1;
+      if (s < nsteps) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int q = 2 * kk + half;
+          const u32x4_t a = sA[buf][arow * 8 + (q ^ (arow & 7))];
+          const u32x4_t b = sB[buf][brow * 8 + (q ^ (brow & 7))];
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                         __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+        }
+      }
+      gload(ra[u], rb[u], s + RD);
+      lstore(ra[(u + 1) % RD], rb[(u + 1) % RD], buf ^ 1);
+      __syncthreads();
     }
-    if (s + 1 < nsteps) lstore(buf ^ 1);
-    __syncthreads();
   }
   // D layout of the 32x32 block: lane -> column, register r -> row 8(r/4) + 4(lane/32) + r%4
   const int e = e0 + wn * 32 + (lane & 31);
@@ -103,26 +115,35 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 
 // ------------------------------------------------------------------ top-k
 
-// One workgroup per chunk of 64 tokens, 4 waves x 16 tokens.  Writes ids and
+// One workgroup per chunk of 64 tokens, 16 waves x 4 tokens.  Writes ids and
 // weights per token, and per (chunk, expert) the token bitmask and its count.
 template <int EPL>
-__global__ __launch_bounds__(256) void k_topk_chunks(const float* __restrict__ L,
-                                                     int32_t* __restrict__ ids,
-                                                     float* __restrict__ w,
-                                                     uint64_t* __restrict__ cmask,
-                                                     int32_t* __restrict__ ccount, int64_t M, int E,
-                                                     int k) {
+__global__ __launch_bounds__(1024) void k_topk_chunks(const float* __restrict__ L,
+                                                      int32_t* __restrict__ ids,
+                                                      float* __restrict__ w,
+                                                      uint64_t* __restrict__ cmask,
+                                                      int32_t* __restrict__ ccount, int64_t M, int E,
+                                                      int k) {
   __shared__ uint32_t mlo[kMaxE], mhi[kMaxE];
+  __shared__ uint64_t s_keys[16][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c = blockIdx.x;
-  for (int e = tid; e < E; e += 256) mlo[e] = mhi[e] = 0;
+  for (int e = tid; e < E; e += 1024) mlo[e] = mhi[e] = 0;
   __syncthreads();
-  for (int i = 0; i < 16; ++i) {
-    const int tl = wave * 16 + i;  // token within the chunk
+  // all four tokens' scores in flight at once
+  float f[4][EPL];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = c * kChunk + wave * 4 + i;
+    load_scores<EPL>(L + (t < M ? t : M - 1) * E, E, lane, f[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tl = wave * 4 + i;  // token within the chunk
     const int64_t t = c * kChunk + tl;
     if (t >= M) break;
     uint64_t top;
-    const uint64_t mine = wave_topk<EPL>(L + t * E, E, k, lane, &top);
+    const uint64_t mine = wave_topk<EPL>(f[i], E, k, lane, &top, s_keys[wave]);
     const float l0 = from_orderable((uint32_t)(top >> 32));
     const float lj = from_orderable((uint32_t)(mine >> 32));
     const int ej = (int)(0xFFFFFFFFu - (uint32_t)mine);
@@ -138,7 +159,7 @@ __global__ __launch_bounds__(256) void k_topk_chunks(const float* __restrict__ L
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) {
+  for (int e = tid; e < E; e += 1024) {
     const uint32_t lo = mlo[e], hi = mhi[e];
     cmask[c * E + e] = ((uint64_t)hi << 32) | lo;
     ccount[c * E + e] = __popc(lo) + __popc(hi);
@@ -197,7 +218,17 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cbase
 
   // pass 1: partial counts per (part, expert)
   int psum = 0;
-  for (int64_t c = c0; c < c1; ++c) psum += cbase[c * E + e];
+  {
+    int64_t c = c0;
+    for (; c + 8 <= c1; c += 8) {  // eight independent loads in flight
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = cbase[(c + j) * E + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) psum += v[j];
+    }
+    for (; c < c1; ++c) psum += cbase[c * E + e];
+  }
   s_part[tid] = active ? psum : 0;
   __syncthreads();
   // expert totals (thread e < E), exclusive scan over experts
@@ -248,7 +279,18 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cbase
   __syncthreads();
   if (active) {
     int run = s_part[tid];
-    for (int64_t c = c0; c < c1; ++c) {
+    int64_t c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = cbase[(c + j) * E + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        cbase[(c + j) * E + e] = run;
+        run += v[j];
+      }
+    }
+    for (; c < c1; ++c) {
       const int v = cbase[c * E + e];
       cbase[c * E + e] = run;
       run += v;
@@ -294,15 +336,15 @@ hipError_t launch_topk_chunks(const float* L, int32_t* ids, float* w, uint64_t* 
                               int64_t M, int E, int k, hipStream_t s) {
   dim3 grid((unsigned)((M + kChunk - 1) / kChunk));
   if (E <= 64)
-    hipLaunchKernelGGL(k_topk_chunks<1>, grid, dim3(256), 0, s, L, ids, w, cmask, cbase, M, E, k);
+    hipLaunchKernelGGL(k_topk_chunks<1>, grid, dim3(1024), 0, s, L, ids, w, cmask, cbase, M, E, k);
   else if (E <= 128)
-    hipLaunchKernelGGL(k_topk_chunks<2>, grid, dim3(256), 0, s, L, ids, w, cmask, cbase, M, E, k);
+    hipLaunchKernelGGL(k_topk_chunks<2>, grid, dim3(1024), 0, s, L, ids, w, cmask, cbase, M, E, k);
   else if (E <= 256)
-    hipLaunchKernelGGL(k_topk_chunks<4>, grid, dim3(256), 0, s, L, ids, w, cmask, cbase, M, E, k);
+    hipLaunchKernelGGL(k_topk_chunks<4>, grid, dim3(1024), 0, s, L, ids, w, cmask, cbase, M, E, k);
   else if (E <= 512)
-    hipLaunchKernelGGL(k_topk_chunks<8>, grid, dim3(256), 0, s, L, ids, w, cmask, cbase, M, E, k);
+    hipLaunchKernelGGL(k_topk_chunks<8>, grid, dim3(1024), 0, s, L, ids, w, cmask, cbase, M, E, k);
   else
-    hipLaunchKernelGGL(k_topk_chunks<16>, grid, dim3(256), 0, s, L, ids, w, cmask, cbase, M, E, k);
+    hipLaunchKernelGGL(k_topk_chunks<16>, grid, dim3(1024), 0, s, L, ids, w, cmask, cbase, M, E, k);
   return hipGetLastError();
 }
 

@@ -21,54 +21,88 @@ __device__ __forceinline__ uint64_t sel_key(float f, int e) {
   return ((uint64_t)orderable(f) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
-}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
   return v;
 }
 
-// One wave selects the top k of E scores of one token; lanes own experts
-// lane, lane+64, ...  Returns, in lane j < k, the rank-j key; all lanes get
-// the rank-0 key in *top.
+// One wave selects the top k of E scores of one token; lane l holds the
+// scores of experts l, l+64, ... in f.  Returns, in lane j < k, the rank-j
+// key; every lane gets the rank-0 key in *top.  s_keys: 64 wave-private LDS
+// entries.
+//
+// Radix select with ballots: 32 rounds of compare + ballot + popcount find
+// T, the k-th largest order-mapped score (count(v >= T) >= k, maximal).  The
+// selection is every score above T plus the lowest-index experts scoring
+// exactly T, as many as needed for k.  The k winners are compacted into LDS
+// by ballot prefix counts, and each of lanes 0..k-1 ranks one winner against
+// the others (keys are unique: score, then index) and stores it at its rank.
+// Loads lane's scores of one token (experts lane, lane+64, ...); padding
+// (e >= E) is -inf, which sorts below every real score.
 template <int EPL>
-__device__ __forceinline__ uint64_t wave_topk(const float* __restrict__ Lrow, int E, int k, int lane,
-                                              uint64_t* top) {
-  uint64_t key[EPL];
+__device__ __forceinline__ void load_scores(const float* __restrict__ Lrow, int E, int lane, float (&f)[EPL]) {
 #pragma unroll
   for (int q = 0; q < EPL; ++q) {
     const int e = lane + 64 * q;
-    key[q] = e < E ? sel_key(Lrow[e], e) : 0ull;
+    f[q] = e < E ? Lrow[e] : -__builtin_inff();
   }
-  // sort the lane's keys descending (insertion network, constant indices only)
+}
+
+template <int EPL>
+__device__ __forceinline__ uint64_t wave_topk(const float (&f)[EPL], int E, int k, int lane, uint64_t* top,
+                                              uint64_t* s_keys) {
+  uint32_t v[EPL];
 #pragma unroll
-  for (int i = 1; i < EPL; ++i)
+  for (int q = 0; q < EPL; ++q) v[q] = lane + 64 * q < E ? orderable(f[q]) : 0u;
+  uint32_t T = 0;
+#pragma unroll 4
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-    for (int j = i; j > 0; --j) {
-      const uint64_t a = key[j - 1], b = key[j];
-      key[j - 1] = a > b ? a : b;
-      key[j] = a > b ? b : a;
-    }
-  uint64_t mine = 0;
-  for (int j = 0; j < k; ++j) {
-    const uint64_t best = wave_max_u64(key[0]);
-    if (j == 0) *top = best;
-    if (lane == j) mine = best;
-    if (key[0] == best) {  // keys are unique: exactly one owner lane pops its head
-#pragma unroll
-      for (int q = 0; q + 1 < EPL; ++q) key[q] = key[q + 1];
-      key[EPL - 1] = 0ull;
-    }
+    for (int q = 0; q < EPL; ++q) cnt += __popcll(__ballot(v[q] >= cand));
+    if (cnt >= k) T = cand;
   }
+  int gt = 0;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) gt += __popcll(__ballot(v[q] > T));
+  const int need_eq = k - gt;
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes with a lower index
+  int base_sel = 0, base_eq = 0;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) {
+    const uint64_t beq = __ballot(v[q] == T);
+    const int eq_rank = base_eq + __popcll(beq & below);
+    const bool sel = v[q] > T || (v[q] == T && eq_rank < need_eq);
+    const uint64_t bsel = __ballot(sel);
+    if (sel)
+      s_keys[base_sel + __popcll(bsel & below)] =
+          ((uint64_t)v[q] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * q));
+    base_sel += __popcll(bsel);
+    base_eq += __popcll(beq);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint64_t key = 0;
+  int rank = 0;
+  if (lane < k) {
+    key = s_keys[lane];
+    for (int i = 0; i < k; ++i) rank += s_keys[i] > key;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < k) s_keys[32 + rank] = key;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t mine = lane < k ? s_keys[32 + lane] : 0ull;
+  *top = s_keys[32];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   return mine;
 }
 
