@@ -39,7 +39,38 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--layers", type=int, default=40, help=argparse.SUPPRESS)
     ap.add_argument("--trace-steps", type=int, default=10)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy three times (the reference "
+                         "kernel of known size for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash():
+    """Hash of the library's kernel sources; counter figures taken from other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "sparse_moe_router_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE scaled by the copy-kernel calibration), or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash() or kernel not in t.get("kernels", {}):
+        return None
+    k = t["kernels"][kernel]
+    return round(k["fetch_kib"] * 1024 * t["fetch_scale"] + k["write_kib"] * 1024 * t["write_scale"])
 
 
 class Hip:
@@ -204,31 +235,38 @@ def bench_decode(args, hip, moe, SD, S):
         layer_hbm_frac=layer_bytes * L / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         kernels_us={n: round(1000.0 * sum(v) / len(v), 3) for n, v in kt.items()},
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel="k_dec_gateup",
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for("k_dec_gateup"),
+                      kernel="k_dec_gateup",
                       bytes_per_launch=gateup_bytes, avg_us=round(avg_ms * 1000, 3)),
     )
     return res, (layers, xpool)
 
 
-def cpu_decode(S, O, layers_sample=4):
-    """Oracle on a bounded sample: one token row through `layers_sample` layers."""
-    import numpy as np
+def cpu_decode(S, O, layers_sample=2, rows=128):
+    """Oracle on a bounded sample of the decode workload: `rows` single-token (M=1)
+    calls through each of `layers_sample` layers; the selected experts' weights are
+    regenerated on the host outside the timing."""
+    import concurrent.futures as cf
     w = S.DECODE
     f = S.bf16_bits_to_f32
-    x = f(S.x_rows(w, 0, 1, 0))
+    xs = f(S.x_rows(w, 0, rows, 0))
     t_total = 0.0
     for l in range(layers_sample):
         r = f(S.router_weight(w, l))
         sh = f(S.shared_weight(w, l))
-        ids = O.topk_ids(O.selection_logits(O.router_logits(x, r)), w.k)
-        cache = {int(e): O.unpack_expert(f(S.expert_weight(w, l, int(e))), w.I, w.H) for e in ids.ravel()}
+        ids = O.topk_ids(O.selection_logits(O.router_logits(xs, r)), w.k)
+        need = sorted(set(int(e) for e in ids.ravel()))
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+            cache = dict(zip(need, ex.map(lambda e: O.unpack_expert(f(S.expert_weight(w, l, e)), w.I, w.H), need)))
         t = time.perf_counter()
-        O.moe_forward(x, r, lambda e: cache[e], sh, w.k, w.I)
+        for i in range(rows):
+            O.moe_forward(xs[i:i + 1], r, lambda e: cache[e], sh, w.k, w.I)
         t_total += time.perf_counter() - t
-    per_layer = t_total / layers_sample
+    per_layer = t_total / (layers_sample * rows)
     return dict(value=1.0 / (per_layer * w.layers), unit="tok/s", cores=blas_threads(), kind="oracle",
-                sample=f"1 token row x {layers_sample} of the 40 layers (fp64 NumPy oracle; selected experts "
-                       f"regenerated outside the timing); tok/s = 1 / (mean layer time x 40)",
+                sample=f"{rows} single-token calls through each of {layers_sample} of the {w.layers} layers "
+                       f"(fp64 NumPy oracle; selected experts regenerated outside the timing); "
+                       f"tok/s = 1 / (mean time per token-layer x {w.layers})",
                 seconds=round(t_total, 3))
 
 
@@ -273,7 +311,8 @@ def bench_prefill(args, hip, moe, SD, S, w):
         mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         kernels_us={n: round(1000.0 * sum(v) / len(v), 2) for n, v in kt.items()},
         roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None, kernel="k_grouped_gemm<gate/up>",
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic_for(f"k_grouped_gemm<0>@{w.name}"),
+                      kernel="k_grouped_gemm<0> (gate/up + SwiGLU)",
                       bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
                       mfma_frac=round(gu_flops / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)),
     )
@@ -281,9 +320,10 @@ def bench_prefill(args, hip, moe, SD, S, w):
     return res
 
 
-def cpu_prefill(S, O, w, m_sample=512):
-    """Oracle on a bounded sample: the first m_sample tokens of the workload through the layer."""
+def cpu_prefill(S, O, w, m_sample=None):
+    """Oracle on the first m_sample tokens (default: all) of the workload through the layer."""
     import concurrent.futures as cf
+    m_sample = m_sample or w.M
     f = S.bf16_bits_to_f32
     x = f(S.x_rows(w, 0, m_sample))
     r = f(S.router_weight(w))
@@ -297,8 +337,9 @@ def cpu_prefill(S, O, w, m_sample=512):
     O.moe_forward(x, r, lambda e: blocks[e], sh, w.k, w.I, bias=bias)
     dt = time.perf_counter() - t
     return dict(value=m_sample / dt, unit="tok/s", cores=blas_threads(), kind="oracle",
-                sample=f"first {m_sample} of the {w.M} tokens through the layer (fp64 NumPy oracle; "
-                       f"{len(need)} experts' weights regenerated outside the timing)",
+                sample=(f"first {m_sample} of the {w.M} tokens" if m_sample < w.M else f"all {w.M} tokens") +
+                       f" through the layer (fp64 NumPy oracle; {len(need)} experts' weights regenerated "
+                       f"outside the timing)",
                 seconds=round(dt, 3))
 
 
@@ -315,6 +356,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hip = Hip()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     dec, keep = bench_decode(args, hip, moe, SD, S)
     del keep
     torch.cuda.empty_cache()

@@ -141,10 +141,11 @@ typedef enum {
 } moe_kernel_t;
 
 /* Instrumentation for moe_layer_forward_traced: caller-created hipEvent_t
- * handles (timing enabled).  Each kernel launch i of the call is bracketed by
- * hipEventRecord(begin[count], stream) / hipEventRecord(end[count], stream)
- * and kernel[count] = its moe_kernel_t; count advances.  Launches beyond
- * capacity run unrecorded. */
+ * handles (timing enabled).  Each kernel of the call is launched with
+ * begin[count] / end[count] as its start / stop events (hipExtLaunchKernel
+ * semantics: the events take the kernel's own start and end time, the
+ * interval a kernel-trace profiler reports), kernel[count] receives its
+ * moe_kernel_t and count advances.  Launches beyond capacity run untimed. */
 typedef struct {
   void* const* begin;
   void* const* end;

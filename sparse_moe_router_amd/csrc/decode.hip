@@ -202,40 +202,40 @@ __global__ __launch_bounds__(1024) void k_dec_down(const uint16_t* __restrict__ 
 
 hipError_t launch_decode_router_shared(const uint16_t* x, const uint16_t* wr, const float* bias,
                                        const uint16_t* shared_w, float* logits, float* h_s,
-                                       const Plan& p, hipStream_t s) {
+                                       const Plan& p, const Launch& lc) {
   const int nrouter = (p.E + 3) / 4;
   const int nshared = p.shared ? (p.Is + 3) / 4 : 0;
-  hipLaunchKernelGGL(k_dec_router_shared, dim3(nrouter + nshared), dim3(256), 0, s, x, wr, bias,
+  launch(lc, k_dec_router_shared, dim3(nrouter + nshared), dim3(256), x, wr, bias,
                      shared_w, logits, h_s, p.H, p.E, p.shared ? p.Is : 0, nrouter);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const float* logits,
-                                int32_t* ids, float* w, float* h_r, const Plan& p, hipStream_t s) {
+                                int32_t* ids, float* w, float* h_r, const Plan& p, const Launch& lc) {
   // p.I == 0 requests the selection only (routing without expert work)
   const int blocks = p.I > 0 ? p.k * ((p.I + 3) / 4) : 1;
   dim3 g(blocks), b(256);
   if (p.E <= 64)
-    hipLaunchKernelGGL(k_dec_gateup<1>, g, b, 0, s, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
+    launch(lc, k_dec_gateup<1>, g, b, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
   else if (p.E <= 128)
-    hipLaunchKernelGGL(k_dec_gateup<2>, g, b, 0, s, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
+    launch(lc, k_dec_gateup<2>, g, b, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
   else if (p.E <= 256)
-    hipLaunchKernelGGL(k_dec_gateup<4>, g, b, 0, s, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
+    launch(lc, k_dec_gateup<4>, g, b, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
   else if (p.E <= 512)
-    hipLaunchKernelGGL(k_dec_gateup<8>, g, b, 0, s, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
+    launch(lc, k_dec_gateup<8>, g, b, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
   else
-    hipLaunchKernelGGL(k_dec_gateup<16>, g, b, 0, s, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
+    launch(lc, k_dec_gateup<16>, g, b, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w, const int32_t* ids,
                               const float* w, const float* h_dec, uint16_t* out, const Plan& p,
-                              hipStream_t s) {
+                              const Launch& lc) {
   const float* h_r = h_dec;
   const float* h_s = h_dec + (int64_t)p.k * p.I;
   const int nslot = p.k + (p.shared ? 1 : 0);
   const int waves = nslot < 16 ? nslot : 16;
-  hipLaunchKernelGGL(k_dec_down, dim3((p.H + DR - 1) / DR), dim3(64 * waves), 0, s, expert_w,
+  launch(lc, k_dec_down, dim3((p.H + DR - 1) / DR), dim3(64 * waves), expert_w,
                      p.shared ? shared_w : nullptr, ids, w, h_r, h_s, out, p.H, p.I, p.Is, p.k, nslot);
   return hipGetLastError();
 }

@@ -317,7 +317,7 @@ unsigned xcd_grid(int64_t logical) { return (unsigned)(((logical + 7) / 8) * 8);
 
 hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
                               const int32_t* perm, const Tile* tiles, const int32_t* ntiles,
-                              uint16_t* h_r, uint16_t* h_s, const Plan& pl, hipStream_t s) {
+                              uint16_t* h_r, uint16_t* h_s, const Plan& pl, const Launch& lc) {
   GemmArgs a{};
   a.a_x = x;
   a.expert_w = expert_w;
@@ -336,13 +336,13 @@ hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const
   const int maxI = pl.I > pl.Is ? pl.I : pl.Is;
   a.npan = (maxI + NWR / 2 - 1) / (NWR / 2);
   a.max_tiles = (int)pl.max_tiles;
-  hipLaunchKernelGGL(k_grouped_gemm<0>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), 0, s, a);
+  launch(lc, k_grouped_gemm<0>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
                             const uint16_t* shared_w, const Tile* tiles, const int32_t* ntiles,
-                            uint16_t* y_r, uint16_t* y_s, const Plan& pl, hipStream_t s) {
+                            uint16_t* y_r, uint16_t* y_s, const Plan& pl, const Launch& lc) {
   GemmArgs a{};
   a.a_r = h_r;
   a.a_s = h_s;
@@ -360,13 +360,13 @@ hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint
   a.k = pl.k;
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
-  hipLaunchKernelGGL(k_grouped_gemm<1>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), 0, s, a);
+  launch(lc, k_grouped_gemm<1>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float* w, const int32_t* inv,
-                          uint16_t* out, const Plan& pl, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)pl.M), dim3(256), 0, s, y_r, pl.shared ? y_s : nullptr, w,
+                          uint16_t* out, const Plan& pl, const Launch& lc) {
+  launch(lc, k_combine, dim3((unsigned)pl.M), dim3(256), y_r, pl.shared ? y_s : nullptr, w,
                      inv, out, pl.H, pl.k);
   return hipGetLastError();
 }

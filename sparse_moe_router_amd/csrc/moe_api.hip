@@ -118,19 +118,23 @@ T* ws_ptr(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
 
-// Launches one kernel through `fn`, bracketed by the trace's events when a
-// trace slot is free.
+// Hands each launch the next pair of trace events (if any): the kernel is
+// then launched with hipExtLaunchKernelGGL, which stamps the events with the
+// kernel's own start and end.
 struct Tracer {
   moe_trace_t* t;
   hipStream_t s;
   template <class F>
   hipError_t run(moe_kernel_t id, F&& fn) {
     const bool rec = t && t->count < t->capacity;
-    hipError_t e;
-    if (rec && (e = hipEventRecord((hipEvent_t)t->begin[t->count], s)) != hipSuccess) return e;
-    if ((e = fn()) != hipSuccess) return e;
+    Launch lc{s, nullptr, nullptr};
     if (rec) {
-      if ((e = hipEventRecord((hipEvent_t)t->end[t->count], s)) != hipSuccess) return e;
+      lc.start = (hipEvent_t)t->begin[t->count];
+      lc.stop = (hipEvent_t)t->end[t->count];
+    }
+    const hipError_t e = fn(lc);
+    if (e != hipSuccess) return e;
+    if (rec) {
       if (t->kernel) t->kernel[t->count] = (int32_t)id;
       t->count++;
     }
@@ -148,24 +152,22 @@ moe_status_t run_routing_grouped(const Plan& p, const moe_desc_t* d, const void*
   int32_t* offsets = (r && r->offsets) ? r->offsets : ws_ptr<int32_t>(ws, p.offsets);
   int32_t* perm = (r && r->perm) ? r->perm : ws_ptr<int32_t>(ws, p.perm);
   hipError_t e;
-  if ((e = tr.run(MOE_K_ROUTER_SCORES, [&] {
-         return launch_router_logits((const uint16_t*)x, (const uint16_t*)wr, d->router_bias, L, p.M, p.H,
-                                     p.E, s);
+  uint64_t* cmask = ws_ptr<uint64_t>(ws, p.cmask);
+  if ((e = tr.run(MOE_K_ROUTER_SCORES, [&](const Launch& lc) {
+         return launch_router_logits((const uint16_t*)x, (const uint16_t*)wr, d->router_bias, L, cmask, p.M,
+                                     p.H, p.E, lc);
        })) != hipSuccess)
     return hip_fail(e);
-  if ((e = tr.run(MOE_K_TOPK, [&] {
-         return launch_topk_chunks(L, ids, w, ws_ptr<uint64_t>(ws, p.cmask), ws_ptr<int32_t>(ws, p.cbase),
-                                   p.M, p.E, p.k, s);
+  if ((e = tr.run(MOE_K_TOPK, [&](const Launch& lc) { return launch_topk(L, ids, w, cmask, p.M, p.E, p.k, lc); })) != hipSuccess)
+    return hip_fail(e);
+  if ((e = tr.run(MOE_K_ROUTE_SCAN, [&](const Launch& lc) {
+         return launch_route_scan(cmask, ws_ptr<int32_t>(ws, p.cbase), counts, offsets, ws_ptr<Tile>(ws, p.tiles),
+                                  ws_ptr<int32_t>(ws, p.ntiles), p.M, p.E, p.k, p.shared, lc);
        })) != hipSuccess)
     return hip_fail(e);
-  if ((e = tr.run(MOE_K_ROUTE_SCAN, [&] {
-         return launch_route_scan(ws_ptr<int32_t>(ws, p.cbase), counts, offsets, ws_ptr<Tile>(ws, p.tiles),
-                                  ws_ptr<int32_t>(ws, p.ntiles), p.M, p.E, p.k, p.shared, s);
-       })) != hipSuccess)
-    return hip_fail(e);
-  if ((e = tr.run(MOE_K_ROUTE_SCATTER, [&] {
+  if ((e = tr.run(MOE_K_ROUTE_SCATTER, [&](const Launch& lc) {
          return launch_route_scatter(ids, ws_ptr<uint64_t>(ws, p.cmask), ws_ptr<int32_t>(ws, p.cbase), perm,
-                                     ws_ptr<int32_t>(ws, p.inv), p.M, p.E, p.k, s);
+                                     ws_ptr<int32_t>(ws, p.inv), p.M, p.E, p.k, lc);
        })) != hipSuccess)
     return hip_fail(e);
   return MOE_OK;
@@ -222,15 +224,15 @@ moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const 
     int32_t* ids = (routing && routing->topk_ids) ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
     float* w = (routing && routing->topk_w) ? routing->topk_w : ws_ptr<float>(workspace, p.w);
     float* h = ws_ptr<float>(workspace, p.h_r);
-    if ((e = tr.run(MOE_K_DEC_ROUTER_SHARED, [&] {
+    if ((e = tr.run(MOE_K_DEC_ROUTER_SHARED, [&](const Launch& lc) {
            return launch_decode_router_shared(xb, (const uint16_t*)router_w, d->router_bias, sw, L,
-                                              h + (int64_t)p.k * p.I, p, s);
+                                              h + (int64_t)p.k * p.I, p, lc);
          })) != hipSuccess)
       return hip_fail(e);
-    if ((e = tr.run(MOE_K_DEC_GATEUP, [&] { return launch_decode_gateup(xb, ew, L, ids, w, h, p, s); })) !=
+    if ((e = tr.run(MOE_K_DEC_GATEUP, [&](const Launch& lc) { return launch_decode_gateup(xb, ew, L, ids, w, h, p, lc); })) !=
         hipSuccess)
       return hip_fail(e);
-    if ((e = tr.run(MOE_K_DEC_DOWN, [&] { return launch_decode_down(ew, sw, ids, w, h, (uint16_t*)out, p, s); })) !=
+    if ((e = tr.run(MOE_K_DEC_DOWN, [&](const Launch& lc) { return launch_decode_down(ew, sw, ids, w, h, (uint16_t*)out, p, lc); })) !=
         hipSuccess)
       return hip_fail(e);
     return MOE_OK;
@@ -244,16 +246,16 @@ moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const 
   uint16_t* y_s = ws_ptr<uint16_t>(workspace, p.y_s);
   const Tile* tiles = ws_ptr<Tile>(workspace, p.tiles);
   const int32_t* ntiles = ws_ptr<int32_t>(workspace, p.ntiles);
-  if ((e = tr.run(MOE_K_GEMM_GATEUP, [&] {
-         return launch_gemm_gateup(xb, ew, sw, perm, tiles, ntiles, h_r, h_s, p, s);
+  if ((e = tr.run(MOE_K_GEMM_GATEUP, [&](const Launch& lc) {
+         return launch_gemm_gateup(xb, ew, sw, perm, tiles, ntiles, h_r, h_s, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
-  if ((e = tr.run(MOE_K_GEMM_DOWN, [&] {
-         return launch_gemm_down(h_r, h_s, ew, sw, tiles, ntiles, y_r, y_s, p, s);
+  if ((e = tr.run(MOE_K_GEMM_DOWN, [&](const Launch& lc) {
+         return launch_gemm_down(h_r, h_s, ew, sw, tiles, ntiles, y_r, y_s, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
-  if ((e = tr.run(MOE_K_COMBINE, [&] {
-         return launch_combine(y_r, y_s, w, ws_ptr<int32_t>(workspace, p.inv), (uint16_t*)out, p, s);
+  if ((e = tr.run(MOE_K_COMBINE, [&](const Launch& lc) {
+         return launch_combine(y_r, y_s, w, ws_ptr<int32_t>(workspace, p.inv), (uint16_t*)out, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
   return MOE_OK;
@@ -293,9 +295,10 @@ moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w,
     float* w = routing->topk_w ? routing->topk_w : ws_ptr<float>(workspace, p.w);
     hipError_t e;
     if ((e = launch_decode_router_shared((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias,
-                                         nullptr, L, nullptr, q, s)) != hipSuccess)
+                                         nullptr, L, nullptr, q, Launch{s, nullptr, nullptr})) != hipSuccess)
       return hip_fail(e);
-    if ((e = launch_decode_gateup((const uint16_t*)x, nullptr, L, ids, w, nullptr, q, s)) != hipSuccess)
+    if ((e = launch_decode_gateup((const uint16_t*)x, nullptr, L, ids, w, nullptr, q, Launch{s, nullptr, nullptr})) !=
+        hipSuccess)
       return hip_fail(e);
     return MOE_OK;
   }

@@ -2,6 +2,7 @@
 // sparse MoE layer library (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -66,40 +67,58 @@ struct Plan {
 bool make_plan(Plan* p, int64_t M, int H, int E, int I, int Is, int k, bool gemv);
 
 // ----------------------------------------------------------------- launchers
-// All launchers enqueue on `s` and return hipGetLastError() of the launch.
+// All launchers enqueue on L.s and return hipGetLastError() of the launch.
+// When L carries events, the kernel is launched with hipExtLaunchKernelGGL,
+// which stamps them with the kernel's own start and end (the same interval
+// a kernel-trace profiler reports), for live per-kernel timing.
 
-// Router scores L[M][E] = x Wr^T (+ bias), fp32 (MFMA).
+struct Launch {
+  hipStream_t s;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+template <typename F, typename... Args>
+inline hipError_t launch(const Launch& L, F kernel, dim3 grid, dim3 block, Args... args) {
+  if (L.start || L.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, L.s, L.start, L.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, L.s, args...);
+  return hipGetLastError();
+}
+
+// Router scores L[M][E] = x Wr^T (+ bias), fp32 (MFMA); clears the chunk masks.
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, float* L,
-                                int64_t M, int H, int E, hipStream_t s);
-// Top-k + weights per token, and per-chunk expert bitmasks / counts.
-hipError_t launch_topk_chunks(const float* L, int32_t* ids, float* w, uint64_t* cmask, int32_t* cbase,
-                              int64_t M, int E, int k, hipStream_t s);
+                                uint64_t* cmask, int64_t M, int H, int E, const Launch& lc);
+// Top-k + weights per token, and the token's bits in the per-chunk expert masks.
+hipError_t launch_topk(const float* L, int32_t* ids, float* w, uint64_t* cmask, int64_t M, int E, int k,
+                       const Launch& lc);
 // counts, offsets, per-chunk bases, block map.
-hipError_t launch_route_scan(int32_t* cbase, int32_t* counts, int32_t* offsets, Tile* tiles,
-                             int32_t* ntiles, int64_t M, int E, int k, bool shared, hipStream_t s);
+hipError_t launch_route_scan(const uint64_t* cmask, int32_t* cbase, int32_t* counts, int32_t* offsets,
+                             Tile* tiles, int32_t* ntiles, int64_t M, int E, int k, bool shared, const Launch& lc);
 // perm / inv from the chunk masks and bases.
 hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const int32_t* cbase,
-                                int32_t* perm, int32_t* inv, int64_t M, int E, int k, hipStream_t s);
+                                int32_t* perm, int32_t* inv, int64_t M, int E, int k, const Launch& lc);
 // Grouped gate/up GEMM + SwiGLU -> h (bf16).
 hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
                               const int32_t* perm, const Tile* tiles, const int32_t* ntiles,
-                              uint16_t* h_r, uint16_t* h_s, const Plan& p, hipStream_t s);
+                              uint16_t* h_r, uint16_t* h_s, const Plan& p, const Launch& lc);
 // Grouped down GEMM -> y (bf16).
 hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
                             const uint16_t* shared_w, const Tile* tiles, const int32_t* ntiles,
-                            uint16_t* y_r, uint16_t* y_s, const Plan& p, hipStream_t s);
+                            uint16_t* y_r, uint16_t* y_s, const Plan& p, const Launch& lc);
 // out[t] = y_s[t] + sum_j w[t,j] y_r[inv[t*k+j]]  (bf16 out)
 hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float* w, const int32_t* inv,
-                          uint16_t* out, const Plan& p, hipStream_t s);
+                          uint16_t* out, const Plan& p, const Launch& lc);
 
 // Decode (M == 1) path.
 hipError_t launch_decode_router_shared(const uint16_t* x, const uint16_t* wr, const float* bias,
                                        const uint16_t* shared_w, float* logits, float* h_dec,
-                                       const Plan& p, hipStream_t s);
+                                       const Plan& p, const Launch& lc);
 hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const float* logits,
-                                int32_t* ids, float* w, float* h_dec, const Plan& p, hipStream_t s);
+                                int32_t* ids, float* w, float* h_dec, const Plan& p, const Launch& lc);
 hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w, const int32_t* ids,
                               const float* w, const float* h_dec, uint16_t* out, const Plan& p,
-                              hipStream_t s);
+                              const Launch& lc);
 
 }  // namespace moe

@@ -22,15 +22,18 @@ namespace {
 // ------------------------------------------------------------------ router scores
 
 // L[t][e] = sum_h x[t][h] * Wr[e][h] (+ bias[e]); fp32 accumulate on MFMA.
-// Tile 64 tokens x 64 experts, 4 waves in 2x2, each wave one 32x32 block,
-// K in steps of 64 staged through LDS (double buffered, XOR-swizzled rows).
+// Tile 64 tokens x 64 experts (= one routing chunk), 4 waves in 2x2, each
+// wave one 32x32 block, K in steps of 64 staged through LDS (double
+// buffered, XOR-swizzled rows).  The tile also clears its chunk's bitmask
+// words (cmask may be NULL on the decode path).
 // Global loads run RD steps ahead in a register ring (loads past the end
 // re-read the last step: never conditional, never out of bounds).
 constexpr int RD = 4;
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ wr,
                                                        const float* __restrict__ bias,
-                                                       float* __restrict__ L, int64_t M, int H,
+                                                       float* __restrict__ L,
+                                                       uint64_t* __restrict__ cmask, int64_t M, int H,
                                                        int E) {
   __shared__ u32x4_t sA[2][64 * 8];
   __shared__ u32x4_t sB[2][64 * 8];
@@ -38,6 +41,8 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   const int64_t t0 = (int64_t)blockIdx.x * 64;
   const int e0 = blockIdx.y * 64;
   const int wm = wave >> 1, wn = wave & 1;
+  // this tile's (chunk, expert) bitmask words start empty; top-k sets their bits
+  if (cmask && tid < 64 && e0 + tid < E) cmask[(int64_t)blockIdx.x * E + e0 + tid] = 0ull;
 
   // loader: 512 16-byte chunks per operand per step, two per thread
   const u32x4_t* srcA[2];
@@ -115,54 +120,30 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 
 // ------------------------------------------------------------------ top-k
 
-// One workgroup per chunk of 64 tokens, 16 waves x 4 tokens.  Writes ids and
-// weights per token, and per (chunk, expert) the token bitmask and its count.
+// One wave per token (4 per workgroup): top-k, weights, and the token's bit
+// in each selected expert's (chunk, expert) mask (64-bit atomicOr: the
+// result does not depend on the order of the ORs).
 template <int EPL>
-__global__ __launch_bounds__(1024) void k_topk_chunks(const float* __restrict__ L,
-                                                      int32_t* __restrict__ ids,
-                                                      float* __restrict__ w,
-                                                      uint64_t* __restrict__ cmask,
-                                                      int32_t* __restrict__ ccount, int64_t M, int E,
-                                                      int k) {
-  __shared__ uint32_t mlo[kMaxE], mhi[kMaxE];
-  __shared__ uint64_t s_keys[16][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t c = blockIdx.x;
-  for (int e = tid; e < E; e += 1024) mlo[e] = mhi[e] = 0;
-  __syncthreads();
-  // all four tokens' scores in flight at once
-  float f[4][EPL];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = c * kChunk + wave * 4 + i;
-    load_scores<EPL>(L + (t < M ? t : M - 1) * E, E, lane, f[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tl = wave * 4 + i;  // token within the chunk
-    const int64_t t = c * kChunk + tl;
-    if (t >= M) break;
-    uint64_t top;
-    const uint64_t mine = wave_topk<EPL>(f[i], E, k, lane, &top, s_keys[wave]);
-    const float l0 = from_orderable((uint32_t)(top >> 32));
-    const float lj = from_orderable((uint32_t)(mine >> 32));
-    const int ej = (int)(0xFFFFFFFFu - (uint32_t)mine);
-    const float ex = lane < k ? expf(lj - l0) : 0.0f;
-    const float sum = wave_sum(ex);
-    if (lane < k) {
-      ids[t * k + lane] = ej;
-      w[t * k + lane] = ex / sum;
-      if (tl < 32)
-        atomicOr(&mlo[ej], 1u << tl);
-      else
-        atomicOr(&mhi[ej], 1u << (tl - 32));
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += 1024) {
-    const uint32_t lo = mlo[e], hi = mhi[e];
-    cmask[c * E + e] = ((uint64_t)hi << 32) | lo;
-    ccount[c * E + e] = __popc(lo) + __popc(hi);
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ L, int32_t* __restrict__ ids,
+                                              float* __restrict__ w, uint64_t* __restrict__ cmask,
+                                              int64_t M, int E, int k) {
+  __shared__ uint64_t s_keys[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= M) return;
+  float f[EPL];
+  load_scores<EPL>(L + t * E, E, lane, f);
+  uint64_t top;
+  const uint64_t mine = wave_topk<EPL>(f, E, k, lane, &top, s_keys[wave]);
+  const float l0 = from_orderable((uint32_t)(top >> 32));
+  const float lj = from_orderable((uint32_t)(mine >> 32));
+  const int ej = (int)(0xFFFFFFFFu - (uint32_t)mine);
+  const float ex = lane < k ? expf(lj - l0) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    ids[t * k + lane] = ej;
+    w[t * k + lane] = ex / sum;
+    atomicOr((unsigned long long*)&cmask[(t / kChunk) * E + ej], 1ull << (t % kChunk));
   }
 }
 
@@ -197,9 +178,11 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   return r;
 }
 
-// Single workgroup.  cbase holds per-(chunk, expert) counts on entry and the
-// group position of the chunk's first assignment to that expert on exit.
-__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cbase,
+// Single workgroup.  Reads the per-(chunk, expert) masks, writes counts,
+// offsets, the block map, and cbase = the group position of the chunk's
+// first assignment to each expert.
+__global__ __launch_bounds__(1024) void k_route_scan(const uint64_t* __restrict__ cmask,
+                                                     int32_t* __restrict__ cbase,
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets,
                                                      Tile* __restrict__ tiles,
@@ -221,13 +204,13 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cbase
   {
     int64_t c = c0;
     for (; c + 8 <= c1; c += 8) {  // eight independent loads in flight
-      int v[8];
+      uint64_t v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = cbase[(c + j) * E + e];
+      for (int j = 0; j < 8; ++j) v[j] = cmask[(c + j) * E + e];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) psum += v[j];
+      for (int j = 0; j < 8; ++j) psum += __popcll(v[j]);
     }
-    for (; c < c1; ++c) psum += cbase[c * E + e];
+    for (; c < c1; ++c) psum += __popcll(cmask[c * E + e]);
   }
   s_part[tid] = active ? psum : 0;
   __syncthreads();
@@ -281,19 +264,18 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ cbase
     int run = s_part[tid];
     int64_t c = c0;
     for (; c + 8 <= c1; c += 8) {
-      int v[8];
+      uint64_t v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = cbase[(c + j) * E + e];
+      for (int j = 0; j < 8; ++j) v[j] = cmask[(c + j) * E + e];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         cbase[(c + j) * E + e] = run;
-        run += v[j];
+        run += __popcll(v[j]);
       }
     }
     for (; c < c1; ++c) {
-      const int v = cbase[c * E + e];
       cbase[c * E + e] = run;
-      run += v;
+      run += __popcll(cmask[c * E + e]);
     }
   }
 }
@@ -326,39 +308,39 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, float* L,
-                                int64_t M, int H, int E, hipStream_t s) {
+                                uint64_t* cmask, int64_t M, int H, int E, const Launch& lc) {
   dim3 grid((unsigned)((M + 63) / 64), (unsigned)((E + 63) / 64));
-  hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, wr, bias, L, M, H, E);
+  launch(lc, k_router_logits, grid, dim3(256), x, wr, bias, L, cmask, M, H, E);
   return hipGetLastError();
 }
 
-hipError_t launch_topk_chunks(const float* L, int32_t* ids, float* w, uint64_t* cmask, int32_t* cbase,
-                              int64_t M, int E, int k, hipStream_t s) {
-  dim3 grid((unsigned)((M + kChunk - 1) / kChunk));
+hipError_t launch_topk(const float* L, int32_t* ids, float* w, uint64_t* cmask, int64_t M, int E, int k,
+                       const Launch& lc) {
+  dim3 grid((unsigned)((M + 3) / 4));
   if (E <= 64)
-    hipLaunchKernelGGL(k_topk_chunks<1>, grid, dim3(1024), 0, s, L, ids, w, cmask, cbase, M, E, k);
+    launch(lc, k_topk<1>, grid, dim3(256), L, ids, w, cmask, M, E, k);
   else if (E <= 128)
-    hipLaunchKernelGGL(k_topk_chunks<2>, grid, dim3(1024), 0, s, L, ids, w, cmask, cbase, M, E, k);
+    launch(lc, k_topk<2>, grid, dim3(256), L, ids, w, cmask, M, E, k);
   else if (E <= 256)
-    hipLaunchKernelGGL(k_topk_chunks<4>, grid, dim3(1024), 0, s, L, ids, w, cmask, cbase, M, E, k);
+    launch(lc, k_topk<4>, grid, dim3(256), L, ids, w, cmask, M, E, k);
   else if (E <= 512)
-    hipLaunchKernelGGL(k_topk_chunks<8>, grid, dim3(1024), 0, s, L, ids, w, cmask, cbase, M, E, k);
+    launch(lc, k_topk<8>, grid, dim3(256), L, ids, w, cmask, M, E, k);
   else
-    hipLaunchKernelGGL(k_topk_chunks<16>, grid, dim3(1024), 0, s, L, ids, w, cmask, cbase, M, E, k);
+    launch(lc, k_topk<16>, grid, dim3(256), L, ids, w, cmask, M, E, k);
   return hipGetLastError();
 }
 
-hipError_t launch_route_scan(int32_t* cbase, int32_t* counts, int32_t* offsets, Tile* tiles,
-                             int32_t* ntiles, int64_t M, int E, int k, bool shared, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, cbase, counts, offsets, tiles, ntiles, M,
-                     E, k, shared ? 1 : 0);
+hipError_t launch_route_scan(const uint64_t* cmask, int32_t* cbase, int32_t* counts, int32_t* offsets,
+                             Tile* tiles, int32_t* ntiles, int64_t M, int E, int k, bool shared, const Launch& lc) {
+  launch(lc, k_route_scan, dim3(1), dim3(1024), cmask, cbase, counts, offsets, tiles, ntiles,
+                     M, E, k, shared ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const int32_t* cbase,
-                                int32_t* perm, int32_t* inv, int64_t M, int E, int k, hipStream_t s) {
+                                int32_t* perm, int32_t* inv, int64_t M, int E, int k, const Launch& lc) {
   dim3 grid((unsigned)((M + kChunk - 1) / kChunk));
-  hipLaunchKernelGGL(k_route_scatter, grid, dim3(256), 0, s, ids, cmask, cbase, perm, inv, M, E, k);
+  launch(lc, k_route_scatter, grid, dim3(256), ids, cmask, cbase, perm, inv, M, E, k);
   return hipGetLastError();
 }
 
