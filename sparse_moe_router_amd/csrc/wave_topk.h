@@ -21,10 +21,26 @@ __device__ __forceinline__ uint64_t sel_key(float f, int e) {
   return ((uint64_t)orderable(f) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
+// DPP move of v (lanes whose source is outside the row or masked off read 0).
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                               BANK_MASK, true));
+}
+
+// Sum over the 64 lanes of a wave (all lanes active), in every lane.  Data
+// parallel primitives on the VALU, no LDS round trips: shift-and-add within
+// each 16-lane row (row_shr 1, 2, 4, 8 leave the row's sum in its lane 15),
+// then row_bcast:15 adds row 0 into row 1 and row 2 into row 3, and
+// row_bcast:31 adds lane 31 into rows 2 and 3, so lane 63 holds the total.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v += dpp_move<0x111>(v);       // row_shr:1
+  v += dpp_move<0x112>(v);       // row_shr:2
+  v += dpp_move<0x114>(v);       // row_shr:4
+  v += dpp_move<0x118>(v);       // row_shr:8
+  v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // One wave selects the top k of E scores of one token; lane l holds the
