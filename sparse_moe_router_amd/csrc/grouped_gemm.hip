@@ -60,8 +60,7 @@ constexpr int BK = 64;        // K per pipeline step
 constexpr int CPR = BK / 8;   // 16-byte chunks per row per step
 constexpr int KK = BK / 16;   // MFMA sub-steps per step
 constexpr int DB = 2;         // weight steps in flight
-constexpr int DA = 2;         // activation steps in flight
-constexpr int U = 2;          // unroll (ring slots are fixed registers)
+constexpr int U = 2;          // unroll: a multiple of DB and of the 2 LDS buffers
 constexpr int LDS_A = 2 * BM * CPR;  // two activation buffers, 16-byte units (64 KB)
 
 __device__ __forceinline__ int swz(int row, int q) { return row * CPR + (q ^ (row & (CPR - 1))); }
@@ -71,14 +70,21 @@ __device__ __forceinline__ int swz(int row, int q) { return row * CPR + (q ^ (ro
 // same columns (col block 1), so SwiGLU is lane-local.  MODE 1: y = A Wd^T
 // over a 256-column panel of H; wave w owns columns [n0+64w, +64).
 //
-// K runs in steps of BK with a register pipeline: the weight fragments of
-// step s+DB and the activation chunks of step s+DA are in flight while step
-// s multiplies; the activation chunks of step s+1 go to the other LDS buffer
-// at the end of step s.  Within a step, MFMA sub-step kk and lane half h
-// take the 8 K-values 32h+8kk .. 32h+8kk+7 on both operands, a consistent
-// permutation of K that lets each lane read 16 contiguous bytes.  Loads past
-// the last step re-read the last step (never out of bounds, never
-// conditional), so no control flow surrounds memory operations.
+// K runs in steps of BK with register pipelines.  Weights: DB ring slots;
+// as soon as the MFMAs of sub-step kk have read their weight fragments, the
+// slot's fragment kk is refilled with the same chunk DB steps ahead, so the
+// weight loads spread through the MFMA phase and about DB steps of weights
+// stay in flight.  Activations: the chunks of step s+1 are written to the
+// other LDS buffer at the start of step s; they were loaded one step
+// earlier, before that step's weight loads, so waiting for them (loads
+// complete in issue order) never waits for the newer weight loads.  The
+// activation fragments are double-buffered across MFMA sub-steps, so the
+// LDS reads of sub-step kk+1 overlap the MFMAs of sub-step kk.  Within a
+// step, MFMA sub-step kk and lane half h take the 8 K-values
+// 32h+8kk .. 32h+8kk+7 on both operands, a consistent permutation of K that
+// lets each lane read 16 contiguous bytes.  Loads past the last step
+// re-read the last step (never out of bounds, never conditional), so no
+// control flow surrounds memory operations.
 template <int MODE, int NRB>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int panel, u32x4_t* smem) {
   constexpr int ACH = NRB * 32 * CPR / 256;  // activation chunks per thread per step
@@ -140,22 +146,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
 
   const int nsteps = K / BK;
   u32x4_t breg[DB][2][KK];
-  u32x4_t areg[DA][ACH];
-  auto load_b = [&](u32x4_t (&r)[2][KK], int st) {
-    const int c0 = (st < nsteps ? st : nsteps - 1) * CPR;
+  u32x4_t areg[ACH];
+  auto chunk0 = [&](int st) { return (st < nsteps ? st : nsteps - 1) * CPR; };
+  auto load_a = [&](int st) {
+    const int c0 = chunk0(st);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) r[cb][kk] = bsrc[cb][c0 + kk];
+    for (int i = 0; i < ACH; ++i) areg[i] = asrc[i][c0];
   };
-  auto load_a = [&](u32x4_t (&r)[ACH], int st) {
-    const int c0 = (st < nsteps ? st : nsteps - 1) * CPR;
+  auto store_a = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) r[i] = asrc[i][c0];
-  };
-  auto store_a = [&](const u32x4_t (&r)[ACH], int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) sA[buf][adst[i]] = r[i];
+    for (int i = 0; i < ACH; ++i) sA[buf][adst[i]] = areg[i];
   };
 
   f32x16_t acc[NRB][2];
@@ -164,39 +164,53 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = (f32x16_t){};
 
-  // prologue
-  load_a(areg[0], 0);
-  load_b(breg[0], 0);
-  load_a(areg[1], 1);
-  load_b(breg[1], 1);
-  store_a(areg[0], 0);
+  // prologue: activation step 0 -> LDS buffer 0, weight steps 0 .. DB-1 in
+  // flight, activation step 1 in registers
+  load_a(0);
+#pragma unroll
+  for (int d = 0; d < DB; ++d)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) breg[d][cb][kk] = bsrc[cb][chunk0(d) + kk];
+  store_a(0);
+  load_a(1);
   __syncthreads();
 
+  // step s: weight slot s % DB, LDS buffer s % 2 (step s+1 goes to the other one)
   for (int s0 = 0; s0 < nsteps; s0 += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u;
-      // a step past the end (odd nsteps) only repeats the clamped loads and
-      // the barrier, so every wave runs the same barriers
-      if (wave_cols && s < nsteps) {
+      const int ub = u % DB;
+      store_a((u + 1) & 1);
+      load_a(s + 2);
+      const int cn = chunk0(s + DB);
+      const bool active = wave_cols && s < nsteps;
+      u32x4_t af[2][NRB];
+      auto read_af = [&](u32x4_t (&f)[NRB], int kk) {
+        const int q = (CPR / 2) * half + kk;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          u32x4_t af[NRB];
-          const int q = (CPR / 2) * half + kk;
+        for (int rb = 0; rb < NRB; ++rb) f[rb] = sA[u & 1][swz(32 * rb + l32, q)];
+      };
+      if (active) read_af(af[0], 0);
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) af[rb] = sA[u][swz(32 * rb + l32, q)];
+      for (int kk = 0; kk < KK; ++kk) {
+        // a step past the end (odd nsteps) only repeats the clamped loads and
+        // the barrier, so every wave runs the same barriers
+        if (active) {
+          if (kk + 1 < KK) read_af(af[(kk + 1) & 1], kk + 1);
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
               acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8_t, af[rb]), __builtin_bit_cast(bf16x8_t, breg[u][cb][kk]),
+                  __builtin_bit_cast(bf16x8_t, af[kk & 1][rb]), __builtin_bit_cast(bf16x8_t, breg[ub][cb][kk]),
                   acc[rb][cb], 0, 0, 0);
         }
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) breg[ub][cb][kk] = bsrc[cb][cn + kk];
       }
-      load_b(breg[u], s + DB);
-      load_a(areg[u], s + DA);
-      store_a(areg[u ^ 1], u ^ 1);
       __syncthreads();
     }
   }
