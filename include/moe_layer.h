@@ -135,8 +135,8 @@ typedef enum {
   MOE_K_GEMM_GATEUP = 5,       /* grouped path: gate/up GEMM + gated activation */
   MOE_K_GEMM_DOWN = 6,         /* grouped path: down GEMM */
   MOE_K_COMBINE = 7,           /* grouped path: weighted combine + shared expert */
-  MOE_K_DEC_ROUTER_SHARED = 8, /* decode: router scores and shared expert gate/up */
-  MOE_K_DEC_GATEUP = 9,        /* decode: top-k and routed experts' gate/up */
+  MOE_K_DEC_ROUTER = 8,        /* decode: router scores */
+  MOE_K_DEC_GATEUP = 9,        /* decode: shared expert gate/up, top-k, routed gate/up */
   MOE_K_DEC_DOWN = 10          /* decode: down projections + combine */
 } moe_kernel_t;
 

@@ -13,10 +13,10 @@
 // Three kernels per layer, all streaming bf16 weight rows with 16-byte loads
 // (64 lanes x 16 B = 1 KB contiguous per load instruction) and fp32 wave
 // reductions:
-//   1. router scores (one wave per expert) and, independent of routing, the
-//      shared expert's gate/up rows + SiLU gate (one wave per row);
-//   2. top-k (recomputed by each workgroup from the scores) and the selected
-//      experts' gate/up rows + SiLU gate;
+//   1. router scores (one wave per expert);
+//   2. the shared expert's gate/up rows + SiLU gate, which stream while the
+//      other workgroups select the top k from the scores (each workgroup
+//      selects for itself), then the selected experts' gate/up rows + SiLU;
 //   3. the down projection: one wave per (expert slot, 4 output rows), the
 //      weighted slot partials summed in slot order through LDS.
 #include "moe_internal.h"
@@ -60,45 +60,47 @@ __device__ __forceinline__ void wave_dots(const uint16_t* __restrict__ x, const 
   if (TWO) *d2 = wave_sum(a2);
 }
 
-// Workgroups [0, nrouter) score experts (one wave per expert), the rest
-// compute the shared expert's gated activation (one wave per row).
-__global__ __launch_bounds__(256) void k_dec_router_shared(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ wr,
-                                                           const float* __restrict__ bias,
-                                                           const uint16_t* __restrict__ shared_w,
-                                                           float* __restrict__ logits,
-                                                           float* __restrict__ h_s, int H, int E,
-                                                           int Is, int nrouter) {
+// Router scores: one wave per expert.
+__global__ __launch_bounds__(256) void k_dec_router(const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ wr,
+                                                    const float* __restrict__ bias,
+                                                    float* __restrict__ logits, int H, int E) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if ((int)blockIdx.x < nrouter) {
-    const int e = blockIdx.x * 4 + wave;
-    if (e >= E) return;
-    float v, unused;
-    wave_dots<false>(x, wr + (int64_t)e * H, nullptr, H, lane, &v, &unused);
-    if (lane == 0) logits[e] = v + (bias ? bias[e] : 0.0f);
-  } else {
-    const int i = (blockIdx.x - nrouter) * 4 + wave;
+  const int e = blockIdx.x * 4 + wave;
+  if (e >= E) return;
+  float v, unused;
+  wave_dots<false>(x, wr + (int64_t)e * H, nullptr, H, lane, &v, &unused);
+  if (lane == 0) logits[e] = v + (bias ? bias[e] : 0.0f);
+}
+
+// Gated activations of the shared and the selected experts, one wave per
+// (gate, up) row pair.  Workgroups [0, nshared) take the shared expert's
+// rows, which do not depend on the routing, so they stream while the other
+// workgroups select: there wave 0 takes the top k of the E scores into LDS,
+// then wave w computes row i = 4*(b % row_blocks) + w of slot j's expert.
+// The first routed workgroup also publishes ids / weights.  With I == 0 only
+// the selection runs.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ expert_w,
+                                                    const uint16_t* __restrict__ shared_w,
+                                                    const float* __restrict__ logits,
+                                                    int32_t* __restrict__ ids,
+                                                    float* __restrict__ wts,
+                                                    float* __restrict__ h_r, float* __restrict__ h_s,
+                                                    int H, int E, int I, int Is, int k, int nshared) {
+  __shared__ int32_t s_ids[kMaxTopK];
+  __shared__ uint64_t s_keys[64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x < nshared) {
+    const int i = blockIdx.x * 4 + wave;
     if (i >= Is) return;
     float g, u;
     wave_dots<true>(x, shared_w + (int64_t)i * H, shared_w + ((int64_t)Is + i) * H, H, lane, &g, &u);
     if (lane == 0) h_s[i] = silu(g) * u;
+    return;
   }
-}
-
-// Each workgroup: wave 0 selects the top k from the E scores into LDS; then
-// wave w computes row i = 4*(blockIdx % rows_blocks) + w of slot j's expert.
-// Workgroup 0 also publishes ids / weights.  With I == 0 only the selection runs.
-template <int EPL>
-__global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__ x,
-                                                    const uint16_t* __restrict__ expert_w,
-                                                    const float* __restrict__ logits,
-                                                    int32_t* __restrict__ ids,
-                                                    float* __restrict__ wts,
-                                                    float* __restrict__ h_r, int H, int E, int I,
-                                                    int k) {
-  __shared__ int32_t s_ids[kMaxTopK];
-  __shared__ uint64_t s_keys[64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.x - nshared;
   if (wave == 0) {
     uint64_t top;
     float f[EPL];
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
     const uint64_t mine = wave_topk<EPL>(f, E, k, lane, &top, s_keys);
     const int ej = (int)(0xFFFFFFFFu - (uint32_t)mine);
     if (lane < k) s_ids[lane] = ej;
-    if (blockIdx.x == 0) {
+    if (b == 0) {
       const float l0 = from_orderable((uint32_t)(top >> 32));
       const float lj = from_orderable((uint32_t)(mine >> 32));
       const float ex = lane < k ? expf(lj - l0) : 0.0f;
@@ -120,8 +122,8 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
   __syncthreads();
   if (I == 0) return;
   const int rblocks = (I + 3) / 4;
-  const int j = blockIdx.x / rblocks;
-  const int i = (blockIdx.x % rblocks) * 4 + wave;
+  const int j = b / rblocks;
+  const int i = (b % rblocks) * 4 + wave;
   if (j >= k || i >= I) return;
   const uint16_t* W = expert_w + (int64_t)s_ids[j] * 3 * I * H;
   float g, u;
@@ -200,32 +202,28 @@ __global__ __launch_bounds__(1024) void k_dec_down(const uint16_t* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_decode_router_shared(const uint16_t* x, const uint16_t* wr, const float* bias,
-                                       const uint16_t* shared_w, float* logits, float* h_s,
-                                       const Plan& p, const Launch& lc) {
-  const int nrouter = (p.E + 3) / 4;
-  const int nshared = p.shared ? (p.Is + 3) / 4 : 0;
-  launch(lc, k_dec_router_shared, dim3(nrouter + nshared), dim3(256), x, wr, bias,
-                     shared_w, logits, h_s, p.H, p.E, p.shared ? p.Is : 0, nrouter);
-  return hipGetLastError();
+hipError_t launch_decode_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                                const Plan& p, const Launch& lc) {
+  return launch(lc, k_dec_router, dim3((p.E + 3) / 4), dim3(256), x, wr, bias, logits, p.H, p.E);
 }
 
-hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const float* logits,
-                                int32_t* ids, float* w, float* h_r, const Plan& p, const Launch& lc) {
+hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
+                                const float* logits, int32_t* ids, float* w, float* h_dec, const Plan& p,
+                                const Launch& lc) {
   // p.I == 0 requests the selection only (routing without expert work)
-  const int blocks = p.I > 0 ? p.k * ((p.I + 3) / 4) : 1;
-  dim3 g(blocks), b(256);
+  const int nshared = p.shared && p.I > 0 ? (p.Is + 3) / 4 : 0;
+  const int blocks = nshared + (p.I > 0 ? p.k * ((p.I + 3) / 4) : 1);
+  float* h_s = h_dec + (int64_t)p.k * p.I;
+  const dim3 g(blocks), b(256);
   if (p.E <= 64)
-    launch(lc, k_dec_gateup<1>, g, b, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
-  else if (p.E <= 128)
-    launch(lc, k_dec_gateup<2>, g, b, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
-  else if (p.E <= 256)
-    launch(lc, k_dec_gateup<4>, g, b, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
-  else if (p.E <= 512)
-    launch(lc, k_dec_gateup<8>, g, b, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
-  else
-    launch(lc, k_dec_gateup<16>, g, b, x, expert_w, logits, ids, w, h_r, p.H, p.E, p.I, p.k);
-  return hipGetLastError();
+    return launch(lc, k_dec_gateup<1>, g, b, x, expert_w, shared_w, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+  if (p.E <= 128)
+    return launch(lc, k_dec_gateup<2>, g, b, x, expert_w, shared_w, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+  if (p.E <= 256)
+    return launch(lc, k_dec_gateup<4>, g, b, x, expert_w, shared_w, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+  if (p.E <= 512)
+    return launch(lc, k_dec_gateup<8>, g, b, x, expert_w, shared_w, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+  return launch(lc, k_dec_gateup<16>, g, b, x, expert_w, shared_w, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
 }
 
 hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w, const int32_t* ids,
@@ -235,9 +233,8 @@ hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w
   const float* h_s = h_dec + (int64_t)p.k * p.I;
   const int nslot = p.k + (p.shared ? 1 : 0);
   const int waves = nslot < 16 ? nslot : 16;
-  launch(lc, k_dec_down, dim3((p.H + DR - 1) / DR), dim3(64 * waves), expert_w,
-                     p.shared ? shared_w : nullptr, ids, w, h_r, h_s, out, p.H, p.I, p.Is, p.k, nslot);
-  return hipGetLastError();
+  return launch(lc, k_dec_down, dim3((p.H + DR - 1) / DR), dim3(64 * waves), expert_w,
+                p.shared ? shared_w : nullptr, ids, w, h_r, h_s, out, p.H, p.I, p.Is, p.k, nslot);
 }
 
 }  // namespace moe

@@ -224,12 +224,11 @@ moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const 
     int32_t* ids = (routing && routing->topk_ids) ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
     float* w = (routing && routing->topk_w) ? routing->topk_w : ws_ptr<float>(workspace, p.w);
     float* h = ws_ptr<float>(workspace, p.h_r);
-    if ((e = tr.run(MOE_K_DEC_ROUTER_SHARED, [&](const Launch& lc) {
-           return launch_decode_router_shared(xb, (const uint16_t*)router_w, d->router_bias, sw, L,
-                                              h + (int64_t)p.k * p.I, p, lc);
+    if ((e = tr.run(MOE_K_DEC_ROUTER, [&](const Launch& lc) {
+           return launch_decode_router(xb, (const uint16_t*)router_w, d->router_bias, L, p, lc);
          })) != hipSuccess)
       return hip_fail(e);
-    if ((e = tr.run(MOE_K_DEC_GATEUP, [&](const Launch& lc) { return launch_decode_gateup(xb, ew, L, ids, w, h, p, lc); })) !=
+    if ((e = tr.run(MOE_K_DEC_GATEUP, [&](const Launch& lc) { return launch_decode_gateup(xb, ew, sw, L, ids, w, h, p, lc); })) !=
         hipSuccess)
       return hip_fail(e);
     if ((e = tr.run(MOE_K_DEC_DOWN, [&](const Launch& lc) { return launch_decode_down(ew, sw, ids, w, h, (uint16_t*)out, p, lc); })) !=
@@ -294,11 +293,11 @@ moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w,
     int32_t* ids = routing->topk_ids ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
     float* w = routing->topk_w ? routing->topk_w : ws_ptr<float>(workspace, p.w);
     hipError_t e;
-    if ((e = launch_decode_router_shared((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias,
-                                         nullptr, L, nullptr, q, Launch{s, nullptr, nullptr})) != hipSuccess)
+    if ((e = launch_decode_router((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias, L, q,
+                                  Launch{s, nullptr, nullptr})) != hipSuccess)
       return hip_fail(e);
-    if ((e = launch_decode_gateup((const uint16_t*)x, nullptr, L, ids, w, nullptr, q, Launch{s, nullptr, nullptr})) !=
-        hipSuccess)
+    if ((e = launch_decode_gateup((const uint16_t*)x, nullptr, nullptr, L, ids, w, nullptr, q,
+                                  Launch{s, nullptr, nullptr})) != hipSuccess)
       return hip_fail(e);
     return MOE_OK;
   }

@@ -114,11 +114,14 @@ hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float*
                           uint16_t* out, const Plan& p, const Launch& lc);
 
 // Decode (M == 1) path.
-hipError_t launch_decode_router_shared(const uint16_t* x, const uint16_t* wr, const float* bias,
-                                       const uint16_t* shared_w, float* logits, float* h_dec,
-                                       const Plan& p, const Launch& lc);
-hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const float* logits,
-                                int32_t* ids, float* w, float* h_dec, const Plan& p, const Launch& lc);
+// Router scores.
+hipError_t launch_decode_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                                const Plan& p, const Launch& lc);
+// Shared and selected experts' gated activations (h_dec: fp32 [k][I] routed,
+// then [Is] shared); top-k ids and weights.
+hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
+                                const float* logits, int32_t* ids, float* w, float* h_dec, const Plan& p,
+                                const Launch& lc);
 hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w, const int32_t* ids,
                               const float* w, const float* h_dec, uint16_t* out, const Plan& p,
                               const Launch& lc);
