@@ -19,6 +19,8 @@ give, in float64 (NumPy; matrix products go to BLAS dgemm):
 5. the always-on shared expert on every token ........ ``swiglu_ffn``
 6. weighted combine of the k expert outputs plus the
    shared expert's output ............................ ``moe_forward``
+7. (4-bit experts) weights rebuilt from 4-bit codes
+   and a scale and bias per group of 64 .............. ``dequant_q4``
 
 Sources (page title, then section):
 - "Optimizing on-device inference for Apple Silicon" (Perplexity, 2026),
@@ -32,7 +34,9 @@ Sources (page title, then section):
   projections go with their gated activation; the output projection goes
   with its routing score and the shared expert's result.
 - same page, "Dequantize weights during matrix multiplication": fp32
-  accumulation, bf16 output (the GPU kernels' precision; the oracle is fp64).
+  accumulation, bf16 output (the GPU kernels' precision; the oracle is fp64);
+  each weight a 4-bit integer code, each group of 64 weights sharing one
+  bf16 scale and one bf16 bias from which its values are rebuilt.
 
 The pages give the structure but no formulas; where they are silent the
 reading used is stated at the function (softmax scoring, renormalisation,
@@ -302,6 +306,52 @@ def dense_forward(x, router_w, experts: ExpertSource, shared, k: int, I: int,
     for e in range(E):
         out = out + Gm[:, e:e + 1] * swiglu_ffn(x, *get(e))
     return out
+
+
+# ---------------------------------------------------- 7. 4-bit group-affine weights
+#
+# "Dequantize weights during matrix multiplication": every weight is stored
+# as a 4-bit integer code and every group of 64 weights shares a bf16 scale
+# and a bf16 bias used to rebuild the weights.  Reading: the rebuilt weight
+# is the affine value w = s * q + b with q the unsigned code 0..15, groups of
+# 64 consecutive weights along a row's reduction dimension, and no further
+# rounding (the GPU matrix kernels round w to bf16 for their operands, as
+# they take x in bf16).  Storage (this library's layout): two codes per byte,
+# low nibble first; one 32-bit word per group, scale in the low 16 bits,
+# bias in the high 16 bits.
+
+Q4_GROUP = 64
+
+
+def bf16_value(bits) -> np.ndarray:
+    """Values of bfloat16 bit patterns (the high half of an IEEE binary32), float64."""
+    hi = (np.asarray(bits, dtype=np.uint64) & np.uint64(0xFFFF)).astype(np.uint32) << np.uint32(16)
+    return hi.view(np.float32).astype(np.float64)
+
+
+def q4_codes(packed) -> np.ndarray:
+    """Unsigned 4-bit codes, two per byte, low nibble first (uint8, length 2 * bytes)."""
+    b = np.asarray(packed, dtype=np.uint8).ravel()
+    q = np.empty(2 * b.size, dtype=np.uint8)
+    q[0::2] = b & np.uint8(0x0F)
+    q[1::2] = b >> np.uint8(4)
+    return q
+
+
+def dequant_q4(packed, scale_bias) -> np.ndarray:
+    """Weights of a 4-bit block, float64: w[i] = s[g] * q[i] + b[g] with g = i // 64.
+
+    packed: the codes (bytes); scale_bias: one uint32 word per group of 64.
+    Applied to a packed expert block (gate [I][H], up [I][H], down [H][I],
+    rows of a multiple of 64 values) it gives the packed fp64 expert block.
+    """
+    q = q4_codes(packed).astype(np.float64)
+    words = np.asarray(scale_bias, dtype=np.uint64).ravel()
+    if q.size != words.size * Q4_GROUP:
+        raise ValueError("4-bit block: codes and scale/bias groups do not match")
+    s = bf16_value(words)
+    b = bf16_value(words >> np.uint64(16))
+    return q * np.repeat(s, Q4_GROUP) + np.repeat(b, Q4_GROUP)
 
 
 def rel_err_per_token(y, ref) -> np.ndarray:

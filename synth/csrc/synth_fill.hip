@@ -38,9 +38,60 @@ __global__ void fill_kernel(uint16_t* __restrict__ dst, uint64_t key, uint64_t s
     dst[i] = variate_bf16(key, start + i, scale);
 }
 
+__global__ void fill_words_kernel(uint64_t* __restrict__ dst, uint64_t key, uint64_t n) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = mix64(key + (i + 1) * kGamma);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  const uint32_t bits = __float_as_uint(v);
+  return (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
+}
+
+__global__ void fill_sb_kernel(uint32_t* __restrict__ dst, uint64_t key, uint64_t n, float s0) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint64_t r = mix64(key + (i + 1) * kGamma);
+    const float u = (float)(uint32_t)((r >> 9) & 0x7FFFFFu) * 0x1p-23f;
+    const float v = (float)(uint32_t)(r >> 43) * 0x1p-21f;
+    const float sm = 0.5f + u;  // exact
+    const uint32_t sb = bf16_rne(s0 * sm);
+    const float sv = __uint_as_float(sb << 16);
+    const float m = 7.0f + v;  // exact
+    const uint32_t bb = bf16_rne(-(sv * m));
+    dst[i] = sb | (bb << 16);
+  }
+}
+
+unsigned blocks_for(uint64_t n) {
+  uint64_t b = (n + 255) / 256;
+  return (unsigned)(b > 65536 ? 65536 : b);
+}
+
 }  // namespace
 
 extern "C" {
+
+// 4-bit codes: dst receives nbytes bytes of stream `key` (output n -> bytes
+// 8(n-1) .. 8n-1, little-endian); nbytes must be a multiple of 8.
+int synth_fill_q4_codes(void* dst, uint64_t key, uint64_t nbytes, void* stream) {
+  if (nbytes == 0) return 0;
+  if (dst == nullptr || nbytes % 8) return (int)hipErrorInvalidValue;
+  const uint64_t n = nbytes / 8;
+  hipLaunchKernelGGL(fill_words_kernel, dim3(blocks_for(n)), dim3(256), 0, (hipStream_t)stream, (uint64_t*)dst,
+                     key, n);
+  return (int)hipGetLastError();
+}
+
+// 4-bit scale/bias words of ngroups groups (s0 = sigma / 4.61 in fp32).
+int synth_fill_q4_scale_bias(void* dst, uint64_t key, uint64_t ngroups, float s0, void* stream) {
+  if (ngroups == 0) return 0;
+  if (dst == nullptr) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(fill_sb_kernel, dim3(blocks_for(ngroups)), dim3(256), 0, (hipStream_t)stream,
+                     (uint32_t*)dst, key, ngroups, s0);
+  return (int)hipGetLastError();
+}
 
 // dst: device buffer of n uint16 (bf16 bits).  Element j receives stream
 // element start+j.  Returns 0 or the hipError_t of the launch.

@@ -25,6 +25,11 @@ def _L():
         L.synth_fill_normal_bf16.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
                                              ctypes.c_float, ctypes.c_void_p]
         L.synth_fill_normal_bf16.restype = ctypes.c_int
+        L.synth_fill_q4_codes.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]
+        L.synth_fill_q4_codes.restype = ctypes.c_int
+        L.synth_fill_q4_scale_bias.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_float,
+                                               ctypes.c_void_p]
+        L.synth_fill_q4_scale_bias.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -55,3 +60,38 @@ def layer_tensors(w: S.Workload, layer: int = 0, device="cuda", x_rows: int = No
         sh = torch.empty(w.shared_elems(), dtype=torch.bfloat16, device=device)
         fill(sh, S.shared_key(w, layer), 0, w.w_sigma)
     return x, r, ex, sh
+
+
+def fill_q4(codes: torch.Tensor, sb: torch.Tensor, code_key: int, sb_key: int, sigma: float, stream=None):
+    """4-bit expert block: codes (uint8, nbytes % 8 == 0) and scale/bias words (int32 view of uint32)."""
+    assert codes.is_cuda and codes.dtype == torch.uint8 and codes.is_contiguous()
+    assert sb.is_cuda and sb.dtype == torch.int32 and sb.is_contiguous()
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    rc = _L().synth_fill_q4_codes(codes.data_ptr(), code_key & S.MASK64, codes.numel(), s)
+    if rc == 0:
+        rc = _L().synth_fill_q4_scale_bias(sb.data_ptr(), sb_key & S.MASK64, sb.numel(),
+                                           ctypes.c_float(float(S.q4_s0(sigma))), s)
+    if rc != 0:
+        raise RuntimeError(f"synth q4 fill failed: hipError {rc}")
+
+
+def layer_tensors_q4(w: S.Workload, layer: int = 0, device="cuda", x_rows: int = None, x_row0: int = 0):
+    """x [rows,H], router [E,H] (bf16); expert codes [E, 3IH/2] uint8 and scale/bias [E, 3IH/64]
+    int32; shared codes / scale-bias (or None) on the device."""
+    rows = w.M if x_rows is None else x_rows
+    x = torch.empty(rows, w.H, dtype=torch.bfloat16, device=device)
+    fill(x, S.x_key(w, layer), x_row0 * w.H, w.x_sigma)
+    r = torch.empty(w.E, w.H, dtype=torch.bfloat16, device=device)
+    fill(r, S.router_key(w, layer), 0, w.router_sigma)
+    n = w.expert_elems()
+    eq = torch.empty(w.E, n // 2, dtype=torch.uint8, device=device)
+    esb = torch.empty(w.E, n // S.Q4_GROUP, dtype=torch.int32, device=device)
+    for e in range(w.E):
+        fill_q4(eq[e], esb[e], S.q4_expert_key(w, layer, e, False), S.q4_expert_key(w, layer, e, True), w.w_sigma)
+    sq = ssb = None
+    if w.I_shared:
+        ns = w.shared_elems()
+        sq = torch.empty(ns // 2, dtype=torch.uint8, device=device)
+        ssb = torch.empty(ns // S.Q4_GROUP, dtype=torch.int32, device=device)
+        fill_q4(sq, ssb, S.q4_shared_key(w, layer, False), S.q4_shared_key(w, layer, True), w.w_sigma)
+    return x, r, eq, esb, sq, ssb

@@ -24,6 +24,20 @@ workload's fp32 variant.
 Keys are derived per (seed, layer, tensor, expert) so that any expert's
 weights can be regenerated alone, which lets the oracle rebuild just the
 experts a token selected at full size.
+
+4-bit group-affine experts
+--------------------------
+The 4-bit variant stores each weight as an unsigned 4-bit code q and each
+group of 64 consecutive weights of a row (along the reduction dimension)
+with one bf16 scale s and bias b.  Codes are the bytes of a stream's
+outputs (output n gives bytes 8(n-1) .. 8n-1, little-endian), two codes per
+byte, low nibble first.  Group g takes output g+1 of a second stream: with
+u = (bits 9..31) / 2^23 and v = (bits 43..63) / 2^21,
+s = bf16(S0 * (0.5 + u)) and b = bf16(-(s * (7 + v))), where S0 is the fp32
+constant sigma / 4.61 (every fp32 step is exact or a single IEEE rounding,
+so host and device agree).  The affine weights s*q + b then have standard
+deviation close to sigma.  The pair is stored as one 32-bit word, s in the
+low half.
 """
 from __future__ import annotations
 
@@ -48,6 +62,13 @@ T_ROUTER = 1
 T_EXPERT = 2
 T_SHARED = 3
 T_PERM = 4
+T_Q4_CODES = 5
+T_Q4_SB = 6
+T_Q4_SHARED_CODES = 7
+T_Q4_SHARED_SB = 8
+
+Q4_GROUP = 64  # weights per scale/bias group
+Q4_STD = 4.61  # standard deviation of q - 7.5 for q uniform on 0..15 (sqrt(255/12))
 
 
 def mix64_int(z: int) -> int:
@@ -249,6 +270,55 @@ def zipf_router_bias(w: Workload, layer: int = 0) -> Optional[np.ndarray]:
     rank = np.empty(w.E, dtype=np.int64)
     rank[order] = np.arange(1, w.E + 1)
     return np.array([-w.zipf_s * math.log(r) for r in rank], dtype=np.float64).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# 4-bit group-affine experts
+# ----------------------------------------------------------------------------
+
+
+def q4_codes(key: int, nbytes: int) -> np.ndarray:
+    """Bytes 0 .. nbytes-1 of code stream ``key`` (two 4-bit codes per byte, low nibble first)."""
+    nout = (nbytes + 7) // 8
+    return splitmix64_outputs(key, 1, nout).view(np.uint8)[:nbytes].copy()
+
+
+def q4_s0(sigma: float) -> np.float32:
+    return np.float32(sigma / Q4_STD)
+
+
+def q4_scale_bias(key: int, ngroups: int, sigma: float) -> np.ndarray:
+    """uint32 [ngroups]: bf16 scale (low half) and bias (high half) of each group."""
+    raw = splitmix64_outputs(key, 1, ngroups)
+    u = ((raw >> np.uint64(9)) & np.uint64(0x7FFFFF)).astype(np.float32) * np.float32(2.0 ** -23)
+    v = (raw >> np.uint64(43)).astype(np.float32) * np.float32(2.0 ** -21)
+    s_bits = f32_to_bf16_bits(q4_s0(sigma) * (np.float32(0.5) + u))
+    s_val = bf16_bits_to_f32(s_bits)
+    b_bits = f32_to_bf16_bits(-(s_val * (np.float32(7.0) + v)))
+    return s_bits.astype(np.uint32) | (b_bits.astype(np.uint32) << np.uint32(16))
+
+
+def q4_expert_key(w: "Workload", layer: int, e: int, sb: bool) -> int:
+    return stream_key(w.seed, layer, T_Q4_SB if sb else T_Q4_CODES, e)
+
+
+def q4_shared_key(w: "Workload", layer: int, sb: bool) -> int:
+    return stream_key(w.seed, layer, T_Q4_SHARED_SB if sb else T_Q4_SHARED_CODES, 0)
+
+
+def q4_expert(w: "Workload", layer: int, e: int):
+    """One routed expert in 4-bit form: (codes uint8 [3*I*H/2], scale/bias uint32 [3*I*H/64]),
+    blocks gate [I][H], up [I][H], down [H][I] as in the bf16 packing."""
+    n = w.expert_elems()
+    return (q4_codes(q4_expert_key(w, layer, e, False), n // 2),
+            q4_scale_bias(q4_expert_key(w, layer, e, True), n // Q4_GROUP, w.w_sigma))
+
+
+def q4_shared(w: "Workload", layer: int = 0):
+    """The shared expert in 4-bit form (same packing)."""
+    n = w.shared_elems()
+    return (q4_codes(q4_shared_key(w, layer, False), n // 2),
+            q4_scale_bias(q4_shared_key(w, layer, True), n // Q4_GROUP, w.w_sigma))
 
 
 def tiny_f32(w: Workload = TINY):

@@ -353,6 +353,74 @@ def check_forced_routing(O):
     assert np.allclose(b["w"][:, [1, 0]], a["w"][:, [0, 1]], rtol=1e-14, atol=0)
 
 
+# ------------------------------------------------------------------ 4-bit weights
+
+def _bf16_bits(v):
+    """bf16 bit pattern of an exactly representable value."""
+    return int(np.array([v], dtype=np.float32).view(np.uint32)[0] >> 16)
+
+
+def check_q4_hand_example(O):
+    """Hand-decoded group: bytes 0x21, 0xF0 hold codes 1, 2, 0, 15 (low nibble first);
+    scale 0.5 and bias -1 give 1*0.5-1, 2*0.5-1, -1, 15*0.5-1; the rest (code 0) -1."""
+    codes = np.zeros(32, np.uint8)
+    codes[0], codes[1] = 0x21, 0xF0
+    word = _bf16_bits(0.5) | (_bf16_bits(-1.0) << 16)
+    w = O.dequant_q4(codes, np.array([word], np.uint32))
+    want = np.full(64, -1.0)
+    want[:4] = [-0.5, 0.0, -1.0, 6.5]
+    assert w.shape == (64,) and np.array_equal(w, want), w[:6]
+
+
+def check_q4_groups_and_affinity(O):
+    """Each 64-value group uses its own (scale, bias); within a group the
+    values are exactly affine in the code: w(q) - w(0) = q * s."""
+    rng = np.random.default_rng(7)
+    ngroups = 5
+    scales = [0.25, -0.125, 2.0, 0.0078125, 1.5]
+    biases = [1.0, -3.0, 0.5, -0.0625, 0.0]
+    words = np.array([_bf16_bits(a) | (_bf16_bits(b) << 16) for a, b in zip(scales, biases)], np.uint32)
+    q = rng.integers(0, 16, size=64 * ngroups).astype(np.uint8)
+    packed = (q[0::2] | (q[1::2] << 4)).astype(np.uint8)
+    w = O.dequant_q4(packed, words)
+    for g in range(ngroups):
+        seg = slice(64 * g, 64 * (g + 1))
+        assert np.array_equal(w[seg], q[seg] * scales[g] + biases[g]), g
+
+
+def check_q4_bf16_decoding(O):
+    """bf16 patterns decode to their values (sign, exponent, zero, subnormal)."""
+    pats = {0x3F80: 1.0, 0xC000: -2.0, 0x0000: 0.0, 0x8000: -0.0, 0x3E80: 0.25, 0x4120: 10.0,
+            0x0001: 2.0 ** -133, 0x7F7F: float(np.finfo(np.float32).max) // 2 ** 104 * 2 ** 104}
+    for bits, v in pats.items():
+        got = O.bf16_value(np.array([bits], np.uint32))[0]
+        if bits == 0x7F7F:
+            assert got == float(np.uint32(0x7F7F0000).view(np.float32)), got
+        else:
+            assert got == v and np.signbit(got) == np.signbit(v), (hex(bits), got)
+
+
+def check_q4_layer_is_dense_on_dequantised(O):
+    """The layer on 4-bit experts equals, for E = 1 and k = 1, two dense SwiGLU
+    FFNs (torch) on weights rebuilt by hand from the codes."""
+    rng = np.random.default_rng(8)
+    H, I, M = 64, 64, 5
+    n = 3 * I * H
+    q = rng.integers(0, 16, size=n).astype(np.uint8)
+    packed = (q[0::2] | (q[1::2] << 4)).astype(np.uint8)
+    s = rng.choice([2.0 ** -7, 2.0 ** -6, 3 * 2.0 ** -8], size=n // 64)
+    b = -8 * s
+    words = np.array([_bf16_bits(a) | (_bf16_bits(c) << 16) for a, c in zip(s, b)], np.uint32)
+    wts = (q.astype(np.float64) - 8.0) * np.repeat(s, 64)  # by hand: s * q + (-8 s)
+    x = rng.standard_normal((M, H))
+    router = np.zeros((1, H))
+    got = O.moe_forward(x, router, lambda e: O.unpack_expert(O.dequant_q4(packed, words), I, H),
+                        O.dequant_q4(packed, words), 1, I)["out"]
+    Wg, Wu, Wd = wts[:I * H].reshape(I, H), wts[I * H:2 * I * H].reshape(I, H), wts[2 * I * H:].reshape(H, I)
+    want = 2 * _torch_ffn(x, Wg, Wu, Wd)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_topk_bruteforce, check_zero_router, check_planted_router, check_router_bias,
     check_k_equals_E_is_softmax, check_k1_weight_one, check_weights_closed_form,
@@ -360,4 +428,6 @@ ALL_CHECKS = [
     check_ffn_matches_torch, check_single_expert_layer, check_identical_experts,
     check_planted_combine, check_dense_equals_grouped, check_token_permutation,
     check_chunk_invariance, check_down_linearity, check_subset_tokens, check_forced_routing,
+    check_q4_hand_example, check_q4_groups_and_affinity, check_q4_bf16_decoding,
+    check_q4_layer_is_dense_on_dequantised,
 ]

@@ -41,6 +41,18 @@ MUTANTS = [
      "sel = np.take_along_axis(p, np.sort(np.asarray(ids, dtype=np.int64), axis=1), axis=1)"),
     ("near_tie_wrong_direction", "((s[:, :-1] - s[:, 1:]) <= eps)", "((s[:, :-1] - s[:, 1:]) >= eps)"),
     ("token_row_gather_wrong", "tok = perm[pos] // k", "tok = perm[pos] % k"),
+    ("q4_high_nibble_first", "q[0::2] = b & np.uint8(0x0F)\n    q[1::2] = b >> np.uint8(4)",
+     "q[1::2] = b & np.uint8(0x0F)\n    q[0::2] = b >> np.uint8(4)"),
+    ("q4_scale_bias_halves_swapped", "s = bf16_value(words)\n    b = bf16_value(words >> np.uint64(16))",
+     "b = bf16_value(words)\n    s = bf16_value(words >> np.uint64(16))"),
+    ("q4_group_of_32", "np.repeat(s, Q4_GROUP) + np.repeat(b, Q4_GROUP)",
+     "np.repeat(np.repeat(s, 2)[:s.size], Q4_GROUP) + np.repeat(np.repeat(b, 2)[:b.size], Q4_GROUP)"),
+    ("q4_bias_subtracted", "np.repeat(s, Q4_GROUP) + np.repeat(b, Q4_GROUP)",
+     "np.repeat(s, Q4_GROUP) - np.repeat(b, Q4_GROUP)"),
+    ("q4_signed_codes", "q = q4_codes(packed).astype(np.float64)",
+     "q = q4_codes(packed).astype(np.int8).astype(np.float64) - 8.0 * (q4_codes(packed) > 7)"),
+    ("q4_bf16_low_bits", "hi = (np.asarray(bits, dtype=np.uint64) & np.uint64(0xFFFF)).astype(np.uint32) << np.uint32(16)",
+     "hi = (np.asarray(bits, dtype=np.uint64) & np.uint64(0xFFFF)).astype(np.uint32) << np.uint32(15)"),
     ("drop_last_group_row", "pos = np.arange(offsets[e], offsets[e + 1])", "pos = np.arange(offsets[e], max(offsets[e], offsets[e + 1] - 1))"),
 ]
 

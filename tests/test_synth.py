@@ -62,3 +62,28 @@ def test_workload_shapes():
     assert S.PREFILL.M * S.PREFILL.k == 32768
     assert S.LONG.tokens == 131072
     assert S.DECODE.layers * S.DECODE.E * S.DECODE.expert_elems() * 2 > 64e9
+
+
+def test_q4_generator():
+    """4-bit experts: code bytes are the stream's outputs, scale/bias words
+    follow their recipe exactly, and the rebuilt weights have mean ~0 and
+    standard deviation ~sigma."""
+    key = S.stream_key(3, 0, S.T_Q4_CODES, 1)
+    b = S.q4_codes(key, 40)
+    assert np.array_equal(b[:16], S.splitmix64_outputs(key, 1, 2).view(np.uint8))
+    assert np.array_equal(S.q4_codes(key, 64)[:40], b)
+    sb = S.q4_scale_bias(S.stream_key(3, 0, S.T_Q4_SB, 1), 4096, 0.02)
+    s = S.bf16_bits_to_f32((sb & 0xFFFF).astype(np.uint16)).astype(np.float64)
+    off = S.bf16_bits_to_f32((sb >> 16).astype(np.uint16)).astype(np.float64)
+    s0 = 0.02 / S.Q4_STD
+    assert np.all(s >= 0.49 * s0) and np.all(s <= 1.51 * s0)
+    assert np.all(-off / s >= 6.9) and np.all(-off / s <= 8.1)
+    codes, words = S.q4_expert(S.TINY, 0, 3)
+    q = np.empty(2 * codes.size)
+    q[0::2], q[1::2] = codes & 15, codes >> 4
+    sv = S.bf16_bits_to_f32((words & 0xFFFF).astype(np.uint16)).astype(np.float64)
+    bv = S.bf16_bits_to_f32((words >> 16).astype(np.uint16)).astype(np.float64)
+    wts = q * np.repeat(sv, S.Q4_GROUP) + np.repeat(bv, S.Q4_GROUP)
+    assert codes.size * 2 == S.TINY.expert_elems() and words.size * 64 == S.TINY.expert_elems()
+    assert abs(wts.mean()) < 0.1 * S.TINY.w_sigma
+    assert abs(wts.std() / S.TINY.w_sigma - 1) < 0.1
