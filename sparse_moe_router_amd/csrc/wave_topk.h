@@ -43,17 +43,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-// One wave selects the top k of E scores of one token; lane l holds the
-// scores of experts l, l+64, ... in f.  Returns, in lane j < k, the rank-j
-// key; every lane gets the rank-0 key in *top.  s_keys: 64 wave-private LDS
-// entries.
-//
-// Radix select with ballots: 32 rounds of compare + ballot + popcount find
-// T, the k-th largest order-mapped score (count(v >= T) >= k, maximal).  The
-// selection is every score above T plus the lowest-index experts scoring
-// exactly T, as many as needed for k.  The k winners are compacted into LDS
-// by ballot prefix counts, and each of lanes 0..k-1 ranks one winner against
-// the others (keys are unique: score, then index) and stores it at its rank.
 // Loads lane's scores of one token (experts lane, lane+64, ...); padding
 // (e >= E) is -inf, which sorts below every real score.
 template <int EPL>
@@ -65,9 +54,20 @@ __device__ __forceinline__ void load_scores(const float* __restrict__ Lrow, int 
   }
 }
 
+// wave_topk_radix: one wave selects the top k of E scores of one token; lane
+// l holds the scores of experts l, l+64, ... in f.  Returns, in lane j < k,
+// the rank-j key; every lane gets the rank-0 key in *top.  s_keys: 64
+// wave-private LDS entries.
+//
+// Radix select with ballots: 32 rounds of compare + ballot + popcount find
+// T, the k-th largest order-mapped score (count(v >= T) >= k, maximal).  The
+// selection is every score above T plus the lowest-index experts scoring
+// exactly T, as many as needed for k.  The k winners are compacted into LDS
+// by ballot prefix counts, and each of lanes 0..k-1 ranks one winner against
+// the others (keys are unique: score, then index) and stores it at its rank.
 template <int EPL>
-__device__ __forceinline__ uint64_t wave_topk(const float (&f)[EPL], int E, int k, int lane, uint64_t* top,
-                                              uint64_t* s_keys) {
+__device__ __forceinline__ uint64_t wave_topk_radix(const float (&f)[EPL], int E, int k, int lane, uint64_t* top,
+                                                    uint64_t* s_keys) {
   uint32_t v[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) v[q] = lane + 64 * q < E ? orderable(f[q]) : 0u;
@@ -116,6 +116,68 @@ __device__ __forceinline__ uint64_t wave_topk(const float (&f)[EPL], int E, int 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const uint64_t mine = lane < k ? s_keys[32 + lane] : 0ull;
   *top = s_keys[32];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return mine;
+}
+
+// The same selection (same results) with far fewer ballots, which dominate
+// the cost: a radix select over the 64 lane maxima alone (one ballot per
+// bit) finds T1, the k-th largest lane maximum.  k distinct lanes hold a
+// value >= T1, so the k-th largest value is >= T1 and every winner is among
+// the candidates {values >= T1}, normally a dozen or so.  The candidates are
+// compacted into LDS and each ranks itself among them by (score, lower
+// index); ranks < k are the selection.  When more than 64 values tie at or
+// above T1, the full radix select above takes over.
+template <int EPL>
+__device__ __forceinline__ uint64_t wave_topk(const float (&f)[EPL], int E, int k, int lane, uint64_t* top,
+                                              uint64_t* s_keys) {
+  uint32_t v[EPL];
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) v[q] = lane + 64 * q < E ? orderable(f[q]) : 0u;
+  uint32_t m = v[0];
+#pragma unroll
+  for (int q = 1; q < EPL; ++q) m = v[q] > m ? v[q] : m;
+  uint32_t T = 0;
+#pragma unroll 8
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    if (__popcll(__ballot(m >= cand)) >= k) T = cand;
+  }
+  int C = 0;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) C += __popcll(__ballot(v[q] >= T));
+  if (C > 64) return wave_topk_radix<EPL>(f, E, k, lane, top, s_keys);
+  const uint64_t below = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) {
+    const bool c = v[q] >= T;
+    const uint64_t b = __ballot(c);
+    if (c)
+      s_keys[base + __popcll(b & below)] =
+          ((uint64_t)v[q] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * q));
+    base += __popcll(b);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint64_t key = 0;
+  int rank = 0;
+  if (lane < C) {
+    key = s_keys[lane];
+    for (int i = 0; i < C; ++i) rank += s_keys[i] > key;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < C && rank < k) s_keys[rank] = key;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t mine = lane < k ? s_keys[lane] : 0ull;
+  *top = s_keys[0];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
