@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-q4", action="store_true", help="skip the 4-bit expert-weight runs")
     ap.add_argument("--layers", type=int, default=40, help=argparse.SUPPRESS)
     ap.add_argument("--trace-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -102,25 +103,36 @@ class Hip:
 
 
 class LayerCall:
-    """Pre-marshalled moe_layer_forward arguments for one layer."""
+    """Pre-marshalled moe_layer_forward (bf16 experts) or moe_layer_forward_q4 arguments for one
+    layer.  ex / sh: bf16 tensors, or (codes, scale_bias) pairs for 4-bit experts."""
 
     def __init__(self, moe, x, r, ex, sh, k, out, ws, bias=None, routing=None):
         import torch
         M, H = x.shape
         E = r.shape[0]
-        I = ex.numel() // (3 * E * H)
-        Is = 0 if sh is None else sh.numel() // (3 * H)
+        self.q4 = isinstance(ex, tuple)
+        if self.q4:
+            I = ex[0].numel() * 2 // (3 * E * H)
+            Is = 0 if sh is None else sh[0].numel() * 2 // (3 * H)
+            self.ex_q4 = moe.MoeQ4(ex[0].data_ptr(), ex[1].data_ptr())
+            self.sh_q4 = None if sh is None else moe.MoeQ4(sh[0].data_ptr(), sh[1].data_ptr())
+            wargs = [ctypes.byref(self.ex_q4), None if sh is None else ctypes.byref(self.sh_q4)]
+        else:
+            I = ex.numel() // (3 * E * H)
+            Is = 0 if sh is None else sh.numel() // (3 * H)
+            wargs = [ex.data_ptr(), None if sh is None else sh.data_ptr()]
         self.lib = moe.lib()
         self.desc = moe.make_desc(M, H, E, I, Is, 0, bias)
         self.routing = moe._routing_struct(routing)
-        self.args = [ctypes.byref(self.desc), x.data_ptr(), r.data_ptr(), ex.data_ptr(),
-                     None if sh is None else sh.data_ptr(), k, out.data_ptr(), ws.data_ptr(), ws.numel(), None,
-                     None if self.routing is None else ctypes.byref(self.routing)]
+        self.args = [ctypes.byref(self.desc), x.data_ptr(), r.data_ptr(), *wargs, k, out.data_ptr(), ws.data_ptr(),
+                     ws.numel(), None, None if self.routing is None else ctypes.byref(self.routing)]
         self.torch = torch
 
     def __call__(self, trace=None):
         self.args[9] = self.torch.cuda.current_stream().cuda_stream
-        if trace is None:
+        if self.q4:
+            st = self.lib.moe_layer_forward_q4(*self.args, None if trace is None else ctypes.byref(trace))
+        elif trace is None:
             st = self.lib.moe_layer_forward(*self.args)
         else:
             st = self.lib.moe_layer_forward_traced(*self.args, ctypes.byref(trace))
@@ -158,7 +170,22 @@ def blas_threads():
 
 # ------------------------------------------------------------------ decode
 
-def bench_decode(args, hip, moe, SD, S):
+def q4_layer(SD, S, w, l, dev="cuda"):
+    """One layer's 4-bit experts on the device: ((codes, scale_bias), (shared codes, shared scale_bias))."""
+    import torch
+    n = w.expert_elems()
+    codes = torch.empty(w.E, n // 2, dtype=torch.uint8, device=dev)
+    sb = torch.empty(w.E, n // S.Q4_GROUP, dtype=torch.int32, device=dev)
+    for e in range(w.E):
+        SD.fill_q4(codes[e], sb[e], S.q4_expert_key(w, l, e, False), S.q4_expert_key(w, l, e, True), w.w_sigma)
+    ns = w.shared_elems()
+    sc = torch.empty(ns // 2, dtype=torch.uint8, device=dev)
+    ssb = torch.empty(ns // S.Q4_GROUP, dtype=torch.int32, device=dev)
+    SD.fill_q4(sc, ssb, S.q4_shared_key(w, l, False), S.q4_shared_key(w, l, True), w.w_sigma)
+    return (codes, sb), (sc, ssb)
+
+
+def bench_decode(args, hip, moe, SD, S, q4=False):
     import torch
     w = S.DECODE
     L = args.layers
@@ -171,11 +198,14 @@ def bench_decode(args, hip, moe, SD, S):
     for l in range(L):
         r = torch.empty(E, H, dtype=torch.bfloat16, device=dev)
         SD.fill(r, S.router_key(w, l), 0, w.router_sigma)
-        ex = torch.empty(E, w.expert_elems(), dtype=torch.bfloat16, device=dev)
-        for e in range(E):
-            SD.fill(ex[e], S.expert_key(w, l, e), 0, w.w_sigma)
-        sh = torch.empty(w.shared_elems(), dtype=torch.bfloat16, device=dev)
-        SD.fill(sh, S.shared_key(w, l), 0, w.w_sigma)
+        if q4:
+            ex, sh = q4_layer(SD, S, w, l, dev)
+        else:
+            ex = torch.empty(E, w.expert_elems(), dtype=torch.bfloat16, device=dev)
+            for e in range(E):
+                SD.fill(ex[e], S.expert_key(w, l, e), 0, w.w_sigma)
+            sh = torch.empty(w.shared_elems(), dtype=torch.bfloat16, device=dev)
+            SD.fill(sh, S.shared_key(w, l), 0, w.w_sigma)
         layers.append((r, ex, sh))
     out = torch.empty(L, H, dtype=torch.bfloat16, device=dev)
     wsn = moe.workspace_size(1, H, E, I, w.I_shared, k)
@@ -223,9 +253,11 @@ def bench_decode(args, hip, moe, SD, S):
             c(tr)
     kt = kernel_times(hip, moe, step, L, args.trace_steps, 3)
 
-    # algorithmic bytes
-    layer_bytes = (k + 1) * w.expert_elems() * 2 + E * H * 2 + 2 * H * 2
-    gateup_bytes = k * 2 * I * H * 2 + H * 2 + E * 4 + k * I * 4
+    # algorithmic bytes (weights: 2 bytes per element in bf16; 4-bit: half a byte per code plus a
+    # 4-byte scale/bias word per 64 elements = 0.5625 bytes per element)
+    wb = 0.5625 if q4 else 2
+    layer_bytes = int((k + 1) * w.expert_elems() * wb) + E * H * 2 + 2 * H * 2
+    gateup_bytes = int(k * 2 * I * H * wb) + H * 2 + E * 4 + k * I * 4
     dom = "dec_gateup"
     avg_ms = sum(kt[dom]) / len(kt[dom])
     achieved = gateup_bytes / (avg_ms * 1e-3) / 1e9
@@ -235,8 +267,8 @@ def bench_decode(args, hip, moe, SD, S):
         layer_hbm_frac=layer_bytes * L / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         kernels_us={n: round(1000.0 * sum(v) / len(v), 3) for n, v in kt.items()},
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for("k_dec_gateup"),
-                      kernel="k_dec_gateup",
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None if q4 else traffic_for("k_dec_gateup"),
+                      kernel="k_dec_gateup" + ("<q4>" if q4 else ""),
                       bytes_per_launch=gateup_bytes, avg_us=round(avg_ms * 1000, 3)),
     )
     return res, (layers, xpool)
@@ -272,9 +304,13 @@ def cpu_decode(S, O, layers_sample=2, rows=128):
 
 # ------------------------------------------------------------------ prefill
 
-def bench_prefill(args, hip, moe, SD, S, w):
+def bench_prefill(args, hip, moe, SD, S, w, q4=False):
     import torch
-    x, r, ex, sh = SD.layer_tensors(w)
+    if q4:
+        x, r, ec, esb, sc, ssb = SD.layer_tensors_q4(w)
+        ex, sh = (ec, esb), (sc, ssb)
+    else:
+        x, r, ex, sh = SD.layer_tensors(w)
     bias = None
     if w.zipf_s:
         bias = torch.from_numpy(S.zipf_router_bias(w)).cuda()
@@ -297,24 +333,37 @@ def bench_prefill(args, hip, moe, SD, S, w):
     c = counts.cpu()
     nonempty = int((c > 0).sum())
     M, H, E, I, k = w.M, w.H, w.E, w.I, w.k
-    layer_bytes = (nonempty + 1) * w.expert_elems() * 2 + E * H * 2 + 2 * M * H * 2
+    wb = 0.5625 if q4 else 2  # weight bytes per element
+    layer_bytes = int((nonempty + 1) * w.expert_elems() * wb) + E * H * 2 + 2 * M * H * 2
     flops = M * (2 * H * E + (k + 1) * 3 * 2 * H * I)
-    gu_bytes = (nonempty + 1) * 2 * I * H * 2 + M * H * 2 + (M * k + M) * I * 2
+    gu_bytes = int((nonempty + 1) * 2 * I * H * wb) + M * H * 2 + (M * k + M) * I * 2
     gu_flops = (M * k + M) * 2 * I * H * 2
     avg = sum(kt["gemm_gateup"]) / len(kt["gemm_gateup"])
     ach = gu_bytes / (avg * 1e-3) / 1e9
+    ach_tf = gu_flops / (avg * 1e-3) / 1e12
+    # the bound is the resource the kernel's algorithmic work needs longer on at peak
+    mfma_bound = gu_flops / BF16_PEAK_TFLOPS / 1e12 > gu_bytes / HBM_PEAK_GBS / 1e9
+    kname = "k_grouped_gemm<0, q4> (gate/up + SwiGLU)" if q4 else "k_grouped_gemm<0> (gate/up + SwiGLU)"
+    if mfma_bound:
+        roof = dict(bound="mfma", achieved=round(ach_tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach_tf / BF16_PEAK_TFLOPS, 4), traffic=None, kernel=kname,
+                    flops_per_launch=gu_flops, bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
+                    hbm_frac=round(ach / HBM_PEAK_GBS, 4))
+    else:
+        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4),
+                    traffic=None if q4 else traffic_for(f"k_grouped_gemm<0>@{w.name}"), kernel=kname,
+                    bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
+                    mfma_frac=round(ach_tf / BF16_PEAK_TFLOPS, 4))
     res = dict(
         value=M / (ms * 1e-3), unit="tok/s", ms_per_step=ms, steps=steps,
-        config=dict(workload=f"{w.name}: {w.describe()}, bf16", nonempty_experts=nonempty,
+        config=dict(workload=f"{w.name}: {w.describe()}, {'4-bit group-affine' if q4 else 'bf16'} experts",
+                    nonempty_experts=nonempty,
                     max_group=int(c.max()), empty_groups=int((c == 0).sum())),
         hbm_frac=layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         kernels_us={n: round(1000.0 * sum(v) / len(v), 2) for n, v in kt.items()},
-        roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic_for(f"k_grouped_gemm<0>@{w.name}"),
-                      kernel="k_grouped_gemm<0> (gate/up + SwiGLU)",
-                      bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
-                      mfma_frac=round(gu_flops / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)),
+        roofline=roof,
     )
     del x, r, ex, sh, ws
     return res
@@ -369,6 +418,17 @@ def main():
     torch.cuda.empty_cache()
     pre = bench_prefill(args, hip, moe, SD, S, S.PREFILL)
     skew = bench_prefill(args, hip, moe, SD, S, S.SKEW)
+    dec_q4 = pre_q4 = None
+    if not args.no_q4:
+        dq, keep = bench_decode(args, hip, moe, SD, S, q4=True)
+        del keep
+        torch.cuda.empty_cache()
+        dec_q4 = {"value": round(dq["value"], 2), "unit": "tok/s", "ms_per_step": round(dq["ms_per_step"], 4),
+                  "us_per_layer": round(dq["layer_us"], 3), "hbm_frac": round(dq["layer_hbm_frac"], 4),
+                  "kernels_us": dq["kernels_us"], "roofline": dq["roofline"],
+                  "config": {"workload": f"decode batch-1, {args.layers} layers, 4-bit group-affine experts "
+                                         f"(g=64, bf16 scale+bias), bf16 router/x/out"}}
+        pre_q4 = bench_prefill(args, hip, moe, SD, S, S.PREFILL, q4=True)
     cpu_d = cpu_p = None
     if not args.no_cpu:
         import oracle.moe_oracle as O
@@ -391,6 +451,8 @@ def main():
                          "kernels_us": dec["kernels_us"]},
         "prefill": pre,
         "prefill_skew": skew,
+        "decode_q4": dec_q4,
+        "prefill_q4": pre_q4,
     }
     print(json.dumps(line), flush=True)
 

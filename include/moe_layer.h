@@ -162,6 +162,36 @@ moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const 
                                       void* stream, const moe_routing_t* routing,
                                       moe_trace_t* trace);
 
+/* 4-bit group-affine expert weights ("Optimizing on-device inference for
+ * Apple Silicon", section "Dequantize weights during matrix multiplication":
+ * 4-bit weights whose groups of 64 share a bf16 scale and bias).
+ * Every weight of the bf16 packing (expert e = gate [I][H], up [I][H],
+ * down [H][I], rows along the reduction dimension) is w = s*q + b, with q
+ * an unsigned 4-bit code and (s, b) the bf16 scale and bias of its group of
+ * 64 consecutive elements of the block (row lengths are multiples of 64, so
+ * a group never spans two rows).
+ *   codes       uint8 [E][3*I*H/2]: element 2i in the low nibble of byte i,
+ *               element 2i+1 in the high nibble
+ *   scale_bias  uint32 [E][3*I*H/64]: group g's scale in bits 0..15, its
+ *               bias in bits 16..31 (bf16 bit patterns)
+ * The shared expert uses the same layout with E = 1 and I_shared.  Both
+ * pointers are device pointers, 16-byte aligned. */
+typedef struct {
+  const void* codes;
+  const void* scale_bias;
+} moe_q4_t;
+
+/* moe_layer_forward (with the optional trace of moe_layer_forward_traced)
+ * on 4-bit expert weights: experts (non-NULL) and shared (NULL when
+ * I_shared == 0) in the layout above.  x, the router and the output stay
+ * bf16; the workspace is sized by moe_workspace_size.  Products accumulate
+ * in fp32: the matrix-matrix path rounds each dequantised weight to bf16
+ * for the MFMA operands, the decode path multiplies in fp32. */
+moe_status_t moe_layer_forward_q4(const moe_desc_t* d, const void* x, const void* router_w,
+                                  const moe_q4_t* experts, const moe_q4_t* shared, int top_k, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const moe_routing_t* routing, moe_trace_t* trace);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t s);
 

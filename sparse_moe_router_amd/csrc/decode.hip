@@ -21,6 +21,7 @@
 //      weighted slot partials summed in slot order through LDS.
 #include "moe_internal.h"
 #include "wave_topk.h"
+#include "weights.h"
 
 namespace moe {
 namespace {
@@ -30,30 +31,28 @@ namespace {
 // a wave costs one memory round trip, not one per loop iteration.
 constexpr int DB = 4;  // 16-byte chunks per lane per batch: 4 x 64 lanes x 8 = 2048 elements
 
-// dot(x[0:n], w[0:n]) and dot(x, w2) for one wave (n % 8 == 0), fp32 in all lanes.
-template <bool TWO>
-__device__ __forceinline__ void wave_dots(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                          const uint16_t* __restrict__ w2, int n, int lane, float* d1,
-                                          float* d2) {
+// dot(x[0:n], w[0:n]) and dot(x, w2) for one wave (n % 8 == 0), fp32 in all
+// lanes; w, w2 point at the rows' first element.
+template <bool TWO, class W>
+__device__ __forceinline__ void wave_dots(const uint16_t* __restrict__ x, const W w, const W w2, int n, int lane,
+                                          float* d1, float* d2) {
   float a1 = 0.0f, a2 = 0.0f;
   for (int base = 0; base < n; base += DB * 512) {
-    u32x4_t xa[DB], wa[DB], wb[DB];
+    u32x4_t xa[DB];
+    typename W::chunk_t wa[DB], wb[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) {
       const int c = base + 512 * i + lane * 8;
       const int cc = c < n ? c : 0;
       xa[i] = *(const u32x4_t*)(x + cc);
-      wa[i] = *(const u32x4_t*)(w + cc);
-      if (TWO) wb[i] = *(const u32x4_t*)(w2 + cc);
+      wa[i] = w.load(cc);
+      if (TWO) wb[i] = w2.load(cc);
     }
 #pragma unroll
     for (int i = 0; i < DB; ++i) {
       if (base + 512 * i + lane * 8 >= n) continue;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a1 += bf16_lo(xa[i][q]) * bf16_lo(wa[i][q]) + bf16_hi(xa[i][q]) * bf16_hi(wa[i][q]);
-        if (TWO) a2 += bf16_lo(xa[i][q]) * bf16_lo(wb[i][q]) + bf16_hi(xa[i][q]) * bf16_hi(wb[i][q]);
-      }
+      a1 += W::dot(wa[i], xa[i]);
+      if (TWO) a2 += W::dot(wb[i], xa[i]);
     }
   }
   *d1 = wave_sum(a1);
@@ -69,7 +68,8 @@ __global__ __launch_bounds__(256) void k_dec_router(const uint16_t* __restrict__
   const int e = blockIdx.x * 4 + wave;
   if (e >= E) return;
   float v, unused;
-  wave_dots<false>(x, wr + (int64_t)e * H, nullptr, H, lane, &v, &unused);
+  const WBf16 row{wr + (int64_t)e * H};
+  wave_dots<false>(x, row, row, H, lane, &v, &unused);
   if (lane == 0) logits[e] = v + (bias ? bias[e] : 0.0f);
 }
 
@@ -80,11 +80,9 @@ __global__ __launch_bounds__(256) void k_dec_router(const uint16_t* __restrict__
 // then wave w computes row i = 4*(b % row_blocks) + w of slot j's expert.
 // The first routed workgroup also publishes ids / weights.  With I == 0 only
 // the selection runs.
-template <int EPL>
-__global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__ x,
-                                                    const uint16_t* __restrict__ expert_w,
-                                                    const uint16_t* __restrict__ shared_w,
-                                                    const float* __restrict__ logits,
+template <int EPL, class W>
+__global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__ x, const W expert_w,
+                                                    const W shared_w, const float* __restrict__ logits,
                                                     int32_t* __restrict__ ids,
                                                     float* __restrict__ wts,
                                                     float* __restrict__ h_r, float* __restrict__ h_s,
@@ -96,7 +94,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
     const int i = blockIdx.x * 4 + wave;
     if (i >= Is) return;
     float g, u;
-    wave_dots<true>(x, shared_w + (int64_t)i * H, shared_w + ((int64_t)Is + i) * H, H, lane, &g, &u);
+    wave_dots<true>(x, shared_w.at((int64_t)i * H), shared_w.at(((int64_t)Is + i) * H), H, lane, &g, &u);
     if (lane == 0) h_s[i] = silu(g) * u;
     return;
   }
@@ -125,9 +123,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
   const int j = b / rblocks;
   const int i = (b % rblocks) * 4 + wave;
   if (j >= k || i >= I) return;
-  const uint16_t* W = expert_w + (int64_t)s_ids[j] * 3 * I * H;
+  const W ew = expert_w.at((int64_t)s_ids[j] * 3 * I * H);
   float g, u;
-  wave_dots<true>(x, W + (int64_t)i * H, W + ((int64_t)I + i) * H, H, lane, &g, &u);
+  wave_dots<true>(x, ew.at((int64_t)i * H), ew.at(((int64_t)I + i) * H), H, lane, &g, &u);
   if (lane == 0) h_r[(int64_t)j * I + i] = silu(g) * u;
 }
 
@@ -136,8 +134,8 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
 // rows each; every wave loads its DR weight rows and its h slice at once,
 // reduces, and the slot partials are summed in slot order through LDS.
 constexpr int DR = 4;
-__global__ __launch_bounds__(1024) void k_dec_down(const uint16_t* __restrict__ expert_w,
-                                                   const uint16_t* __restrict__ shared_w,
+template <class W>
+__global__ __launch_bounds__(1024) void k_dec_down(const W expert_w, const W shared_w,
                                                    const int32_t* __restrict__ ids,
                                                    const float* __restrict__ wts,
                                                    const float* __restrict__ h_r,
@@ -152,14 +150,14 @@ __global__ __launch_bounds__(1024) void k_dec_down(const uint16_t* __restrict__ 
   for (int j = wave; j < nslot; j += blockDim.x >> 6) {
     const bool sh = j == k;  // the shared expert
     const int n = sh ? Is : I;
-    const uint16_t* wd;
+    W wd;
     const float* hj;
     float wj = 1.0f;
     if (sh) {
-      wd = shared_w + (int64_t)2 * Is * H;
+      wd = shared_w.at((int64_t)2 * Is * H);
       hj = h_s;
     } else {
-      wd = expert_w + (int64_t)ids[j] * 3 * I * H + (int64_t)2 * I * H;
+      wd = expert_w.at((int64_t)ids[j] * 3 * I * H + (int64_t)2 * I * H);
       hj = h_r + (int64_t)j * I;
       wj = wts[j];
     }
@@ -170,20 +168,17 @@ __global__ __launch_bounds__(1024) void k_dec_down(const uint16_t* __restrict__ 
       const int q0 = base + lane * 8;
       const bool ok = q0 < n;
       const int qq = ok ? q0 : 0;
-      u32x4_t b[DR];
+      typename W::chunk_t b[DR];
 #pragma unroll
       for (int r = 0; r < DR; ++r) {
         const int c = c0 + r < H ? c0 + r : H - 1;
-        b[r] = *(const u32x4_t*)(wd + (int64_t)c * n + qq);
+        b[r] = wd.load((int64_t)c * n + qq);
       }
       const f32x4_t h0 = *(const f32x4_t*)(hj + qq);
       const f32x4_t h1 = *(const f32x4_t*)(hj + qq + 4);
       if (ok) {
 #pragma unroll
-        for (int r = 0; r < DR; ++r)
-          part[r] += bf16_lo(b[r][0]) * h0[0] + bf16_hi(b[r][0]) * h0[1] + bf16_lo(b[r][1]) * h0[2] +
-                     bf16_hi(b[r][1]) * h0[3] + bf16_lo(b[r][2]) * h1[0] + bf16_hi(b[r][2]) * h1[1] +
-                     bf16_lo(b[r][3]) * h1[2] + bf16_hi(b[r][3]) * h1[3];
+        for (int r = 0; r < DR; ++r) part[r] += W::dot(b[r], h0, h1);
       }
     }
 #pragma unroll
@@ -207,34 +202,57 @@ hipError_t launch_decode_router(const uint16_t* x, const uint16_t* wr, const flo
   return launch(lc, k_dec_router, dim3((p.E + 3) / 4), dim3(256), x, wr, bias, logits, p.H, p.E);
 }
 
-hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
-                                const float* logits, int32_t* ids, float* w, float* h_dec, const Plan& p,
-                                const Launch& lc) {
+namespace {
+
+template <class W>
+hipError_t decode_gateup(const uint16_t* x, const W ew, const W sw, const float* logits, int32_t* ids, float* w,
+                         float* h_dec, const Plan& p, const Launch& lc) {
   // p.I == 0 requests the selection only (routing without expert work)
   const int nshared = p.shared && p.I > 0 ? (p.Is + 3) / 4 : 0;
   const int blocks = nshared + (p.I > 0 ? p.k * ((p.I + 3) / 4) : 1);
   float* h_s = h_dec + (int64_t)p.k * p.I;
   const dim3 g(blocks), b(256);
-  if (p.E <= 64)
-    return launch(lc, k_dec_gateup<1>, g, b, x, expert_w, shared_w, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
-  if (p.E <= 128)
-    return launch(lc, k_dec_gateup<2>, g, b, x, expert_w, shared_w, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
-  if (p.E <= 256)
-    return launch(lc, k_dec_gateup<4>, g, b, x, expert_w, shared_w, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
-  if (p.E <= 512)
-    return launch(lc, k_dec_gateup<8>, g, b, x, expert_w, shared_w, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
-  return launch(lc, k_dec_gateup<16>, g, b, x, expert_w, shared_w, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+  if (p.E <= 64) return launch(lc, k_dec_gateup<1, W>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+  if (p.E <= 128) return launch(lc, k_dec_gateup<2, W>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+  if (p.E <= 256) return launch(lc, k_dec_gateup<4, W>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+  if (p.E <= 512) return launch(lc, k_dec_gateup<8, W>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+  return launch(lc, k_dec_gateup<16, W>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+}
+
+template <class W>
+hipError_t decode_down(const W ew, const W sw, const int32_t* ids, const float* w, const float* h_dec,
+                       uint16_t* out, const Plan& p, const Launch& lc) {
+  const float* h_r = h_dec;
+  const float* h_s = h_dec + (int64_t)p.k * p.I;
+  const int nslot = p.k + (p.shared ? 1 : 0);
+  const int waves = nslot < 16 ? nslot : 16;
+  return launch(lc, k_dec_down<W>, dim3((p.H + DR - 1) / DR), dim3(64 * waves), ew, sw, ids, w, h_r, h_s, out,
+                p.H, p.I, p.Is, p.k, nslot);
+}
+
+}  // namespace
+
+hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
+                                const float* logits, int32_t* ids, float* w, float* h_dec, const Plan& p,
+                                const Launch& lc) {
+  return decode_gateup(x, WBf16{expert_w}, WBf16{p.shared ? shared_w : nullptr}, logits, ids, w, h_dec, p, lc);
 }
 
 hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w, const int32_t* ids,
                               const float* w, const float* h_dec, uint16_t* out, const Plan& p,
                               const Launch& lc) {
-  const float* h_r = h_dec;
-  const float* h_s = h_dec + (int64_t)p.k * p.I;
-  const int nslot = p.k + (p.shared ? 1 : 0);
-  const int waves = nslot < 16 ? nslot : 16;
-  return launch(lc, k_dec_down, dim3((p.H + DR - 1) / DR), dim3(64 * waves), expert_w,
-                p.shared ? shared_w : nullptr, ids, w, h_r, h_s, out, p.H, p.I, p.Is, p.k, nslot);
+  return decode_down(WBf16{expert_w}, WBf16{p.shared ? shared_w : nullptr}, ids, w, h_dec, out, p, lc);
+}
+
+hipError_t launch_decode_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh,
+                                   const float* logits, int32_t* ids, float* w, float* h_dec, const Plan& p,
+                                   const Launch& lc) {
+  return decode_gateup(x, WQ4{ex.codes, ex.groups}, WQ4{sh.codes, sh.groups}, logits, ids, w, h_dec, p, lc);
+}
+
+hipError_t launch_decode_down_q4(const Q4Weights& ex, const Q4Weights& sh, const int32_t* ids, const float* w,
+                                 const float* h_dec, uint16_t* out, const Plan& p, const Launch& lc) {
+  return decode_down(WQ4{ex.codes, ex.groups}, WQ4{sh.codes, sh.groups}, ids, w, h_dec, out, p, lc);
 }
 
 }  // namespace moe

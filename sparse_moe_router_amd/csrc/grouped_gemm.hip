@@ -48,6 +48,10 @@ struct GemmArgs {
   const int32_t* perm;
   const Tile* tiles;
   const int32_t* ntiles;
+  const uint32_t* ex_codes;   // 4-bit weights (Q4 kernels): codes, 8 per word
+  const uint32_t* ex_groups;  // (scale, bias) per 64 elements
+  const uint32_t* sh_codes;
+  const uint32_t* sh_groups;
   uint16_t* out_r;
   uint16_t* out_s;
   int64_t M;
@@ -59,11 +63,24 @@ struct GemmArgs {
 constexpr int BK = 64;        // K per pipeline step
 constexpr int CPR = BK / 8;   // 16-byte chunks per row per step
 constexpr int KK = BK / 16;   // MFMA sub-steps per step
-constexpr int DB = 2;         // weight steps in flight
-constexpr int U = 2;          // unroll: a multiple of DB and of the 2 LDS buffers
+constexpr int DB2 = 2;        // weight steps in flight, bf16 weights (16 registers per step)
+constexpr int DB4 = 4;        // weight steps in flight, 4-bit weights (5 registers per step)
 constexpr int LDS_A = 2 * BM * CPR;  // two activation buffers, 16-byte units (64 KB)
 
 __device__ __forceinline__ int swz(int row, int q) { return row * CPR + (q ^ (row & (CPR - 1))); }
+
+// Eight 4-bit codes (element j in bits 4j..4j+3) of one 64-element group
+// with its (scale, bias) word -> eight bf16 weights s*q + b (fp32, then
+// rounded to nearest even), as an MFMA operand fragment.
+__device__ __forceinline__ u32x4_t dequant8(uint32_t c, uint32_t g) {
+  const float s = bf16_lo(g), b = bf16_hi(g);
+  const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;  // elements 0,2,4,6 / 1,3,5,7
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    r[j] = pack_bf16x2(s * (float)((lo >> (8 * j)) & 0xFFu) + b, s * (float)((hi >> (8 * j)) & 0xFFu) + b);
+  return r;
+}
 
 // One tile.  MODE 0: h = silu(A Wg^T) * (A Wu^T) over a 128-column panel of
 // I; wave w owns gate rows [n0+32w, +32) (col block 0) and the up rows of the
@@ -85,8 +102,17 @@ __device__ __forceinline__ int swz(int row, int q) { return row * CPR + (q ^ (ro
 // lets each lane read 16 contiguous bytes.  Loads past the last step
 // re-read the last step (never out of bounds, never conditional), so no
 // control flow surrounds memory operations.
-template <int MODE, int NRB>
+//
+// Q4: the weights are 4-bit codes with a (scale, bias) per 64-element group
+// ("Dequantize weights during matrix multiplication").  A step's 64 K-values
+// of a weight row are exactly one group, so per step and column block a
+// lane loads 16 bytes of codes (its 32 K-values, the four sub-steps) and one
+// group word, and expands each sub-step's eight codes to bf16 operands in
+// registers just before the MFMA; the ring then holds DB4 steps.
+template <int MODE, int NRB, bool Q4>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int panel, u32x4_t* smem) {
+  constexpr int DB = Q4 ? DB4 : DB2;
+  constexpr int U = DB;  // unroll: a multiple of DB and of the 2 LDS buffers
   constexpr int ACH = NRB * 32 * CPR / 256;  // activation chunks per thread per step
   const bool is_shared = tl.g >= p.E;
   const int Ig = is_shared ? p.Is : p.I;
@@ -109,21 +135,35 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   }
   const bool wave_cols = ncol0 < N;  // wave-uniform: does this wave own any output column?
 
-  // ---- this wave's weight rows: col block cb -> one 16-byte chunk per lane per sub-step
+  // ---- this wave's weight rows: col block cb -> one 16-byte chunk per lane per
+  //      sub-step (bf16), or per step plus a group word (4-bit)
   const u32x4_t* bsrc[2];
+  const u32x4_t* qsrc[2];
+  const uint32_t* gsrc[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     int wrow;
-    const uint16_t* base;
+    int64_t rbase;  // first element of the row set within the expert block
     if (MODE == 0) {
       wrow = ncol0 + l32;
-      base = cb == 0 ? W : W + (int64_t)Ig * p.H;  // gate, then up
+      rbase = cb == 0 ? 0 : (int64_t)Ig * p.H;  // gate, then up
     } else {
       wrow = ncol0 + 32 * cb + l32;
-      base = W + (int64_t)2 * Ig * p.H;  // down [H][Ig]
+      rbase = (int64_t)2 * Ig * p.H;  // down [H][Ig]
     }
     if (wrow >= N) wrow = 0;  // columns past N compute on row 0 and are never stored
-    bsrc[cb] = (const u32x4_t*)(base + (int64_t)wrow * ldw) + (CPR / 2) * half;
+    const int64_t e0 = rbase + (int64_t)wrow * ldw;  // the row's first element (a multiple of 64)
+    if (Q4) {
+      const uint32_t* cbase = is_shared ? p.sh_codes : p.ex_codes + (int64_t)tl.g * 3 * p.I * p.H / 8;
+      const uint32_t* gbase = is_shared ? p.sh_groups : p.ex_groups + (int64_t)tl.g * 3 * p.I * p.H / 64;
+      qsrc[cb] = (const u32x4_t*)(cbase + e0 / 8) + half;  // step st: element 2 st
+      gsrc[cb] = gbase + e0 / 64;                          // step st: element st
+      bsrc[cb] = nullptr;
+    } else {
+      bsrc[cb] = (const u32x4_t*)(W + e0) + (CPR / 2) * half;
+      qsrc[cb] = nullptr;
+      gsrc[cb] = nullptr;
+    }
   }
 
   // ---- activation-tile loader: ACH chunks per thread per step (row-contiguous, coalesced)
@@ -145,9 +185,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   }
 
   const int nsteps = K / BK;
-  u32x4_t breg[DB][2][KK];
+  u32x4_t breg[Q4 ? 1 : DB][2][KK];
+  u32x4_t qreg[Q4 ? DB : 1][2];
+  uint32_t greg[Q4 ? DB : 1][2];
   u32x4_t areg[ACH];
-  auto chunk0 = [&](int st) { return (st < nsteps ? st : nsteps - 1) * CPR; };
+  auto clampst = [&](int st) { return st < nsteps ? st : nsteps - 1; };
+  auto chunk0 = [&](int st) { return clampst(st) * CPR; };
+  // weights of step st into ring slot d (all sub-steps)
+  auto load_b = [&](int st, int d) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      if (Q4) {
+        qreg[d][cb] = qsrc[cb][2 * clampst(st)];
+        greg[d][cb] = gsrc[cb][clampst(st)];
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) breg[d][cb][kk] = bsrc[cb][chunk0(st) + kk];
+      }
+    }
+  };
   auto load_a = [&](int st) {
     const int c0 = chunk0(st);
 #pragma unroll
@@ -168,11 +224,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   // flight, activation step 1 in registers
   load_a(0);
 #pragma unroll
-  for (int d = 0; d < DB; ++d)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) breg[d][cb][kk] = bsrc[cb][chunk0(d) + kk];
+  for (int d = 0; d < DB; ++d) load_b(d, d);
   store_a(0);
   load_a(1);
   __syncthreads();
@@ -186,6 +238,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
       store_a((u + 1) & 1);
       load_a(s + 2);
       const int cn = chunk0(s + DB);
+      const int sn = clampst(s + DB);
       const bool active = wave_cols && s < nsteps;
       u32x4_t af[2][NRB];
       auto read_af = [&](u32x4_t (&f)[NRB], int kk) {
@@ -200,16 +253,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
         // the barrier, so every wave runs the same barriers
         if (active) {
           if (kk + 1 < KK) read_af(af[(kk + 1) & 1], kk + 1);
+          u32x4_t bw[2];
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) bw[cb] = Q4 ? dequant8(qreg[ub][cb][kk], greg[ub][cb]) : breg[Q4 ? 0 : ub][cb][kk];
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
-              acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8_t, af[kk & 1][rb]), __builtin_bit_cast(bf16x8_t, breg[ub][cb][kk]),
-                  acc[rb][cb], 0, 0, 0);
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[kk & 1][rb]),
+                                                                    __builtin_bit_cast(bf16x8_t, bw[cb]),
+                                                                    acc[rb][cb], 0, 0, 0);
         }
+        if (Q4) {
+          if (kk == KK - 1) {  // the step's codes are consumed: refill the slot DB steps ahead
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) breg[ub][cb][kk] = bsrc[cb][cn + kk];
+            for (int cb = 0; cb < 2; ++cb) {
+              qreg[ub][cb] = qsrc[cb][2 * sn];
+              greg[ub][cb] = gsrc[cb][sn];
+            }
+          }
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) breg[Q4 ? 0 : ub][cb][kk] = bsrc[cb][cn + kk];
+        }
       }
       __syncthreads();
     }
@@ -255,7 +321,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   }
 }
 
-template <int MODE>
+template <int MODE, bool Q4>
 __global__ __launch_bounds__(256, 1) void k_grouped_gemm(GemmArgs p) {
   __shared__ u32x4_t smem[LDS_A];
 
@@ -276,10 +342,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm(GemmArgs p) {
   // row blocks of 32, rounded up to even: the inner loop is specialised per count
   const int nrb2 = ((tl.rows + 63) >> 6) << 1;
   switch (nrb2) {
-    case 2: gemm_tile<MODE, 2>(p, tl, panel, smem); break;
-    case 4: gemm_tile<MODE, 4>(p, tl, panel, smem); break;
-    case 6: gemm_tile<MODE, 6>(p, tl, panel, smem); break;
-    default: gemm_tile<MODE, 8>(p, tl, panel, smem); break;
+    case 2: gemm_tile<MODE, 2, Q4>(p, tl, panel, smem); break;
+    case 4: gemm_tile<MODE, 4, Q4>(p, tl, panel, smem); break;
+    case 6: gemm_tile<MODE, 6, Q4>(p, tl, panel, smem); break;
+    default: gemm_tile<MODE, 8, Q4>(p, tl, panel, smem); break;
   }
 }
 
@@ -350,8 +416,7 @@ hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const
   const int maxI = pl.I > pl.Is ? pl.I : pl.Is;
   a.npan = (maxI + NWR / 2 - 1) / (NWR / 2);
   a.max_tiles = (int)pl.max_tiles;
-  launch(lc, k_grouped_gemm<0>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
-  return hipGetLastError();
+  return launch(lc, k_grouped_gemm<0, false>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
 }
 
 hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
@@ -374,15 +439,64 @@ hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint
   a.k = pl.k;
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
-  launch(lc, k_grouped_gemm<1>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
-  return hipGetLastError();
+  return launch(lc, k_grouped_gemm<1, false>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
 }
 
 hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float* w, const int32_t* inv,
                           uint16_t* out, const Plan& pl, const Launch& lc) {
-  launch(lc, k_combine, dim3((unsigned)pl.M), dim3(256), y_r, pl.shared ? y_s : nullptr, w,
-                     inv, out, pl.H, pl.k);
-  return hipGetLastError();
+  return launch(lc, k_combine, dim3((unsigned)pl.M), dim3(256), y_r, pl.shared ? y_s : nullptr, w, inv, out, pl.H,
+                pl.k);
+}
+
+hipError_t launch_gemm_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const int32_t* perm,
+                                 const Tile* tiles, const int32_t* ntiles, uint16_t* h_r, uint16_t* h_s,
+                                 const Plan& pl, const Launch& lc) {
+  GemmArgs a{};
+  a.a_x = x;
+  a.ex_codes = ex.codes;
+  a.ex_groups = ex.groups;
+  a.sh_codes = sh.codes;
+  a.sh_groups = sh.groups;
+  a.perm = perm;
+  a.tiles = tiles;
+  a.ntiles = ntiles;
+  a.out_r = h_r;
+  a.out_s = h_s;
+  a.M = pl.M;
+  a.H = pl.H;
+  a.E = pl.E;
+  a.I = pl.I;
+  a.Is = pl.Is;
+  a.k = pl.k;
+  const int maxI = pl.I > pl.Is ? pl.I : pl.Is;
+  a.npan = (maxI + NWR / 2 - 1) / (NWR / 2);
+  a.max_tiles = (int)pl.max_tiles;
+  return launch(lc, k_grouped_gemm<0, true>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
+}
+
+hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q4Weights& ex, const Q4Weights& sh,
+                               const Tile* tiles, const int32_t* ntiles, uint16_t* y_r, uint16_t* y_s, const Plan& pl,
+                               const Launch& lc) {
+  GemmArgs a{};
+  a.a_r = h_r;
+  a.a_s = h_s;
+  a.ex_codes = ex.codes;
+  a.ex_groups = ex.groups;
+  a.sh_codes = sh.codes;
+  a.sh_groups = sh.groups;
+  a.tiles = tiles;
+  a.ntiles = ntiles;
+  a.out_r = y_r;
+  a.out_s = y_s;
+  a.M = pl.M;
+  a.H = pl.H;
+  a.E = pl.E;
+  a.I = pl.I;
+  a.Is = pl.Is;
+  a.k = pl.k;
+  a.npan = (pl.H + NWR - 1) / NWR;
+  a.max_tiles = (int)pl.max_tiles;
+  return launch(lc, k_grouped_gemm<1, true>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
 }
 
 }  // namespace moe

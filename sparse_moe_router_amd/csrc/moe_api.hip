@@ -185,19 +185,38 @@ size_t moe_workspace_size(const moe_desc_t* d, int top_k) {
   return p.total;
 }
 
-moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const void* router_w,
-                                      const void* expert_w, const void* shared_w, int top_k,
-                                      void* out, void* workspace, size_t workspace_bytes,
-                                      void* stream, const moe_routing_t* routing,
-                                      moe_trace_t* trace) {
+}  // extern "C"
+
+namespace {
+
+// The expert weights of one call: bf16 blocks, or 4-bit codes + group words.
+struct Weights {
+  bool q4;
+  const uint16_t* ew;
+  const uint16_t* sw;
+  Q4Weights eq, sq;
+};
+
+moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router_w, const Weights& wt, int top_k,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream,
+                          const moe_routing_t* routing, moe_trace_t* trace) {
   bool gemv = false;
   moe_status_t st = check_desc(d, top_k, &gemv);
   if (st != MOE_OK) return st;
-  if (!x || !router_w || !expert_w || !out) return MOE_ERR_INVALID_ARG;
-  if ((d->I_shared > 0) != (shared_w != nullptr)) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(expert_w, 16) || !aligned(out, 16) ||
-      (shared_w && !aligned(shared_w, 16)))
-    return MOE_ERR_MISALIGNED;
+  if (!x || !router_w || !out) return MOE_ERR_INVALID_ARG;
+  if (wt.q4) {
+    if (!wt.eq.codes || !wt.eq.groups) return MOE_ERR_INVALID_ARG;
+    const bool has_sh = wt.sq.codes || wt.sq.groups;
+    if ((d->I_shared > 0) != has_sh || (has_sh && (!wt.sq.codes || !wt.sq.groups))) return MOE_ERR_INVALID_ARG;
+    if (!aligned(wt.eq.codes, 16) || !aligned(wt.eq.groups, 16) || (has_sh && (!aligned(wt.sq.codes, 16) ||
+                                                                               !aligned(wt.sq.groups, 16))))
+      return MOE_ERR_MISALIGNED;
+  } else {
+    if (!wt.ew) return MOE_ERR_INVALID_ARG;
+    if ((d->I_shared > 0) != (wt.sw != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(wt.ew, 16) || (wt.sw && !aligned(wt.sw, 16))) return MOE_ERR_MISALIGNED;
+  }
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(out, 16)) return MOE_ERR_MISALIGNED;
   if ((st = check_routing(routing)) != MOE_OK) return st;
   const size_t xbytes = (size_t)d->M * d->H * 2;
   if (overlap(x, xbytes, out, xbytes)) return MOE_ERR_INVALID_ARG;
@@ -216,8 +235,6 @@ moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const 
   hipStream_t s = (hipStream_t)stream;
   Tracer tr{trace, s};
   const uint16_t* xb = (const uint16_t*)x;
-  const uint16_t* ew = (const uint16_t*)expert_w;
-  const uint16_t* sw = (const uint16_t*)shared_w;
   hipError_t e;
   if (gemv) {
     float* L = (routing && routing->logits) ? routing->logits : ws_ptr<float>(workspace, p.logits);
@@ -228,11 +245,15 @@ moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const 
            return launch_decode_router(xb, (const uint16_t*)router_w, d->router_bias, L, p, lc);
          })) != hipSuccess)
       return hip_fail(e);
-    if ((e = tr.run(MOE_K_DEC_GATEUP, [&](const Launch& lc) { return launch_decode_gateup(xb, ew, sw, L, ids, w, h, p, lc); })) !=
-        hipSuccess)
+    if ((e = tr.run(MOE_K_DEC_GATEUP, [&](const Launch& lc) {
+           return wt.q4 ? launch_decode_gateup_q4(xb, wt.eq, wt.sq, L, ids, w, h, p, lc)
+                        : launch_decode_gateup(xb, wt.ew, wt.sw, L, ids, w, h, p, lc);
+         })) != hipSuccess)
       return hip_fail(e);
-    if ((e = tr.run(MOE_K_DEC_DOWN, [&](const Launch& lc) { return launch_decode_down(ew, sw, ids, w, h, (uint16_t*)out, p, lc); })) !=
-        hipSuccess)
+    if ((e = tr.run(MOE_K_DEC_DOWN, [&](const Launch& lc) {
+           return wt.q4 ? launch_decode_down_q4(wt.eq, wt.sq, ids, w, h, (uint16_t*)out, p, lc)
+                        : launch_decode_down(wt.ew, wt.sw, ids, w, h, (uint16_t*)out, p, lc);
+         })) != hipSuccess)
       return hip_fail(e);
     return MOE_OK;
   }
@@ -246,11 +267,13 @@ moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const 
   const Tile* tiles = ws_ptr<Tile>(workspace, p.tiles);
   const int32_t* ntiles = ws_ptr<int32_t>(workspace, p.ntiles);
   if ((e = tr.run(MOE_K_GEMM_GATEUP, [&](const Launch& lc) {
-         return launch_gemm_gateup(xb, ew, sw, perm, tiles, ntiles, h_r, h_s, p, lc);
+         return wt.q4 ? launch_gemm_gateup_q4(xb, wt.eq, wt.sq, perm, tiles, ntiles, h_r, h_s, p, lc)
+                      : launch_gemm_gateup(xb, wt.ew, wt.sw, perm, tiles, ntiles, h_r, h_s, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = tr.run(MOE_K_GEMM_DOWN, [&](const Launch& lc) {
-         return launch_gemm_down(h_r, h_s, ew, sw, tiles, ntiles, y_r, y_s, p, lc);
+         return wt.q4 ? launch_gemm_down_q4(h_r, h_s, wt.eq, wt.sq, tiles, ntiles, y_r, y_s, p, lc)
+                      : launch_gemm_down(h_r, h_s, wt.ew, wt.sw, tiles, ntiles, y_r, y_s, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = tr.run(MOE_K_COMBINE, [&](const Launch& lc) {
@@ -258,6 +281,34 @@ moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const 
        })) != hipSuccess)
     return hip_fail(e);
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const void* router_w,
+                                      const void* expert_w, const void* shared_w, int top_k,
+                                      void* out, void* workspace, size_t workspace_bytes,
+                                      void* stream, const moe_routing_t* routing,
+                                      moe_trace_t* trace) {
+  Weights wt{};
+  wt.q4 = false;
+  wt.ew = (const uint16_t*)expert_w;
+  wt.sw = (const uint16_t*)shared_w;
+  return forward_impl(d, x, router_w, wt, top_k, out, workspace, workspace_bytes, stream, routing, trace);
+}
+
+moe_status_t moe_layer_forward_q4(const moe_desc_t* d, const void* x, const void* router_w,
+                                  const moe_q4_t* experts, const moe_q4_t* shared, int top_k, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const moe_routing_t* routing, moe_trace_t* trace) {
+  if (!experts) return MOE_ERR_INVALID_ARG;
+  Weights wt{};
+  wt.q4 = true;
+  wt.eq = Q4Weights{(const uint32_t*)experts->codes, (const uint32_t*)experts->scale_bias};
+  if (shared) wt.sq = Q4Weights{(const uint32_t*)shared->codes, (const uint32_t*)shared->scale_bias};
+  return forward_impl(d, x, router_w, wt, top_k, out, workspace, workspace_bytes, stream, routing, trace);
 }
 
 moe_status_t moe_layer_forward(const moe_desc_t* d, const void* x, const void* router_w,

@@ -89,6 +89,13 @@ inline hipError_t launch(const Launch& L, F kernel, dim3 grid, dim3 block, Args.
   return hipGetLastError();
 }
 
+// 4-bit group-affine weights of one or E experts (packing as the bf16 blocks):
+// codes, 8 per 32-bit word; one (scale, bias) word per 64 elements.
+struct Q4Weights {
+  const uint32_t* codes;
+  const uint32_t* groups;
+};
+
 // Router scores L[M][E] = x Wr^T (+ bias), fp32 (MFMA); clears the chunk masks.
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, float* L,
                                 uint64_t* cmask, int64_t M, int H, int E, const Launch& lc);
@@ -109,6 +116,13 @@ hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const
 hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
                             const uint16_t* shared_w, const Tile* tiles, const int32_t* ntiles,
                             uint16_t* y_r, uint16_t* y_s, const Plan& p, const Launch& lc);
+// The two grouped GEMMs reading 4-bit weights (same outputs and layouts).
+hipError_t launch_gemm_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const int32_t* perm,
+                                 const Tile* tiles, const int32_t* ntiles, uint16_t* h_r, uint16_t* h_s,
+                                 const Plan& p, const Launch& lc);
+hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q4Weights& ex, const Q4Weights& sh,
+                               const Tile* tiles, const int32_t* ntiles, uint16_t* y_r, uint16_t* y_s, const Plan& p,
+                               const Launch& lc);
 // out[t] = y_s[t] + sum_j w[t,j] y_r[inv[t*k+j]]  (bf16 out)
 hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float* w, const int32_t* inv,
                           uint16_t* out, const Plan& p, const Launch& lc);
@@ -125,5 +139,12 @@ hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, con
 hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w, const int32_t* ids,
                               const float* w, const float* h_dec, uint16_t* out, const Plan& p,
                               const Launch& lc);
+
+// The decode kernels above, reading 4-bit weights (same outputs and layout).
+hipError_t launch_decode_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh,
+                                   const float* logits, int32_t* ids, float* w, float* h_dec, const Plan& p,
+                                   const Launch& lc);
+hipError_t launch_decode_down_q4(const Q4Weights& ex, const Q4Weights& sh, const int32_t* ids, const float* w,
+                                 const float* h_dec, uint16_t* out, const Plan& p, const Launch& lc);
 
 }  // namespace moe

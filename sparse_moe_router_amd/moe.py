@@ -23,7 +23,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_MISALIGNED", 5: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_layer_forward", "moe_route", "moe_layer_forward_traced",
-           "moe_status_string", "moe_last_hip_error")
+           "moe_layer_forward_q4", "moe_status_string", "moe_last_hip_error")
 
 # moe_kernel_t
 KERNELS = {1: "router_scores", 2: "topk", 3: "route_scan", 4: "route_scatter", 5: "gemm_gateup",
@@ -45,6 +45,10 @@ class MoeTrace(ctypes.Structure):
     _fields_ = [("begin", ctypes.POINTER(ctypes.c_void_p)), ("end", ctypes.POINTER(ctypes.c_void_p)),
                 ("kernel", ctypes.POINTER(ctypes.c_int32)), ("capacity", ctypes.c_int32),
                 ("count", ctypes.c_int32)]
+
+
+class MoeQ4(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scale_bias", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -71,6 +75,10 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.restype = ctypes.c_int
         L.moe_layer_forward_traced.argtypes = L.moe_layer_forward.argtypes + [ctypes.POINTER(MoeTrace)]
         L.moe_layer_forward_traced.restype = ctypes.c_int
+        L.moe_layer_forward_q4.argtypes = [ctypes.POINTER(MoeDesc), vp, vp, ctypes.POINTER(MoeQ4),
+                                           ctypes.POINTER(MoeQ4), ctypes.c_int, vp, vp, sz, vp,
+                                           ctypes.POINTER(MoeRouting), ctypes.POINTER(MoeTrace)]
+        L.moe_layer_forward_q4.restype = ctypes.c_int
         L.moe_route.argtypes = [ctypes.POINTER(MoeDesc), vp, vp, ctypes.c_int, vp, sz, vp,
                                 ctypes.POINTER(MoeRouting)]
         L.moe_route.restype = ctypes.c_int
@@ -171,6 +179,43 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, expert_w: torch.Tensor,
     else:
         st = lib().moe_layer_forward_traced(*args, ctypes.byref(trace))
     _check(st, "moe_layer_forward")
+    return out
+
+
+def forward_q4(x: torch.Tensor, router_w: torch.Tensor, codes: torch.Tensor, scale_bias: torch.Tensor,
+               shared_codes: Optional[torch.Tensor], shared_scale_bias: Optional[torch.Tensor], top_k: int,
+               out: Optional[torch.Tensor] = None, router_bias: Optional[torch.Tensor] = None,
+               routing: Optional[dict] = None, flags: int = 0, workspace: Optional[torch.Tensor] = None,
+               stream=None, trace: Optional[MoeTrace] = None) -> torch.Tensor:
+    """moe_layer_forward_q4.  codes uint8 [E, 3*I*H/2] (two 4-bit codes per byte, low nibble first);
+    scale_bias int32 [E, 3*I*H/64] (bf16 scale in the low half, bf16 bias in the high half of each
+    word); shared_codes / shared_scale_bias the same for the shared expert (E = 1), or None."""
+    M, H = x.shape
+    E = router_w.shape[0]
+    I = codes.numel() * 2 // (3 * E * H)
+    I_s = 0 if shared_codes is None else shared_codes.numel() * 2 // (3 * H)
+    if scale_bias.numel() * 64 != codes.numel() * 2:
+        raise ValueError("scale_bias must hold one word per 64 codes")
+    if shared_codes is not None and (shared_scale_bias is None or shared_scale_bias.numel() * 64 != shared_codes.numel() * 2):
+        raise ValueError("shared_scale_bias must hold one word per 64 shared codes")
+    if out is None:
+        out = torch.empty_like(x)
+    d = make_desc(M, H, E, I, I_s, flags, router_bias)
+    need = lib().moe_workspace_size(ctypes.byref(d), int(top_k))
+    if need == 0 and M > 0:
+        raise MoeError(2, "moe_workspace_size rejected the shapes")
+    ws = workspace if workspace is not None else _workspace(need, x.device)
+    r = _routing_struct(routing)
+    ex = MoeQ4(_ptr(codes, torch.uint8, "codes"), _ptr(scale_bias, torch.int32, "scale_bias"))
+    sh = None if shared_codes is None else MoeQ4(_ptr(shared_codes, torch.uint8, "shared_codes"),
+                                                  _ptr(shared_scale_bias, torch.int32, "shared_scale_bias"))
+    st = lib().moe_layer_forward_q4(ctypes.byref(d), _ptr(x, torch.bfloat16, "x"),
+                                    _ptr(router_w, torch.bfloat16, "router_w"), ctypes.byref(ex),
+                                    None if sh is None else ctypes.byref(sh), int(top_k),
+                                    _ptr(out, torch.bfloat16, "out"), _ptr(ws, torch.uint8, "workspace"), ws.numel(),
+                                    _stream(stream), None if r is None else ctypes.byref(r),
+                                    None if trace is None else ctypes.byref(trace))
+    _check(st, "moe_layer_forward_q4")
     return out
 
 

@@ -18,7 +18,7 @@ OK, INVALID, SHAPE, WS, MISALIGNED = 0, 1, 2, 3, 4
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -125,3 +125,31 @@ def test_python_binding_refuses_cpu_tensors():
     ex = torch.zeros(16, 3 * 128 * 256, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         moe.forward(x, r, ex, None, 2)
+
+
+def fwd_q4(d, k=2, x=FAKE, r=FAKE + (1 << 24), codes=FAKE + (2 << 24), sb=FAKE + (8 << 24),
+           sh_codes=FAKE + (3 << 24), sh_sb=FAKE + (9 << 24), out=FAKE + (4 << 24), ws=FAKE + (5 << 24),
+           wsb=1 << 40, experts=True, shared=True):
+    ex = moe.MoeQ4(codes, sb)
+    sh = moe.MoeQ4(sh_codes, sh_sb)
+    return moe.lib().moe_layer_forward_q4(ctypes.byref(d), x, r, ctypes.byref(ex) if experts else None,
+                                          ctypes.byref(sh) if shared else None, k, out, ws, wsb, None, None, None)
+
+
+def test_forward_q4_rejects_bad_arguments():
+    d = _desc()
+    assert fwd_q4(d, experts=False) == INVALID
+    assert fwd_q4(d, codes=None) == INVALID
+    assert fwd_q4(d, sb=None) == INVALID
+    assert fwd_q4(d, shared=False) == INVALID  # I_shared > 0 needs shared weights
+    assert fwd_q4(d, sh_sb=None) == INVALID  # half a shared weight set
+    assert fwd_q4(_desc(Is=0)) == INVALID  # shared weights given but I_shared == 0
+    assert fwd_q4(d, x=None) == INVALID
+    assert fwd_q4(d, out=FAKE) == INVALID
+    assert fwd_q4(d, codes=FAKE + (2 << 24) + 4) == MISALIGNED
+    assert fwd_q4(d, sb=FAKE + (8 << 24) + 4) == MISALIGNED
+    assert fwd_q4(d, sh_codes=FAKE + (3 << 24) + 8) == MISALIGNED
+    assert fwd_q4(d, wsb=ws_size(d, 2) - 1) == WS
+    assert fwd_q4(_desc(I=96)) == SHAPE
+    assert fwd_q4(d, k=17) == SHAPE
+    assert fwd_q4(_desc(M=0), ws=None, wsb=0) == OK

@@ -1,0 +1,170 @@
+"""GPU parity of the 4-bit expert-weight path (moe_layer_forward_q4) against
+the oracle: the oracle rebuilds every weight from its code and its group's
+scale and bias (dequant_q4) and runs the same layer in float64, on the
+seeded synthetic workloads (4-bit variant) and on the edge shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from gpu_util import check, moe, routing_buffers, S, SD, f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    moe.lib()
+    yield
+
+
+class HostLayerQ4:
+    """Oracle-side copy of one layer with 4-bit experts, regenerated on the host."""
+
+    def __init__(self, w, layer=0):
+        self.w, self.layer = w, layer
+        self.router = f32(S.router_weight(w, layer))
+        self.bias = S.zipf_router_bias(w, layer)
+        self.shared = None
+        if w.I_shared:
+            c, g = S.q4_shared(w, layer)
+            self.shared = O.dequant_q4(c, g)
+        self._experts = {}
+
+    def x(self, row0, n):
+        return f32(S.x_rows(self.w, row0, n, self.layer))
+
+    def expert(self, e):
+        if e not in self._experts:
+            c, g = S.q4_expert(self.w, self.layer, e)
+            self._experts[e] = O.unpack_expert(O.dequant_q4(c, g), self.w.I, self.w.H)
+        return self._experts[e]
+
+    def oracle(self, x_host, tokens=None):
+        def fn(force):
+            return O.moe_forward(x_host, self.router, self.expert, self.shared, self.w.k, self.w.I, bias=self.bias,
+                                 force_ids=force, tokens=tokens, I_shared=self.w.I_shared)
+        return fn
+
+
+def run_q4(x, r, codes, sb, sc, ssb, k, bias=None, flags=0):
+    M, E = x.shape[0], r.shape[0]
+    grouped = not (M == 1 and not (flags & moe.FLAG_FORCE_GEMM))
+    rb = routing_buffers(M, E, k, grouped=grouped)
+    out = moe.forward_q4(x, r, codes, sb, sc, ssb, k, routing=rb, flags=flags, router_bias=bias)
+    torch.cuda.synchronize()
+    res = {name: t.cpu().numpy() for name, t in rb.items()}
+    res["out"] = out.float().cpu().numpy()
+    return res
+
+
+def bits_to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def test_device_q4_generator_matches_host():
+    w = S.TINY
+    codes = torch.empty(w.expert_elems() // 2, dtype=torch.uint8, device="cuda")
+    sb = torch.empty(w.expert_elems() // 64, dtype=torch.int32, device="cuda")
+    ck, gk = S.q4_expert_key(w, 0, 5, False), S.q4_expert_key(w, 0, 5, True)
+    SD.fill_q4(codes, sb, ck, gk, w.w_sigma)
+    hc, hg = S.q4_expert(w, 0, 5)
+    assert np.array_equal(codes.cpu().numpy(), hc)
+    assert np.array_equal(sb.cpu().numpy().view(np.uint32), hg)
+
+
+def test_q4_tiny_grouped_all_tokens():
+    w = S.TINY
+    hl = HostLayerQ4(w)
+    x, r, ex, esb, sh, ssb = SD.layer_tensors_q4(w)
+    g = run_q4(x, r, ex, esb, sh, ssb, w.k)
+    check(g, hl.oracle(hl.x(0, w.M)), w.k, w.E, label="q4 tiny")
+
+
+@pytest.mark.parametrize("flags", [0, moe.FLAG_FORCE_GEMM])
+def test_q4_tiny_single_rows(flags):
+    w = S.TINY
+    hl = HostLayerQ4(w)
+    _, r, ex, esb, sh, ssb = SD.layer_tensors_q4(w)
+    for t in [0, 9, 63]:
+        x1 = bits_to_dev(S.x_rows(w, t, 1))
+        g = run_q4(x1, r, ex, esb, sh, ssb, w.k, flags=flags)
+        check(g, hl.oracle(hl.x(t, 1)), w.k, w.E, grouped=bool(flags), label=f"q4 tiny row {t} flags {flags}")
+
+
+def test_q4_decode_full_shape():
+    w = S.DECODE
+    for layer, row in [(0, 0), (11, 5)]:
+        hl = HostLayerQ4(w, layer)
+        x1 = bits_to_dev(S.x_rows(w, row, 1, layer))
+        _, r, ex, esb, sh, ssb = SD.layer_tensors_q4(w, layer, x_rows=1)
+        g = run_q4(x1, r, ex, esb, sh, ssb, w.k)
+        del ex, esb
+        check(g, hl.oracle(hl.x(row, 1)), w.k, w.E, grouped=False, label=f"q4 decode layer {layer}")
+
+
+@pytest.mark.parametrize("name", ["PREFILL", "SKEW"])
+def test_q4_prefill_full_sampled(name):
+    w = getattr(S, name)
+    hl = HostLayerQ4(w)
+    x, r, ex, esb, sh, ssb = SD.layer_tensors_q4(w)
+    bias = None if hl.bias is None else torch.from_numpy(hl.bias).cuda()
+    g = run_q4(x, r, ex, esb, sh, ssb, w.k, bias=bias)
+    del ex, esb
+    rng = np.random.default_rng(17)
+    sample = sorted(set(rng.choice(w.M, 6, replace=False).tolist()) | {0, w.M - 1})
+    st = check(g, hl.oracle(hl.x(0, w.M), tokens=sample), w.k, w.E, rows=sample, label=f"q4 {name}")
+    assert g["counts"].sum() == w.M * w.k
+    print(name, st)
+
+
+def _q4_random(E, n, rng, sigma=0.02):
+    """Random 4-bit blocks: codes uint8 [E, n/2], words uint32 [E, n/64] (host), from the generator's recipe."""
+    codes = rng.integers(0, 256, size=(E, n // 2), dtype=np.uint8)
+    words = np.stack([S.q4_scale_bias(int(rng.integers(1 << 62)), n // 64, sigma) for _ in range(E)])
+    return codes, words
+
+
+def _edge_q4(M, H, E, k, I, Is, flags=0, seed=0):
+    rng = np.random.default_rng(seed)
+    q = lambda a: S.bf16_bits_to_f32(S.f32_to_bf16_bits(a.astype(np.float32)))
+    x = q(rng.standard_normal((M, H)))
+    r = q(rng.standard_normal((E, H)) * 0.02)
+    codes, words = _q4_random(E, 3 * I * H, rng)
+    sc = sw = None
+    if Is:
+        sc, sw = _q4_random(1, 3 * Is * H, rng)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).cuda()
+    dev_w = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).cuda()
+    g = run_q4(up(x), up(r), torch.from_numpy(codes).cuda(), dev_w(words),
+               None if sc is None else torch.from_numpy(sc[0]).cuda(), None if sw is None else dev_w(sw[0]),
+               k, flags=flags)
+    experts = lambda e: O.unpack_expert(O.dequant_q4(codes[e], words[e]), I, H)
+    shared = None if sc is None else O.dequant_q4(sc[0], sw[0])
+
+    def fn(force):
+        return O.moe_forward(x, r, experts, shared, k, I, force_ids=force, I_shared=Is)
+    grouped = not (M == 1 and not (flags & moe.FLAG_FORCE_GEMM))
+    return check(g, fn, k, E, grouped=grouped, label=f"q4 M={M} H={H} E={E} k={k} I={I} Is={Is}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 65, 257])
+def test_q4_ragged_token_counts(M):
+    _edge_q4(M, 256, 32, 4, 128, 128, seed=M)
+    if M == 1:
+        _edge_q4(1, 256, 32, 4, 128, 128, flags=moe.FLAG_FORCE_GEMM, seed=100)
+
+
+def test_q4_no_shared_expert_and_shapes():
+    _edge_q4(70, 256, 16, 2, 128, 0, seed=1)
+    _edge_q4(1, 256, 16, 2, 128, 0, seed=2)
+    _edge_q4(60, 192, 16, 2, 64, 256, seed=3)
+    _edge_q4(1, 192, 16, 2, 64, 256, seed=4)
+
+
+def test_q4_many_experts_and_top32():
+    _edge_q4(40, 128, 300, 8, 64, 64, seed=5)
+    _edge_q4(1, 128, 300, 8, 64, 64, seed=6)
+    _edge_q4(1, 128, 64, 32, 64, 64, seed=7)
+    _edge_q4(20, 128, 64, 32, 64, 64, seed=8)
