@@ -49,28 +49,43 @@ def parse():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def kernel_source_hash():
-    """Hash of the library's kernel sources; counter figures taken from other sources are stale."""
+# source files each kernel is built from (traffic figures taken from other sources are stale)
+KERNEL_SOURCES = {
+    "k_dec": ("decode.hip", "wave_topk.h", "weights.h", "moe_internal.h"),
+    "k_grouped_gemm": ("grouped_gemm.hip", "moe_internal.h"),
+    "k_combine": ("grouped_gemm.hip", "moe_internal.h"),
+    "k_router_logits": ("route.hip", "moe_internal.h"),
+    "k_topk": ("route.hip", "wave_topk.h", "moe_internal.h"),
+    "k_route": ("route.hip", "moe_internal.h"),
+}
+
+
+def kernel_source_hash(kernel: str):
+    """Hash of the sources of `kernel` (its name or name prefix), or None if unknown."""
     import hashlib
+    files = next((v for k, v in KERNEL_SOURCES.items() if kernel.startswith(k)), None)
+    if files is None:
+        return None
     h = hashlib.sha256()
     d = os.path.join(ROOT, "sparse_moe_router_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in files:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE and
-    WRITE_SIZE scaled by the copy-kernel calibration), or None if absent or stale."""
+def traffic_for(key: str):
+    """HBM bytes per launch of the kernel under `key` in the committed counter summary (FETCH_SIZE
+    and WRITE_SIZE scaled by the copy-kernel calibration), or None if absent or if the kernel's
+    sources changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash() or kernel not in t.get("kernels", {}):
+    k = t.get("kernels", {}).get(key)
+    if k is None or k.get("source_hash") != kernel_source_hash(key):
         return None
-    k = t["kernels"][kernel]
     return round(k["fetch_kib"] * 1024 * t["fetch_scale"] + k["write_kib"] * 1024 * t["write_scale"])
 
 
@@ -257,7 +272,8 @@ def bench_decode(args, hip, moe, SD, S, q4=False):
     # 4-byte scale/bias word per 64 elements = 0.5625 bytes per element)
     wb = 0.5625 if q4 else 2
     layer_bytes = int((k + 1) * w.expert_elems() * wb) + E * H * 2 + 2 * H * 2
-    gateup_bytes = int(k * 2 * I * H * wb) + H * 2 + E * 4 + k * I * 4
+    # the gate/up kernel streams the selected experts' and the shared expert's gate/up rows
+    gateup_bytes = int((k * I + w.I_shared) * 2 * H * wb) + H * 2 + E * 4 + (k * I + w.I_shared) * 4
     dom = "dec_gateup"
     avg_ms = sum(kt[dom]) / len(kt[dom])
     achieved = gateup_bytes / (avg_ms * 1e-3) / 1e9
@@ -267,7 +283,7 @@ def bench_decode(args, hip, moe, SD, S, q4=False):
         layer_hbm_frac=layer_bytes * L / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         kernels_us={n: round(1000.0 * sum(v) / len(v), 3) for n, v in kt.items()},
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None if q4 else traffic_for("k_dec_gateup"),
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for("k_dec_gateup<q4>" if q4 else "k_dec_gateup"),
                       kernel="k_dec_gateup" + ("<q4>" if q4 else ""),
                       bytes_per_launch=gateup_bytes, avg_us=round(avg_ms * 1000, 3)),
     )
@@ -346,13 +362,16 @@ def bench_prefill(args, hip, moe, SD, S, w, q4=False):
     kname = "k_grouped_gemm<0, q4> (gate/up + SwiGLU)" if q4 else "k_grouped_gemm<0> (gate/up + SwiGLU)"
     if mfma_bound:
         roof = dict(bound="mfma", achieved=round(ach_tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach_tf / BF16_PEAK_TFLOPS, 4), traffic=None, kernel=kname,
+                    frac=round(ach_tf / BF16_PEAK_TFLOPS, 4),
+                    traffic=traffic_for(f"k_grouped_gemm<0,q4>@{w.name}" if q4 else f"k_grouped_gemm<0>@{w.name}"),
+                    kernel=kname,
                     flops_per_launch=gu_flops, bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
                     hbm_frac=round(ach / HBM_PEAK_GBS, 4))
     else:
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBS, 4),
-                    traffic=None if q4 else traffic_for(f"k_grouped_gemm<0>@{w.name}"), kernel=kname,
+                    traffic=traffic_for(f"k_grouped_gemm<0,q4>@{w.name}" if q4 else f"k_grouped_gemm<0>@{w.name}"),
+                    kernel=kname,
                     bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
                     mfma_frac=round(ach_tf / BF16_PEAK_TFLOPS, 4))
     res = dict(
