@@ -121,7 +121,7 @@ class LayerCall:
     """Pre-marshalled moe_layer_forward (bf16 experts) or moe_layer_forward_q4 arguments for one
     layer.  ex / sh: bf16 tensors, or (codes, scale_bias) pairs for 4-bit experts."""
 
-    def __init__(self, moe, x, r, ex, sh, k, out, ws, bias=None, routing=None):
+    def __init__(self, moe, x, r, ex, sh, k, out, ws, bias=None, routing=None, flags=0):
         import torch
         M, H = x.shape
         E = r.shape[0]
@@ -137,7 +137,7 @@ class LayerCall:
             Is = 0 if sh is None else sh.numel() // (3 * H)
             wargs = [ex.data_ptr(), None if sh is None else sh.data_ptr()]
         self.lib = moe.lib()
-        self.desc = moe.make_desc(M, H, E, I, Is, 0, bias)
+        self.desc = moe.make_desc(M, H, E, I, Is, flags, bias)
         self.routing = moe._routing_struct(routing)
         self.args = [ctypes.byref(self.desc), x.data_ptr(), r.data_ptr(), *wargs, k, out.data_ptr(), ws.data_ptr(),
                      ws.numel(), None, None if self.routing is None else ctypes.byref(self.routing)]
@@ -290,6 +290,63 @@ def bench_decode(args, hip, moe, SD, S, q4=False):
     return res, (layers, xpool)
 
 
+def bench_small(args, hip, moe, S, layers, xpool, Ms=(2, 4, 8, 16, 32, 64)):
+    """Small batches of M token rows through the decode workload's layers: the matrix-vector
+    path over the union of the selected experts (FORCE_GEMV) beside the grouped path
+    (FORCE_GEMM), both HIP-graph replayed.  Bytes = the union's expert weights + the shared
+    expert + router + activations, from the routing the call itself produced."""
+    import torch
+    w = S.DECODE
+    H, E, I, k, Is = w.H, w.E, w.I, w.k, w.I_shared
+    L = len(layers)
+    q4 = isinstance(layers[0][1], tuple)
+    wb = 0.5625 if q4 else 2
+    cap_stream = torch.cuda.Stream()
+    steps = max(5, args.steps // 10)
+    res = {}
+    for M in Ms:
+        x = xpool[:M]
+        entry = {}
+        for name, flags in (("small", moe.FLAG_FORCE_GEMV), ("grouped", moe.FLAG_FORCE_GEMM)):
+            out = torch.empty(L, M, H, dtype=torch.bfloat16, device="cuda")
+            ids = torch.empty(L, M, k, dtype=torch.int32, device="cuda")
+            ws = torch.empty(moe.workspace_size(M, H, E, I, Is, k, flags=flags), dtype=torch.uint8, device="cuda")
+            calls = [LayerCall(moe, x, r, ex, sh, k, out[l], ws, routing={"topk_ids": ids[l]}, flags=flags)
+                     for l, (r, ex, sh) in enumerate(layers)]
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_stream):
+                for c in calls:
+                    c()
+            for _ in range(2):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            union = sum(len(torch.unique(ids[l]).tolist()) for l in range(L)) / L
+            layer_bytes = (union + 1) * w.expert_elems() * wb + E * H * 2 + 2 * M * H * 2
+            kt = kernel_times(hip, moe, lambda s, tr: [c(tr) for c in calls], L, 3, 7)
+            entry[name] = {"tok_s": round(M * 1000.0 / ms, 1), "us_per_layer": round(ms * 1000.0 / L, 3),
+                           "hbm_frac": round(layer_bytes * L / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "kernels_us": {n: round(1000.0 * sum(v) / len(v), 3) for n, v in kt.items()}}
+            entry["union_experts"] = round(union, 2)
+            if name == "small":
+                small_out = out.clone()
+            else:
+                d = (out.float() - small_out.float()).abs().amax(dim=-1) / small_out.float().abs().amax(dim=-1)
+                entry["paths_max_rel_diff"] = round(float(d.max()), 5)
+            del calls, ws
+        res[str(M)] = entry
+    return res
+
+
 def cpu_decode(S, O, layers_sample=2, rows=128):
     """Oracle on a bounded sample of the decode workload: `rows` single-token (M=1)
     calls through each of `layers_sample` layers; the selected experts' weights are
@@ -433,13 +490,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     dec, keep = bench_decode(args, hip, moe, SD, S)
+    small = bench_small(args, hip, moe, S, *keep)
     del keep
     torch.cuda.empty_cache()
     pre = bench_prefill(args, hip, moe, SD, S, S.PREFILL)
     skew = bench_prefill(args, hip, moe, SD, S, S.SKEW)
-    dec_q4 = pre_q4 = None
+    dec_q4 = pre_q4 = small_q4 = None
     if not args.no_q4:
         dq, keep = bench_decode(args, hip, moe, SD, S, q4=True)
+        small_q4 = bench_small(args, hip, moe, S, *keep, Ms=(2, 8, 16))
         del keep
         torch.cuda.empty_cache()
         dec_q4 = {"value": round(dq["value"], 2), "unit": "tok/s", "ms_per_step": round(dq["ms_per_step"], 4),
@@ -472,6 +531,9 @@ def main():
         "prefill_skew": skew,
         "decode_q4": dec_q4,
         "prefill_q4": pre_q4,
+        "small_batch": {"config": {"workload": f"M token rows x {args.layers} decode layers (same weights), "
+                                               f"matrix-vector path over the union of selected experts "
+                                               f"vs grouped path"}, "bf16": small, "q4": small_q4},
     }
     print(json.dumps(line), flush=True)
 

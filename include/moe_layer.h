@@ -80,8 +80,15 @@ typedef enum {
   MOE_ERR_HIP = 5                  /* a HIP launch failed */
 } moe_status_t;
 
-/* Path selection.  Default: the decode path when M == 1, else the grouped path. */
-#define MOE_FLAG_FORCE_GEMV 0x1u /* decode (matrix-vector) path; requires M == 1 */
+/* Path selection.  M == 1: the decode path.  2 <= M <= 64: the small-batch
+ * path, matrix-vector products over the union of the experts the rows select,
+ * each expert's weights read once for all rows routed to it (section "Limits
+ * of further optimization": few-row batches pick different experts).  By
+ * default the matrix-vector paths run when M <= 64 and M * top_k <= 4 * E
+ * (at most four assignments per expert on average), the grouped path
+ * otherwise; the flags override that choice.  Only the grouped path reports
+ * counts / offsets / perm. */
+#define MOE_FLAG_FORCE_GEMV 0x1u /* matrix-vector paths; requires M <= 64 */
 #define MOE_FLAG_FORCE_GEMM 0x2u /* grouped (matrix-matrix) path, also at M == 1 */
 
 typedef struct {
@@ -137,7 +144,11 @@ typedef enum {
   MOE_K_COMBINE = 7,           /* grouped path: weighted combine + shared expert */
   MOE_K_DEC_ROUTER = 8,        /* decode: router scores */
   MOE_K_DEC_GATEUP = 9,        /* decode: shared expert gate/up, top-k, routed gate/up */
-  MOE_K_DEC_DOWN = 10          /* decode: down projections + combine */
+  MOE_K_DEC_DOWN = 10,         /* decode: down projections + combine */
+  MOE_K_SM_ROUTER = 11,        /* small batch: router scores */
+  MOE_K_SM_TOPK = 12,          /* small batch: top-k, weights, union of the selected experts */
+  MOE_K_SM_GATEUP = 13,        /* small batch: shared and union experts' gate/up + activation */
+  MOE_K_SM_DOWN = 14           /* small batch: down projections + combine */
 } moe_kernel_t;
 
 /* Instrumentation for moe_layer_forward_traced: caller-created hipEvent_t

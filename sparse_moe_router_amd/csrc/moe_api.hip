@@ -54,10 +54,20 @@ bool make_plan(Plan* p, int64_t M, int H, int E, int I, int Is, int k, bool gemv
   size_t off = 0;
   bool ok = true;
   if (gemv) {
-    ok &= place(&off, &p->logits, (uint64_t)E * 4);
-    ok &= place(&off, &p->ids, (uint64_t)k * 4);
-    ok &= place(&off, &p->w, (uint64_t)k * 4);
-    ok &= place(&off, &p->h_r, ((uint64_t)k * I + (uint64_t)Is) * 4);  // fp32 [k][I] then [Is]
+    // one row: fp32 h = [k][I] routed, then [Is] shared; more rows: the
+    // union lists, h = [M*k][I] per assignment, then [M][Is]
+    const uint64_t A = (uint64_t)p->A;
+    ok &= place(&off, &p->logits, (uint64_t)M * E * 4);
+    ok &= place(&off, &p->ids, A * 4);
+    ok &= place(&off, &p->w, A * 4);
+    ok &= place(&off, &p->h_r, (A * I + (uint64_t)M * Is) * 4);
+    if (M > 1) {
+      ok &= place(&off, &p->un_count, 8);
+      ok &= place(&off, &p->un_exp, (A < (uint64_t)E ? A : (uint64_t)E) * 4);
+      ok &= place(&off, &p->un_off, ((A < (uint64_t)E ? A : (uint64_t)E) + 1) * 4);
+      ok &= place(&off, &p->un_pair, A * 4);
+      ok &= place(&off, &p->un_unit, (uint64_t)small_units(M, k, E) * 4);
+    }
   } else {
     const uint64_t A = (uint64_t)p->A;
     ok &= place(&off, &p->logits, (uint64_t)M * E * 4);
@@ -99,8 +109,11 @@ moe_status_t check_desc(const moe_desc_t* d, int top_k, bool* gemv) {
   if (d->E < 1 || d->E > kMaxE) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (top_k < 1 || top_k > d->E || top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (d->M * (int64_t)top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
-  if ((d->flags & MOE_FLAG_FORCE_GEMV) && d->M != 1) return MOE_ERR_UNSUPPORTED_SHAPE;
-  *gemv = (d->flags & MOE_FLAG_FORCE_GEMV) || (d->M == 1 && !(d->flags & MOE_FLAG_FORCE_GEMM));
+  if ((d->flags & MOE_FLAG_FORCE_GEMV) && d->M > kMaxSmallM) return MOE_ERR_UNSUPPORTED_SHAPE;
+  // default: one row -> decode path; up to kMaxSmallM rows averaging at most
+  // kSmallRows assignments per expert -> small-batch path; else grouped
+  const bool small = d->M <= kMaxSmallM && d->M * (int64_t)top_k <= (int64_t)kSmallRows * d->E;
+  *gemv = (d->flags & MOE_FLAG_FORCE_GEMV) || (small && !(d->flags & MOE_FLAG_FORCE_GEMM));
   if (d->router_bias && !aligned(d->router_bias, 16)) return MOE_ERR_MISALIGNED;
   return MOE_OK;
 }
@@ -116,6 +129,11 @@ moe_status_t check_routing(const moe_routing_t* r) {
 template <class T>
 T* ws_ptr(void* ws, size_t off) {
   return (T*)((char*)ws + off);
+}
+
+SmallUnion small_union(void* ws, const Plan& p) {
+  return SmallUnion{ws_ptr<int32_t>(ws, p.un_count), ws_ptr<int32_t>(ws, p.un_exp), ws_ptr<int32_t>(ws, p.un_off),
+                    ws_ptr<int32_t>(ws, p.un_pair), ws_ptr<int32_t>(ws, p.un_unit)};
 }
 
 // Hands each launch the next pair of trace events (if any): the kernel is
@@ -236,6 +254,31 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   Tracer tr{trace, s};
   const uint16_t* xb = (const uint16_t*)x;
   hipError_t e;
+  if (gemv && p.M > 1) {
+    float* L = (routing && routing->logits) ? routing->logits : ws_ptr<float>(workspace, p.logits);
+    int32_t* ids = (routing && routing->topk_ids) ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
+    float* w = (routing && routing->topk_w) ? routing->topk_w : ws_ptr<float>(workspace, p.w);
+    float* h = ws_ptr<float>(workspace, p.h_r);
+    const SmallUnion un = small_union(workspace, p);
+    if ((e = tr.run(MOE_K_SM_ROUTER, [&](const Launch& lc) {
+           return launch_small_router(xb, (const uint16_t*)router_w, d->router_bias, L, p, lc);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = tr.run(MOE_K_SM_TOPK, [&](const Launch& lc) { return launch_small_topk(L, ids, w, un, p, lc); })) !=
+        hipSuccess)
+      return hip_fail(e);
+    if ((e = tr.run(MOE_K_SM_GATEUP, [&](const Launch& lc) {
+           return wt.q4 ? launch_small_gateup_q4(xb, wt.eq, wt.sq, un, h, p, lc)
+                        : launch_small_gateup(xb, wt.ew, wt.sw, un, h, p, lc);
+         })) != hipSuccess)
+      return hip_fail(e);
+    if ((e = tr.run(MOE_K_SM_DOWN, [&](const Launch& lc) {
+           return wt.q4 ? launch_small_down_q4(wt.eq, wt.sq, w, un, h, (uint16_t*)out, p, lc)
+                        : launch_small_down(wt.ew, wt.sw, w, un, h, (uint16_t*)out, p, lc);
+         })) != hipSuccess)
+      return hip_fail(e);
+    return MOE_OK;
+  }
   if (gemv) {
     float* L = (routing && routing->logits) ? routing->logits : ws_ptr<float>(workspace, p.logits);
     int32_t* ids = (routing && routing->topk_ids) ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
@@ -344,6 +387,15 @@ moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w,
     int32_t* ids = routing->topk_ids ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
     float* w = routing->topk_w ? routing->topk_w : ws_ptr<float>(workspace, p.w);
     hipError_t e;
+    if (p.M > 1) {
+      if ((e = launch_small_router((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias, L, p,
+                                   Launch{s, nullptr, nullptr})) != hipSuccess)
+        return hip_fail(e);
+      if ((e = launch_small_topk(L, ids, w, small_union(workspace, p), p, Launch{s, nullptr, nullptr})) !=
+          hipSuccess)
+        return hip_fail(e);
+      return MOE_OK;
+    }
     if ((e = launch_decode_router((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias, L, q,
                                   Launch{s, nullptr, nullptr})) != hipSuccess)
       return hip_fail(e);

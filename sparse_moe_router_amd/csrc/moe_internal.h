@@ -15,6 +15,8 @@ constexpr int kChunk = 64;    // tokens per routing chunk: one bit per token in 
 constexpr int kTileM = 256;   // rows per grouped-GEMM tile (block-map granularity)
 constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 32;
+constexpr int kMaxSmallM = 64;  // most rows the matrix-vector paths take
+constexpr int kSmallRows = 4;   // small-batch path: assignments per register batch / work unit
 
 // ----------------------------------------------------------------- vector types
 
@@ -62,6 +64,7 @@ struct Plan {
   int64_t max_tiles;
   // byte offsets into the workspace (all 256-aligned)
   size_t logits, ids, w, cmask, cbase, counts, offsets, perm, inv, tiles, ntiles, h_r, h_s, y_r, y_s;
+  size_t un_count, un_exp, un_off, un_pair, un_unit;  // small-batch path: union of the selected experts
   size_t total;
 };
 
@@ -81,12 +84,16 @@ struct Launch {
 };
 
 template <typename F, typename... Args>
-inline hipError_t launch(const Launch& L, F kernel, dim3 grid, dim3 block, Args... args) {
+inline hipError_t launch_shm(const Launch& L, F kernel, dim3 grid, dim3 block, size_t shm, Args... args) {
   if (L.start || L.stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, L.s, L.start, L.stop, 0, args...);
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, L.s, L.start, L.stop, 0, args...);
   else
-    hipLaunchKernelGGL(kernel, grid, block, 0, L.s, args...);
+    hipLaunchKernelGGL(kernel, grid, block, shm, L.s, args...);
   return hipGetLastError();
+}
+template <typename F, typename... Args>
+inline hipError_t launch(const Launch& L, F kernel, dim3 grid, dim3 block, Args... args) {
+  return launch_shm(L, kernel, grid, block, 0, args...);
 }
 
 // 4-bit group-affine weights of one or E experts (packing as the bf16 blocks):
@@ -146,5 +153,34 @@ hipError_t launch_decode_gateup_q4(const uint16_t* x, const Q4Weights& ex, const
                                    const Launch& lc);
 hipError_t launch_decode_down_q4(const Q4Weights& ex, const Q4Weights& sh, const int32_t* ids, const float* w,
                                  const float* h_dec, uint16_t* out, const Plan& p, const Launch& lc);
+
+// Small-batch path (2 <= M <= kMaxSmallM): matrix-vector products over the
+// union of the experts the rows select.  h: fp32 [M*k][I] per assignment,
+// then [M][Is] shared.
+struct SmallUnion {
+  int32_t* count;  // [2] distinct experts U, down-projection work units
+  int32_t* exp;    // [min(E, M*k)] experts, ascending
+  int32_t* off;    // [U+1] list offsets into pair
+  int32_t* pair;   // [M*k] assignments t*k + j, grouped by expert
+  int32_t* unit;   // [small_units(M, k, E)] down-projection work units
+};
+// Most work units: one per kSmallRows assignments of each expert, rounded
+// up per expert (at most min(E, M*k) roundings), plus the shared expert's.
+inline int64_t small_units(int64_t M, int k, int E) {
+  const int64_t A = M * k;
+  return (A < E ? A : E) + (A + kSmallRows - 1) / kSmallRows + (M + kSmallRows - 1) / kSmallRows;
+}
+hipError_t launch_small_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                               const Plan& p, const Launch& lc);
+hipError_t launch_small_topk(const float* logits, int32_t* ids, float* w, const SmallUnion& un, const Plan& p,
+                             const Launch& lc);
+hipError_t launch_small_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
+                               const SmallUnion& un, float* h, const Plan& p, const Launch& lc);
+hipError_t launch_small_down(const uint16_t* expert_w, const uint16_t* shared_w, const float* w,
+                             const SmallUnion& un, const float* h, uint16_t* out, const Plan& p, const Launch& lc);
+hipError_t launch_small_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const SmallUnion& un,
+                                  float* h, const Plan& p, const Launch& lc);
+hipError_t launch_small_down_q4(const Q4Weights& ex, const Q4Weights& sh, const float* w, const SmallUnion& un,
+                                const float* h, uint16_t* out, const Plan& p, const Launch& lc);
 
 }  // namespace moe

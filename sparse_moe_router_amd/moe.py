@@ -27,7 +27,8 @@ EXPORTS = ("moe_workspace_size", "moe_layer_forward", "moe_route", "moe_layer_fo
 
 # moe_kernel_t
 KERNELS = {1: "router_scores", 2: "topk", 3: "route_scan", 4: "route_scatter", 5: "gemm_gateup",
-           6: "gemm_down", 7: "combine", 8: "dec_router", 9: "dec_gateup", 10: "dec_down"}
+           6: "gemm_down", 7: "combine", 8: "dec_router", 9: "dec_gateup", 10: "dec_down",
+           11: "sm_router", 12: "sm_topk", 13: "sm_gateup", 14: "sm_down"}
 
 
 class MoeDesc(ctypes.Structure):

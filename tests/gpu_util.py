@@ -83,10 +83,20 @@ def routing_buffers(M, E, k, dev="cuda", grouped=True):
     return r
 
 
+def grouped_path(M, k, E, flags):
+    """True when the call runs the grouped path (which alone reports counts / offsets / perm):
+    the path rule of moe_layer.h."""
+    if flags & moe.FLAG_FORCE_GEMV:
+        return False
+    if flags & moe.FLAG_FORCE_GEMM:
+        return True
+    return not (M <= 64 and M * k <= 4 * E)
+
+
 def run_gpu(x, r, ex, sh, k, bias=None, flags=0):
     """One moe_layer_forward call; returns numpy out (fp32 of bf16) and routing outputs."""
     M, E = x.shape[0], r.shape[0]
-    grouped = not (M == 1 and not (flags & moe.FLAG_FORCE_GEMM))
+    grouped = grouped_path(M, k, E, flags)
     rb = routing_buffers(M, E, k, grouped=grouped)
     out = moe.forward(x, r, ex, sh, k, routing=rb, flags=flags, router_bias=bias)
     torch.cuda.synchronize()
@@ -135,3 +145,38 @@ def oracle_fn(hl: HostLayer, x_host, tokens=None):
 @functools.lru_cache(maxsize=None)
 def gpu_ok():
     return torch.cuda.is_available()
+
+
+def upload(a, dtype=torch.bfloat16):
+    """Host fp32 array holding bf16-representable values -> device bf16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dtype).cuda()
+
+
+def bits_to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def rand_case(M, H, E, k, I, Is, seed=0, bias=None, zero_router=False, hot=None):
+    """Random bf16-representable layer inputs (host fp32): x ~ N(0,1), weights ~ N(0, 0.02)."""
+    rng = np.random.default_rng(seed)
+    q = lambda a: S.bf16_bits_to_f32(S.f32_to_bf16_bits(a.astype(np.float32)))
+    x = q(rng.standard_normal((M, H)))
+    r = np.zeros((E, H), np.float32) if zero_router else q(rng.standard_normal((E, H)) * 0.02)
+    ex = q(rng.standard_normal((E, 3 * I * H)) * 0.02)
+    sh = q(rng.standard_normal(3 * Is * H) * 0.02) if Is else None
+    if hot is not None:
+        bias = np.zeros(E, np.float32)
+        bias[hot] = 100.0
+    return x, r, ex, sh, bias
+
+
+def edge_case(M, H, E, k, I, Is, flags=0, **kw):
+    """One random layer through the GPU, every output checked against the oracle."""
+    x, r, ex, sh, bias = rand_case(M, H, E, k, I, Is, **kw)
+    g = run_gpu(upload(x), upload(r), upload(ex), None if sh is None else upload(sh), k,
+                bias=None if bias is None else torch.from_numpy(bias).cuda(), flags=flags)
+
+    def fn(force):
+        return O.moe_forward(x, r, ex, sh, k, I, bias=bias, force_ids=force, I_shared=Is)
+    return g, check(g, fn, k, E, grouped=grouped_path(M, k, E, flags),
+                    label=f"M={M} H={H} E={E} k={k} I={I} Is={Is} flags={flags} {kw}")

@@ -61,7 +61,9 @@ def test_workspace_size_valid_and_invalid():
     assert ws_size(_desc(), 17) == 0  # top_k > E
     assert ws_size(_desc(E=64), 33) == 0  # top_k > 32
     assert ws_size(_desc(M=1 << 28), 8) == 0  # M*k >= 2^31
-    assert ws_size(_desc(M=5, flags=moe.FLAG_FORCE_GEMV), 2) == 0
+    assert ws_size(_desc(M=65, flags=moe.FLAG_FORCE_GEMV), 2) == 0  # matrix-vector paths take M <= 64
+    small = ws_size(_desc(M=5, flags=moe.FLAG_FORCE_GEMV), 2)
+    assert small > ws_size(_desc(M=1, flags=moe.FLAG_FORCE_GEMV), 2) > 0
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails its checks first
@@ -91,7 +93,7 @@ def test_forward_rejects_bad_arguments():
     assert fwd(_desc(H=100)) == SHAPE
     assert fwd(d, k=0) == SHAPE
     assert fwd(d, k=17) == SHAPE
-    assert fwd(_desc(M=3, flags=moe.FLAG_FORCE_GEMV)) == SHAPE
+    assert fwd(_desc(M=65, flags=moe.FLAG_FORCE_GEMV)) == SHAPE
     assert fwd(_desc(flags=3)) == INVALID
     bad_bias = _desc(bias=FAKE + (6 << 24) + 4)
     assert fwd(bad_bias) == MISALIGNED

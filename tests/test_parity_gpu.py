@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import oracle.moe_oracle as O
-from gpu_util import (HostLayer, check, device_layer, moe, oracle_fn, run_gpu, S, SD, f32)
+from gpu_util import (HostLayer, bits_to_dev, check, device_layer, edge_case as _edge, moe, oracle_fn,
+                      run_gpu, S, SD, f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -16,15 +17,6 @@ def _gpu():
     assert torch.cuda.is_available(), "GPU tests need an MI355X"
     moe.lib()
     yield
-
-
-def upload(a, dtype=torch.bfloat16):
-    """Host fp32 array holding bf16-representable values -> device bf16 tensor."""
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dtype).cuda()
-
-
-def bits_to_dev(bits):
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
 # ------------------------------------------------------------------ generator
@@ -115,33 +107,10 @@ def test_decode_full_shape():
 
 # ------------------------------------------------------------------ edge cases (every output checked)
 
-def _rand_case(M, H, E, k, I, Is, seed=0, bias=None, zero_router=False, hot=None):
-    rng = np.random.default_rng(seed)
-    q = lambda a: S.bf16_bits_to_f32(S.f32_to_bf16_bits(a.astype(np.float32)))
-    x = q(rng.standard_normal((M, H)))
-    r = np.zeros((E, H), np.float32) if zero_router else q(rng.standard_normal((E, H)) * 0.02)
-    ex = q(rng.standard_normal((E, 3 * I * H)) * 0.02)
-    sh = q(rng.standard_normal(3 * Is * H) * 0.02) if Is else None
-    if hot is not None:
-        bias = np.zeros(E, np.float32)
-        bias[hot] = 100.0
-    return x, r, ex, sh, bias
-
-
-def _edge(M, H, E, k, I, Is, flags=0, **kw):
-    x, r, ex, sh, bias = _rand_case(M, H, E, k, I, Is, **kw)
-    g = run_gpu(upload(x), upload(r), upload(ex), None if sh is None else upload(sh), k,
-                bias=None if bias is None else torch.from_numpy(bias).cuda(), flags=flags)
-
-    def fn(force):
-        return O.moe_forward(x, r, ex, sh, k, I, bias=bias, force_ids=force, I_shared=Is)
-    grouped = not (M == 1 and not (flags & moe.FLAG_FORCE_GEMM))
-    return g, check(g, fn, k, E, grouped=grouped, label=f"M={M} H={H} E={E} k={k} I={I} Is={Is} {kw}")
-
-
 @pytest.mark.parametrize("M", [1, 2, 63, 64, 65, 257, 700])
 def test_ragged_token_counts(M):
-    _edge(M, 256, 32, 4, 128, 128, flags=moe.FLAG_FORCE_GEMM if M == 1 else 0, seed=M)
+    # grouped path at every M (small M would default to the matrix-vector paths)
+    _edge(M, 256, 32, 4, 128, 128, flags=moe.FLAG_FORCE_GEMM if M <= 64 else 0, seed=M)
 
 
 def test_no_shared_expert():

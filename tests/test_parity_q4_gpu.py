@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle.moe_oracle as O
-from gpu_util import check, moe, routing_buffers, S, SD, f32
+from gpu_util import check, grouped_path, moe, routing_buffers, S, SD, f32
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ class HostLayerQ4:
 
 def run_q4(x, r, codes, sb, sc, ssb, k, bias=None, flags=0):
     M, E = x.shape[0], r.shape[0]
-    grouped = not (M == 1 and not (flags & moe.FLAG_FORCE_GEMM))
+    grouped = grouped_path(M, k, E, flags)
     rb = routing_buffers(M, E, k, grouped=grouped)
     out = moe.forward_q4(x, r, codes, sb, sc, ssb, k, routing=rb, flags=flags, router_bias=bias)
     torch.cuda.synchronize()
@@ -145,15 +145,15 @@ def _edge_q4(M, H, E, k, I, Is, flags=0, seed=0):
 
     def fn(force):
         return O.moe_forward(x, r, experts, shared, k, I, force_ids=force, I_shared=Is)
-    grouped = not (M == 1 and not (flags & moe.FLAG_FORCE_GEMM))
+    grouped = grouped_path(M, k, E, flags)
     return check(g, fn, k, E, grouped=grouped, label=f"q4 M={M} H={H} E={E} k={k} I={I} Is={Is}")
 
 
 @pytest.mark.parametrize("M", [1, 2, 65, 257])
 def test_q4_ragged_token_counts(M):
-    _edge_q4(M, 256, 32, 4, 128, 128, seed=M)
-    if M == 1:
-        _edge_q4(1, 256, 32, 4, 128, 128, flags=moe.FLAG_FORCE_GEMM, seed=100)
+    _edge_q4(M, 256, 32, 4, 128, 128, seed=M)  # M = 2: the small-batch path
+    if M <= 64:
+        _edge_q4(M, 256, 32, 4, 128, 128, flags=moe.FLAG_FORCE_GEMM, seed=100 + M)
 
 
 def test_q4_no_shared_expert_and_shapes():
@@ -164,7 +164,30 @@ def test_q4_no_shared_expert_and_shapes():
 
 
 def test_q4_many_experts_and_top32():
-    _edge_q4(40, 128, 300, 8, 64, 64, seed=5)
+    _edge_q4(40, 128, 300, 8, 64, 64, flags=moe.FLAG_FORCE_GEMM, seed=5)
     _edge_q4(1, 128, 300, 8, 64, 64, seed=6)
     _edge_q4(1, 128, 64, 32, 64, 64, seed=7)
     _edge_q4(20, 128, 64, 32, 64, 64, seed=8)
+
+
+# ------------------------------------------------------------------ small-batch path (4-bit experts)
+
+def test_q4_small_decode_shape():
+    w = S.DECODE
+    M, layer = 8, 2
+    hl = HostLayerQ4(w, layer)
+    _, r, ex, esb, sh, ssb = SD.layer_tensors_q4(w, layer, x_rows=1)
+    g = run_q4(bits_to_dev(S.x_rows(w, 20, M, layer)), r, ex, esb, sh, ssb, w.k, flags=moe.FLAG_FORCE_GEMV)
+    del ex, esb
+    check(g, hl.oracle(hl.x(20, M)), w.k, w.E, grouped=False, label=f"q4 small decode-shape M={M}")
+
+
+@pytest.mark.parametrize("M", [2, 16, 64])
+def test_q4_small_edges(M):
+    _edge_q4(M, 256, 32, 4, 128, 128, flags=moe.FLAG_FORCE_GEMV, seed=300 + M)
+
+
+def test_q4_small_shapes():
+    _edge_q4(7, 256, 16, 2, 128, 0, flags=moe.FLAG_FORCE_GEMV, seed=9)
+    _edge_q4(7, 192, 16, 2, 64, 256, flags=moe.FLAG_FORCE_GEMV, seed=10)
+    _edge_q4(20, 128, 64, 32, 64, 64, flags=moe.FLAG_FORCE_GEMV, seed=11)
