@@ -220,13 +220,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = (f32x16_t){};
 
-  // prologue: activation step 0 -> LDS buffer 0, weight steps 0 .. DB-1 in
-  // flight, activation step 1 in registers
+  // prologue: activation step 0 -> LDS buffer 0, activation step 1 in
+  // registers, then weight steps 0 .. DB-1 in flight.  Issuing the weights
+  // after activation step 1, as in every later step, keeps the compiler's
+  // wait counts at the loop head exact (it merges the entry state with the
+  // back-edge state, and a shorter queue behind activation step 1 on entry
+  // would make every step wait for weights issued one step earlier).
   load_a(0);
-#pragma unroll
-  for (int d = 0; d < DB; ++d) load_b(d, d);
   store_a(0);
   load_a(1);
+#pragma unroll
+  for (int d = 0; d < DB; ++d) load_b(d, d);
   __syncthreads();
 
   // step s: weight slot s % DB, LDS buffer s % 2 (step s+1 goes to the other one)
