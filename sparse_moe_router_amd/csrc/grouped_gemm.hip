@@ -13,22 +13,25 @@
 //    output projection goes with its routing score and the shared expert.
 //
 // Tile: up to 256 rows of one expert group (eight 32-row blocks) x 256
-// weight rows, one 4-wave workgroup per CU.  Every wave covers all rows of
-// the tile and its own 64 weight rows (a 256x64 fp32 accumulator, 256
-// registers, in AGPRs).  The weights -- the HBM stream -- go straight from
-// global memory into MFMA operand registers, each byte loaded once per tile
-// and never through LDS; the activation tile (rows of a routed group
-// gathered through the scatter permutation, never copied) is staged once
-// per K-step in LDS and read by all four waves.  With tiles of 256 rows an
-// expert's weights are read once whenever it has at most 256 rows (all
-// experts at near-uniform routing).  The number of 32-row blocks is a
-// template parameter chosen per tile (rounded up to even), so the inner
-// loop has no branches and row blocks past the group's rows cost nothing.
+// weight rows, one 8-wave workgroup per CU (two waves per SIMD: the LDS
+// serves one wave's operand reads about half as fast as two waves', and one
+// wave's stalls hide behind the other's MFMAs).  Weights and the gathered
+// activation rows (rows of a routed group through the scatter permutation,
+// never copied) travel straight from global memory into LDS rings by
+// global->LDS transfers, 8 rows x 128 bytes per instruction, each weight byte
+// once per tile; a wave computes up to 128 rows x 64 columns (128 fp32
+// accumulator registers).  With tiles of 256 rows an expert's weights are
+// read once whenever it has at most 256 rows (all experts at near-uniform
+// routing).  The number of 32-row blocks is a template parameter chosen per
+// tile (rounded up to even), so the inner loop has no branches and row
+// blocks past the group's rows cost nothing.
 //
 // Launch order is XCD-aware: workgroup b runs on XCD b % 8, and consecutive
 // logical tiles (the panels of one row tile, then the next row tile of the
 // same expert) are given to the same XCD so activation rows and weight
 // panels are re-read from that XCD's L2 instead of HBM.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -63,11 +66,41 @@ struct GemmArgs {
 constexpr int BK = 64;        // K per pipeline step
 constexpr int CPR = BK / 8;   // 16-byte chunks per row per step
 constexpr int KK = BK / 16;   // MFMA sub-steps per step
-constexpr int DB2 = 2;        // weight steps in flight, bf16 weights (16 registers per step)
-constexpr int DB4 = 4;        // weight steps in flight, 4-bit weights (5 registers per step)
-constexpr int LDS_A = 2 * BM * CPR;  // two activation buffers, 16-byte units (64 KB)
+constexpr int SA = BM * CPR;  // activation stage: BM rows x BK, 16-byte units (32 KB)
+constexpr int SB = NWR * CPR; // weight stage: NWR rows x BK (32 KB); 4-bit: codes then group words
+constexpr int DA = 2;         // activation stages in the LDS ring
+constexpr int DW = 3;         // weight stages in the LDS ring (2 steps ahead)
 
-__device__ __forceinline__ int swz(int row, int q) { return row * CPR + (q ^ (row & (CPR - 1))); }
+// The LDS rings: distinct arrays per stage, so that the compiler can tell a
+// read of one stage from the transfers still in flight into the others.
+struct Ring {
+  u32x4_t* a[DA];
+  u32x4_t* w[DW];
+};
+
+// global -> LDS transfer of 16 (or 4) bytes per lane: lane i of the wave
+// writes bytes [16 i, 16 i + 16) after the wave-uniform LDS address `dst`.
+__device__ __forceinline__ void dma16(const void* src, u32x4_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 left at its maximum, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// Workgroup barrier that orders nothing by itself: the waits before it are
+// explicit, and the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Eight 4-bit codes (element j in bits 4j..4j+3) of one 64-element group
 // with its (scale, bias) word -> eight bf16 weights s*q + b (fp32, then
@@ -82,96 +115,99 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t c, uint32_t g) {
   return r;
 }
 
-// One tile.  MODE 0: h = silu(A Wg^T) * (A Wu^T) over a 128-column panel of
-// I; wave w owns gate rows [n0+32w, +32) (col block 0) and the up rows of the
-// same columns (col block 1), so SwiGLU is lane-local.  MODE 1: y = A Wd^T
-// over a 256-column panel of H; wave w owns columns [n0+64w, +64).
+// One tile, eight waves (two per SIMD, so one wave's LDS and memory stalls
+// overlap the other's MFMAs).  Wave w = 4 rg + cg: column group cg, row group
+// rg.  MODE 0: h = silu(A Wg^T) * (A Wu^T) over a 128-column panel of I;
+// column group cg owns gate rows [n0+32cg, +32) (col block 0) and the up rows
+// of the same columns (col block 1), so SwiGLU is lane-local.  MODE 1:
+// y = A Wd^T over a 256-column panel of H; column group cg owns columns
+// [n0+64cg, +64).  Row group rg owns the 32-row blocks rb = rg, rg+2, ...
 //
-// K runs in steps of BK with register pipelines.  Weights: DB ring slots;
-// as soon as the MFMAs of sub-step kk have read their weight fragments, the
-// slot's fragment kk is refilled with the same chunk DB steps ahead, so the
-// weight loads spread through the MFMA phase and about DB steps of weights
-// stay in flight.  Activations: the chunks of step s+1 are written to the
-// other LDS buffer at the start of step s; they were loaded one step
-// earlier, before that step's weight loads, so waiting for them (loads
-// complete in issue order) never waits for the newer weight loads.  The
-// activation fragments are double-buffered across MFMA sub-steps, so the
-// LDS reads of sub-step kk+1 overlap the MFMAs of sub-step kk.  Within a
-// step, MFMA sub-step kk and lane half h take the 8 K-values
-// 32h+8kk .. 32h+8kk+7 on both operands, a consistent permutation of K that
-// lets each lane read 16 contiguous bytes.  Loads past the last step
-// re-read the last step (never out of bounds, never conditional), so no
-// control flow surrounds memory operations.
+// K runs in steps of BK through two LDS rings filled by direct global->LDS
+// transfers (no register staging): the weight tile (NWR rows x BK) in DW
+// stages, DW - 1 steps ahead, and the gathered activation tile (rows of a
+// routed group through the scatter permutation) in DA stages, one step
+// ahead.  Every transfer moves 8 rows x 128 bytes (whole cache lines).  At
+// step s each wave waits for its own transfers of step s (exact counts: the
+// transfers issued after them are known), passes the barrier (then every
+// wave's transfers of step s are done), refills the stages consumed at step
+// s-1 and multiplies from the stages of step s.  Rows of a stage are 128
+// bytes with the 16-byte chunks XOR-swizzled by the row (chunk q of row r at
+// position q ^ (r & 7)), realised by choosing each lane's source chunk, so
+// the MFMA operand reads are conflict-free.  MFMA sub-step kk and lane half
+// h take the 8 K-values 32h+8kk .. 32h+8kk+7 on both operands, a consistent
+// permutation of K.
 //
-// Q4: the weights are 4-bit codes with a (scale, bias) per 64-element group
-// ("Dequantize weights during matrix multiplication").  A step's 64 K-values
-// of a weight row are exactly one group, so per step and column block a
-// lane loads 16 bytes of codes (its 32 K-values, the four sub-steps) and one
-// group word, and expands each sub-step's eight codes to bf16 operands in
-// registers just before the MFMA; the ring then holds DB4 steps.
+// Q4: a step's 64 K-values of a weight row are one group: the stage holds
+// the rows' 32 bytes of codes and their group words, expanded to bf16
+// operands in registers just before the MFMA.
 template <int MODE, int NRB, bool Q4>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int panel, u32x4_t* smem) {
-  constexpr int DB = Q4 ? DB4 : DB2;
-  constexpr int U = DB;  // unroll: a multiple of DB and of the 2 LDS buffers
-  constexpr int ACH = NRB * 32 * CPR / 256;  // activation chunks per thread per step
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int panel, const Ring& ring) {
+  constexpr int NRH = NRB / 2;     // row blocks per row group
+  constexpr int U = DA * DW;       // unroll: every ring stage index static
   const bool is_shared = tl.g >= p.E;
   const int Ig = is_shared ? p.Is : p.I;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  u32x4_t(*sA)[BM * CPR] = (u32x4_t(*)[BM * CPR])smem;
+  const int cg = wave & 3, rg = wave >> 2;
+  const int lr = lane >> 3, lq = (lane & 7) ^ lr;  // transfers: row within 8, swizzled source chunk
 
-  const uint16_t* W = is_shared ? p.shared_w : p.expert_w + (int64_t)tl.g * 3 * p.I * p.H;
   int K, N, ncol0, ldw;
   if (MODE == 0) {
     K = p.H;
     N = Ig;
-    ncol0 = panel * (NWR / 2) + 32 * wave;
+    ncol0 = panel * (NWR / 2) + 32 * cg;
     ldw = p.H;
   } else {
     K = Ig;
     N = p.H;
-    ncol0 = panel * NWR + WN * wave;
+    ncol0 = panel * NWR + WN * cg;
     ldw = Ig;
   }
   const bool wave_cols = ncol0 < N;  // wave-uniform: does this wave own any output column?
+  const int nsteps = K / BK;
 
-  // ---- this wave's weight rows: col block cb -> one 16-byte chunk per lane per
-  //      sub-step (bf16), or per step plus a group word (4-bit)
-  const u32x4_t* bsrc[2];
-  const u32x4_t* qsrc[2];
-  const uint32_t* gsrc[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  // ---- weight rows of column group cg: (col block cb, row l of 32) -> first element
+  auto wrow_elem = [&](int cb, int l) -> int64_t {
     int wrow;
-    int64_t rbase;  // first element of the row set within the expert block
+    int64_t rbase;
     if (MODE == 0) {
-      wrow = ncol0 + l32;
+      wrow = ncol0 + l;
       rbase = cb == 0 ? 0 : (int64_t)Ig * p.H;  // gate, then up
     } else {
-      wrow = ncol0 + 32 * cb + l32;
+      wrow = ncol0 + 32 * cb + l;
       rbase = (int64_t)2 * Ig * p.H;  // down [H][Ig]
     }
     if (wrow >= N) wrow = 0;  // columns past N compute on row 0 and are never stored
-    const int64_t e0 = rbase + (int64_t)wrow * ldw;  // the row's first element (a multiple of 64)
-    if (Q4) {
-      const uint32_t* cbase = is_shared ? p.sh_codes : p.ex_codes + (int64_t)tl.g * 3 * p.I * p.H / 8;
-      const uint32_t* gbase = is_shared ? p.sh_groups : p.ex_groups + (int64_t)tl.g * 3 * p.I * p.H / 64;
-      qsrc[cb] = (const u32x4_t*)(cbase + e0 / 8) + half;  // step st: element 2 st
-      gsrc[cb] = gbase + e0 / 64;                          // step st: element st
-      bsrc[cb] = nullptr;
-    } else {
-      bsrc[cb] = (const u32x4_t*)(W + e0) + (CPR / 2) * half;
-      qsrc[cb] = nullptr;
-      gsrc[cb] = nullptr;
-    }
+    return rbase + (int64_t)wrow * ldw;
+  };
+  // stage row of (cg, cb, l): R = 64 cg + 32 cb + l; this wave moves cb = rg
+  const char* wsrc;            // bf16 rows, or 4-bit codes
+  const char* gsrc = nullptr;  // 4-bit group words
+  uint32_t woff[4];            // byte offsets within the expert block
+  uint32_t goff = 0;
+  if (Q4) {
+    const int64_t eb = is_shared ? 0 : (int64_t)tl.g * 3 * p.I * p.H;  // expert block, elements
+    wsrc = (const char*)(is_shared ? p.sh_codes : p.ex_codes) + eb / 2;
+    gsrc = (const char*)(is_shared ? p.sh_groups : p.ex_groups) + eb / 16;
+    // codes: rows 64cg + 32rg + lane/2, 16 bytes (half lane&1) each
+    woff[0] = (uint32_t)(wrow_elem(rg, lane >> 1) / 2 + 16 * (lane & 1));
+    woff[1] = woff[2] = woff[3] = 0;
+    // group words: rows 64cg + lane (moved by row group 0)
+    goff = (uint32_t)(wrow_elem(lane >> 5, lane & 31) / 64 * 4);
+  } else {
+    const uint16_t* W = is_shared ? p.shared_w : p.expert_w + (int64_t)tl.g * 3 * p.I * p.H;
+    wsrc = (const char*)W;
+    // transfer i: rows 8i + lane/8 of col block rg, chunk lq
+#pragma unroll
+    for (int i = 0; i < 4; ++i) woff[i] = (uint32_t)((wrow_elem(rg, 8 * i + lr) + 8 * lq) * 2);
   }
 
-  // ---- activation-tile loader: ACH chunks per thread per step (row-contiguous, coalesced)
-  const u32x4_t* asrc[ACH];
-  int adst[ACH];
+  // ---- activation rows this wave moves: rows (wave*NRH + i)*8 + lane/8, chunk lq
+  const char* asrc[NRH];
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int c = tid + 256 * i, row = c / CPR, q = c % CPR;
+  for (int i = 0; i < NRH; ++i) {
+    const int row = (wave * NRH + i) * 8 + lr;
     const int r = row < tl.rows ? row : 0;
     const uint16_t* rowp;
     if (MODE == 0) {
@@ -180,111 +216,138 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
     } else {
       rowp = (is_shared ? p.a_s : p.a_r) + ((int64_t)tl.pos0 + r) * Ig;
     }
-    asrc[i] = (const u32x4_t*)rowp + q;
-    adst[i] = swz(row, q);
+    asrc[i] = (const char*)(rowp + 8 * lq);
   }
 
-  const int nsteps = K / BK;
-  u32x4_t breg[Q4 ? 1 : DB][2][KK];
-  u32x4_t qreg[Q4 ? DB : 1][2];
-  uint32_t greg[Q4 ? DB : 1][2];
-  u32x4_t areg[ACH];
+  auto load_a = [&](u32x4_t* st, int s) {
+#pragma unroll
+    for (int i = 0; i < NRH; ++i) dma16(asrc[i] + (int64_t)s * 128, st + (wave * NRH + i) * 64);
+  };
+  auto load_w = [&](u32x4_t* st, int s) {
+    if (Q4) {
+      dma16(wsrc + woff[0] + (int64_t)s * 32, st + (cg * 2 + rg) * 64);
+      if (rg == 0) dma4(gsrc + goff + (int64_t)s * 4, (uint32_t*)(st + 2 * NWR) + cg * 64);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16(wsrc + woff[i] + (int64_t)s * 128, st + (cg * 8 + rg * 4 + i) * 64);
+    }
+  };
+
+  f32x16_t acc[NRH][2];
+#pragma unroll
+  for (int j = 0; j < NRH; ++j)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[j][cb] = (f32x16_t){};
+
+  // operand reads: activation row 32 (2j + rg) + l32, weight row 64 cg + 32 cb
+  // + l32, chunk 4 half + kk, swizzled by the row (both rows are = l32 mod 8)
+  const int swr = l32 & 7;
+  // One K-step from stages (sa, sw).  The step's transfers (activation step
+  // a_next into na, weight step w_next into nw) are issued between the MFMA
+  // sub-steps: a wave that stalls issuing them leaves its SIMD to the other
+  // wave there, instead of all transfers of a step queueing up front.  The
+  // scheduling barriers keep that order (and the transfers after the barrier
+  // of the step).
+  auto step = [&](const u32x4_t* sa, const u32x4_t* sw, u32x4_t* na, int a_next, u32x4_t* nw, int w_next) {
+    u32x4_t af[2][NRH], bf[2][2];
+    u32x4_t bq[2];
+    uint32_t bg[2] = {0, 0};
+    auto read_af = [&](u32x4_t (&f)[NRH], int kk) {
+      const int q = (4 * half + kk) ^ swr;
+#pragma unroll
+      for (int j = 0; j < NRH; ++j) f[j] = sa[(32 * (2 * j + rg) + l32) * CPR + q];
+    };
+    auto read_bf = [&](u32x4_t (&f)[2], int kk) {
+      const int q = (4 * half + kk) ^ swr;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) f[cb] = sw[(64 * cg + 32 * cb + l32) * CPR + q];
+    };
+    if (Q4) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int R = 64 * cg + 32 * cb + l32;
+        bq[cb] = sw[2 * R + half];
+        bg[cb] = ((const uint32_t*)(sw + 2 * NWR))[R];
+      }
+    } else {
+      read_bf(bf[0], 0);
+    }
+    read_af(af[0], 0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) {
+        read_af(af[(kk + 1) & 1], kk + 1);
+        if (!Q4) read_bf(bf[(kk + 1) & 1], kk + 1);
+      }
+      u32x4_t bw[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) bw[cb] = Q4 ? dequant8(bq[cb][kk], bg[cb]) : bf[kk & 1][cb];
+#pragma unroll
+      for (int j = 0; j < NRH; ++j)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          acc[j][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[kk & 1][j]),
+                                                               __builtin_bit_cast(bf16x8_t, bw[cb]),
+                                                               acc[j][cb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) load_a(na, a_next);
+      if (kk == 1) load_w(nw, w_next);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // prologue: weight steps 0 .. DW-2, then activation step 0.  Transfers
+  // are never conditional (a branch would merge the compiler's wait
+  // bookkeeping into a full wait): steps past the end re-read the last step
+  // into a stage nobody reads.
   auto clampst = [&](int st) { return st < nsteps ? st : nsteps - 1; };
-  auto chunk0 = [&](int st) { return clampst(st) * CPR; };
-  // weights of step st into ring slot d (all sub-steps)
-  auto load_b = [&](int st, int d) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      if (Q4) {
-        qreg[d][cb] = qsrc[cb][2 * clampst(st)];
-        greg[d][cb] = gsrc[cb][clampst(st)];
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) breg[d][cb][kk] = bsrc[cb][chunk0(st) + kk];
-      }
-    }
-  };
-  auto load_a = [&](int st) {
-    const int c0 = chunk0(st);
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) areg[i] = asrc[i][c0];
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) sA[buf][adst[i]] = areg[i];
-  };
+  for (int d = 0; d < DW - 1; ++d) load_w(ring.w[d], clampst(d));
+  load_a(ring.a[0], 0);
 
-  f32x16_t acc[NRB][2];
+  // The K loop, one copy per kind of wave (a branch inside the loop would
+  // merge the compiler's wait bookkeeping of both kinds at every step).
+  auto kloop = [&](auto cols, auto nw) {
+    constexpr int NWC = decltype(nw)::value;
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = (f32x16_t){};
-
-  // prologue: activation step 0 -> LDS buffer 0, activation step 1 in
-  // registers, then weight steps 0 .. DB-1 in flight.  Issuing the weights
-  // after activation step 1, as in every later step, keeps the compiler's
-  // wait counts at the loop head exact (it merges the entry state with the
-  // back-edge state, and a shorter queue behind activation step 1 on entry
-  // would make every step wait for weights issued one step earlier).
-  load_a(0);
-  store_a(0);
-  load_a(1);
-#pragma unroll
-  for (int d = 0; d < DB; ++d) load_b(d, d);
-  __syncthreads();
-
-  // step s: weight slot s % DB, LDS buffer s % 2 (step s+1 goes to the other one)
-  for (int s0 = 0; s0 < nsteps; s0 += U) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u;
-      const int ub = u % DB;
-      store_a((u + 1) & 1);
-      load_a(s + 2);
-      const int cn = chunk0(s + DB);
-      const int sn = clampst(s + DB);
-      const bool active = wave_cols && s < nsteps;
-      u32x4_t af[2][NRB];
-      auto read_af = [&](u32x4_t (&f)[NRB], int kk) {
-        const int q = (CPR / 2) * half + kk;
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) f[rb] = sA[u & 1][swz(32 * rb + l32, q)];
-      };
-      if (active) read_af(af[0], 0);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        // a step past the end (odd nsteps) only repeats the clamped loads and
-        // the barrier, so every wave runs the same barriers
-        if (active) {
-          if (kk + 1 < KK) read_af(af[(kk + 1) & 1], kk + 1);
-          u32x4_t bw[2];
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) bw[cb] = Q4 ? dequant8(qreg[ub][cb][kk], greg[ub][cb]) : breg[Q4 ? 0 : ub][cb][kk];
-#pragma unroll
-          for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-              acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[kk & 1][rb]),
-                                                                    __builtin_bit_cast(bf16x8_t, bw[cb]),
-                                                                    acc[rb][cb], 0, 0, 0);
-        }
-        if (Q4) {
-          if (kk == KK - 1) {  // the step's codes are consumed: refill the slot DB steps ahead
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-              qreg[ub][cb] = qsrc[cb][2 * sn];
-              greg[ub][cb] = gsrc[cb][sn];
-            }
-          }
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u;
+        if (s >= nsteps) break;  // uniform
+        // own transfers of step s done: after activation step s (issued
+        // during step s-1) only a weight step was issued (NWC transfers); at
+        // s = 0 the activation transfers were the last ones.  Own operand
+        // reads of step s-1 are done too (lgkmcnt 0), so the stages of step
+        // s-1 may be refilled once every wave has passed the barrier.
+        if (s == 0)
+          wait_vm_lgkm0<0>();
+        else
+          wait_vm_lgkm0<NWC>();
+        barrier_only();
+        if (decltype(cols)::value) {
+          step(ring.a[u % DA], ring.w[u % DW], ring.a[(u + 1) % DA], clampst(s + 1), ring.w[(u + DW - 1) % DW],
+               clampst(s + DW - 1));
         } else {
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) breg[Q4 ? 0 : ub][cb][kk] = bsrc[cb][cn + kk];
+          load_a(ring.a[(u + 1) % DA], clampst(s + 1));
+          load_w(ring.w[(u + DW - 1) % DW], clampst(s + DW - 1));
         }
       }
-      __syncthreads();
     }
+  };
+  // weight transfers per wave per step: bf16 4 (the row group's col block of
+  // its column group); 4-bit 1 of codes, plus the group words in row group 0
+  typedef std::integral_constant<int, Q4 ? 2 : 4> NW0;
+  typedef std::integral_constant<int, Q4 ? 1 : 4> NW1;
+  if (wave_cols) {
+    if (rg == 0) kloop(std::true_type{}, NW0{}); else kloop(std::true_type{}, NW1{});
+  } else {
+    if (rg == 0) kloop(std::false_type{}, NW0{}); else kloop(std::false_type{}, NW1{});
   }
+  // every wave's reads done before the activation stage is reused for staging
+  wait_vm_lgkm0<0>();
+  barrier_only();
   if (!wave_cols) return;
+  u32x4_t* smem = ring.a[0];
 
   // ---- epilogue: per 32-row block, round to bf16, stage through this wave's
   //      slice of the (now idle) LDS, write 16-byte chunks.
@@ -296,16 +359,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   uint16_t* obase = is_shared ? p.out_s : p.out_r;
   const int ldo = MODE == 0 ? Ig : p.H;
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    if (32 * rb >= tl.rows) break;  // uniform; rb stays a constant
+  for (int j = 0; j < NRH; ++j) {
+    const int rb = 2 * j + rg;
+    if (32 * rb >= tl.rows) break;  // uniform; j stays a constant
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * half + (r & 3);
       if (MODE == 0) {
-        stage[row * OC + l32] = (uint16_t)f32_to_bf16(silu(acc[rb][0][r]) * acc[rb][1][r]);
+        stage[row * OC + l32] = (uint16_t)f32_to_bf16(silu(acc[j][0][r]) * acc[j][1][r]);
       } else {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) stage[row * OC + 32 * cb + l32] = (uint16_t)f32_to_bf16(acc[rb][cb][r]);
+        for (int cb = 0; cb < 2; ++cb) stage[row * OC + 32 * cb + l32] = (uint16_t)f32_to_bf16(acc[j][cb][r]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -326,8 +390,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
 }
 
 template <int MODE, bool Q4>
-__global__ __launch_bounds__(256, 1) void k_grouped_gemm(GemmArgs p) {
-  __shared__ u32x4_t smem[LDS_A];
+__global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmArgs p) {
+  __shared__ u32x4_t sA0[SA], sA1[SA], sW0[SB], sW1[SB], sW2[SB];  // 160 KB
+  const Ring rg{{sA0, sA1}, {sW0, sW1, sW2}};
 
   // ---- logical tile from the XCD-aware launch order
   const int nt = *p.ntiles;
@@ -346,10 +411,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm(GemmArgs p) {
   // row blocks of 32, rounded up to even: the inner loop is specialised per count
   const int nrb2 = ((tl.rows + 63) >> 6) << 1;
   switch (nrb2) {
-    case 2: gemm_tile<MODE, 2, Q4>(p, tl, panel, smem); break;
-    case 4: gemm_tile<MODE, 4, Q4>(p, tl, panel, smem); break;
-    case 6: gemm_tile<MODE, 6, Q4>(p, tl, panel, smem); break;
-    default: gemm_tile<MODE, 8, Q4>(p, tl, panel, smem); break;
+    case 2: gemm_tile<MODE, 2, Q4>(p, tl, panel, rg); break;
+    case 4: gemm_tile<MODE, 4, Q4>(p, tl, panel, rg); break;
+    case 6: gemm_tile<MODE, 6, Q4>(p, tl, panel, rg); break;
+    default: gemm_tile<MODE, 8, Q4>(p, tl, panel, rg); break;
   }
 }
 
@@ -420,7 +485,7 @@ hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const
   const int maxI = pl.I > pl.Is ? pl.I : pl.Is;
   a.npan = (maxI + NWR / 2 - 1) / (NWR / 2);
   a.max_tiles = (int)pl.max_tiles;
-  return launch(lc, k_grouped_gemm<0, false>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
+  return launch(lc, k_grouped_gemm<0, false>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(512), a);
 }
 
 hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
@@ -443,7 +508,7 @@ hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint
   a.k = pl.k;
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
-  return launch(lc, k_grouped_gemm<1, false>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
+  return launch(lc, k_grouped_gemm<1, false>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(512), a);
 }
 
 hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float* w, const int32_t* inv,
@@ -475,7 +540,7 @@ hipError_t launch_gemm_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q
   const int maxI = pl.I > pl.Is ? pl.I : pl.Is;
   a.npan = (maxI + NWR / 2 - 1) / (NWR / 2);
   a.max_tiles = (int)pl.max_tiles;
-  return launch(lc, k_grouped_gemm<0, true>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
+  return launch(lc, k_grouped_gemm<0, true>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(512), a);
 }
 
 hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q4Weights& ex, const Q4Weights& sh,
@@ -500,7 +565,7 @@ hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q
   a.k = pl.k;
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
-  return launch(lc, k_grouped_gemm<1, true>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(256), a);
+  return launch(lc, k_grouped_gemm<1, true>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(512), a);
 }
 
 }  // namespace moe
