@@ -26,10 +26,9 @@
 // tile (rounded up to even), so the inner loop has no branches and row
 // blocks past the group's rows cost nothing.
 //
-// Launch order is XCD-aware: workgroup b runs on XCD b % 8, and consecutive
-// logical tiles (the panels of one row tile, then the next row tile of the
-// same expert) are given to the same XCD so activation rows and weight
-// panels are re-read from that XCD's L2 instead of HBM.
+// Launch order is XCD-aware: workgroup b runs on XCD b % 8; the tiles are
+// dealt to the XCDs round-robin (heaviest first) and the panels of a tile
+// stay on one XCD, so its activation rows are re-read from that XCD's L2.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -394,16 +393,17 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmArgs p) {
   __shared__ u32x4_t sA0[SA], sA1[SA], sW0[SB], sW1[SB], sW2[SB];  // 160 KB
   const Ring rg{{sA0, sA1}, {sW0, sW1, sW2}};
 
-  // ---- logical tile from the XCD-aware launch order
-  const int nt = *p.ntiles;
-  const int V = (nt < p.max_tiles ? nt : p.max_tiles) * p.npan;
+  // ---- tile of this workgroup, XCD-aware: workgroup b runs on XCD b % 8;
+  //      XCD x takes the tiles t = x (mod 8), all panels of a tile in a row
+  //      (its activation rows are re-read from that XCD's L2), the last tiles
+  //      of the block map first (the shared expert's full 256-row tiles, the
+  //      heaviest, start early and spread over all XCDs)
+  const int nt = *p.ntiles < p.max_tiles ? *p.ntiles : p.max_tiles;
   const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
-  const int per = (V + 7) >> 3;
-  if (local >= per) return;
-  const int lid = xcd * per + local;
-  if (lid >= V) return;
-  const Tile tl = p.tiles[lid / p.npan];
-  const int panel = lid % p.npan;
+  const int j = local / p.npan, panel = local % p.npan;  // j-th tile of this XCD
+  const int t = nt - 1 - (8 * j + (7 - xcd));            // from the end, dealt round-robin
+  if (t < 0) return;
+  const Tile tl = p.tiles[t];
   if (MODE == 0) {
     const int Ig = tl.g >= p.E ? p.Is : p.I;
     if (panel * (NWR / 2) >= Ig) return;
@@ -460,7 +460,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
   }
 }
 
-unsigned xcd_grid(int64_t logical) { return (unsigned)(((logical + 7) / 8) * 8); }
+// 8 XCDs x (most tiles per XCD) x panels: every tile's panels have a workgroup
+unsigned xcd_grid(int64_t max_tiles, int npan) { return (unsigned)(8 * ((max_tiles + 7) / 8) * npan); }
 
 }  // namespace
 
@@ -485,7 +486,7 @@ hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const
   const int maxI = pl.I > pl.Is ? pl.I : pl.Is;
   a.npan = (maxI + NWR / 2 - 1) / (NWR / 2);
   a.max_tiles = (int)pl.max_tiles;
-  return launch(lc, k_grouped_gemm<0, false>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(512), a);
+  return launch(lc, k_grouped_gemm<0, false>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 
 hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
@@ -508,7 +509,7 @@ hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint
   a.k = pl.k;
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
-  return launch(lc, k_grouped_gemm<1, false>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(512), a);
+  return launch(lc, k_grouped_gemm<1, false>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 
 hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float* w, const int32_t* inv,
@@ -540,7 +541,7 @@ hipError_t launch_gemm_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q
   const int maxI = pl.I > pl.Is ? pl.I : pl.Is;
   a.npan = (maxI + NWR / 2 - 1) / (NWR / 2);
   a.max_tiles = (int)pl.max_tiles;
-  return launch(lc, k_grouped_gemm<0, true>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(512), a);
+  return launch(lc, k_grouped_gemm<0, true>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 
 hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q4Weights& ex, const Q4Weights& sh,
@@ -565,7 +566,7 @@ hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q
   a.k = pl.k;
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
-  return launch(lc, k_grouped_gemm<1, true>, dim3(xcd_grid(pl.max_tiles * a.npan)), dim3(512), a);
+  return launch(lc, k_grouped_gemm<1, true>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 
 }  // namespace moe
