@@ -7,7 +7,9 @@ distinct weights (H=2048, 256 experts top-8 + 1 shared, I=512, bf16; 64.7 GB
 of weights, so every layer streams from HBM).  One step = one token through
 all 40 layers, replayed from a captured HIP graph; the input row rotates
 through a pool of 64 rows.  Alongside: prefill of M=4096 tokens through one
-layer (same shapes), one step = one layer call.
+layer (same shapes; near-uniform and Zipf-skewed routing), one step = one
+layer call; and a long prompt of 131,072 tokens through one layer as 16
+calls of 8,192 rows with one reused workspace, one step = all 16 calls.
 
 Inputs are seeded synthetic tensors generated on the device before timing.
 Printed: one JSON line with throughput, the dominant kernel's roofline
@@ -38,6 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-q4", action="store_true", help="skip the 4-bit expert-weight runs")
+    ap.add_argument("--no-long", action="store_true", help="skip the chunked long-prefill run")
     ap.add_argument("--layers", type=int, default=40, help=argparse.SUPPRESS)
     ap.add_argument("--trace-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -378,6 +381,32 @@ def cpu_decode(S, O, layers_sample=2, rows=128):
 
 # ------------------------------------------------------------------ prefill
 
+def gateup_roofline(kt, w, M, nonempty, q4):
+    """Roofline position of the gate/up grouped GEMM (k_grouped_gemm<0>) for M rows: algorithmic
+    bytes (weights of the experts that received rows + the shared expert, x once, h written) or
+    flops per launch over its average event-timed duration; the bound is the resource that work
+    needs longer on at peak."""
+    H, I, k = w.H, w.I, w.k
+    wb = 0.5625 if q4 else 2  # weight bytes per element
+    gu_bytes = int((nonempty + 1) * 2 * I * H * wb) + M * H * 2 + (M * k + M) * I * 2
+    gu_flops = (M * k + M) * 2 * I * H * 2
+    avg = sum(kt["gemm_gateup"]) / len(kt["gemm_gateup"])
+    ach = gu_bytes / (avg * 1e-3) / 1e9
+    ach_tf = gu_flops / (avg * 1e-3) / 1e12
+    mfma_bound = gu_flops / BF16_PEAK_TFLOPS / 1e12 > gu_bytes / HBM_PEAK_GBS / 1e9
+    kname = "k_grouped_gemm<0, q4> (gate/up + SwiGLU)" if q4 else "k_grouped_gemm<0> (gate/up + SwiGLU)"
+    traffic = traffic_for(f"k_grouped_gemm<0,q4>@{w.name}" if q4 else f"k_grouped_gemm<0>@{w.name}")
+    if mfma_bound:
+        return dict(bound="mfma", achieved=round(ach_tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach_tf / BF16_PEAK_TFLOPS, 4), traffic=traffic, kernel=kname,
+                    flops_per_launch=gu_flops, bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
+                    hbm_frac=round(ach / HBM_PEAK_GBS, 4))
+    return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic, kernel=kname,
+                bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
+                mfma_frac=round(ach_tf / BF16_PEAK_TFLOPS, 4))
+
+
 def bench_prefill(args, hip, moe, SD, S, w, q4=False):
     import torch
     if q4:
@@ -410,28 +439,7 @@ def bench_prefill(args, hip, moe, SD, S, w, q4=False):
     wb = 0.5625 if q4 else 2  # weight bytes per element
     layer_bytes = int((nonempty + 1) * w.expert_elems() * wb) + E * H * 2 + 2 * M * H * 2
     flops = M * (2 * H * E + (k + 1) * 3 * 2 * H * I)
-    gu_bytes = int((nonempty + 1) * 2 * I * H * wb) + M * H * 2 + (M * k + M) * I * 2
-    gu_flops = (M * k + M) * 2 * I * H * 2
-    avg = sum(kt["gemm_gateup"]) / len(kt["gemm_gateup"])
-    ach = gu_bytes / (avg * 1e-3) / 1e9
-    ach_tf = gu_flops / (avg * 1e-3) / 1e12
-    # the bound is the resource the kernel's algorithmic work needs longer on at peak
-    mfma_bound = gu_flops / BF16_PEAK_TFLOPS / 1e12 > gu_bytes / HBM_PEAK_GBS / 1e9
-    kname = "k_grouped_gemm<0, q4> (gate/up + SwiGLU)" if q4 else "k_grouped_gemm<0> (gate/up + SwiGLU)"
-    if mfma_bound:
-        roof = dict(bound="mfma", achieved=round(ach_tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach_tf / BF16_PEAK_TFLOPS, 4),
-                    traffic=traffic_for(f"k_grouped_gemm<0,q4>@{w.name}" if q4 else f"k_grouped_gemm<0>@{w.name}"),
-                    kernel=kname,
-                    flops_per_launch=gu_flops, bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
-                    hbm_frac=round(ach / HBM_PEAK_GBS, 4))
-    else:
-        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(ach / HBM_PEAK_GBS, 4),
-                    traffic=traffic_for(f"k_grouped_gemm<0,q4>@{w.name}" if q4 else f"k_grouped_gemm<0>@{w.name}"),
-                    kernel=kname,
-                    bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
-                    mfma_frac=round(ach_tf / BF16_PEAK_TFLOPS, 4))
+    roof = gateup_roofline(kt, w, M, nonempty, q4)
     res = dict(
         value=M / (ms * 1e-3), unit="tok/s", ms_per_step=ms, steps=steps,
         config=dict(workload=f"{w.name}: {w.describe()}, {'4-bit group-affine' if q4 else 'bf16'} experts",
@@ -443,6 +451,63 @@ def bench_prefill(args, hip, moe, SD, S, w, q4=False):
         roofline=roof,
     )
     del x, r, ex, sh, ws
+    return res
+
+
+def bench_long(args, hip, moe, SD, S, w):
+    """Long prefill: w.tokens token rows through one layer as w.chunks calls of w.M rows on
+    consecutive slices of one input, with one workspace sized for a chunk and reused.  One pass =
+    all chunks; reports the sustained rates over whole passes and the spread over chunks."""
+    import torch
+    x, r, ex, sh = SD.layer_tensors(w, x_rows=w.tokens)
+    out = torch.empty_like(x)
+    ws = torch.empty(moe.workspace_size(w.M, w.H, w.E, w.I, w.I_shared, w.k), dtype=torch.uint8, device="cuda")
+    counts = torch.empty(w.chunks, w.E, dtype=torch.int32, device="cuda")
+    M = w.M
+    calls = [LayerCall(moe, x[c * M:(c + 1) * M], r, ex, sh, w.k, out[c * M:(c + 1) * M], ws,
+                       routing={"counts": counts[c]}) for c in range(w.chunks)]
+
+    def one_pass():
+        for call in calls:
+            call()
+
+    one_pass()
+    torch.cuda.synchronize()
+    passes = max(2, args.steps // 50)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(passes):
+        one_pass()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / passes
+    # one more pass with an event between chunks: the per-chunk spread
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(w.chunks + 1)]
+    ev[0].record()
+    for c, call in enumerate(calls):
+        call()
+        ev[c + 1].record()
+    torch.cuda.synchronize()
+    chunk_ms = [ev[c].elapsed_time(ev[c + 1]) for c in range(w.chunks)]
+    kt = kernel_times(hip, moe, lambda s, tr: calls[s % w.chunks](tr), 1, max(args.trace_steps, w.chunks), 7)
+    c = counts.cpu()
+    nonempty = (c > 0).sum(dim=1)
+    H, E, I, k = w.H, w.E, w.I, w.k
+    flops = w.tokens * (2 * H * E + (k + 1) * 3 * 2 * H * I)
+    layer_bytes = sum(int((int(n) + 1) * w.expert_elems() * 2) + E * H * 2 + 2 * M * H * 2 for n in nonempty)
+    res = dict(
+        value=w.tokens / (ms * 1e-3), unit="tok/s", ms_per_pass=ms, passes=passes,
+        config=dict(workload=f"{w.name}: {w.describe()}, bf16 experts, one workspace reused",
+                    nonempty_experts_min=int(nonempty.min()), max_group=int(c.max()),
+                    empty_groups_max=int((c == 0).sum(dim=1).max())),
+        mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        hbm_frac=layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        chunk_us={"mean": round(1000.0 * sum(chunk_ms) / len(chunk_ms), 1),
+                  "min": round(1000.0 * min(chunk_ms), 1), "max": round(1000.0 * max(chunk_ms), 1)},
+        kernels_us={n: round(1000.0 * sum(v) / len(v), 2) for n, v in kt.items()},
+        roofline=gateup_roofline(kt, w, M, int(nonempty.float().mean().round()), False),
+    )
+    del x, out, r, ex, sh, ws
     return res
 
 
@@ -496,6 +561,8 @@ def main():
     torch.cuda.empty_cache()
     pre = bench_prefill(args, hip, moe, SD, S, S.PREFILL)
     skew = bench_prefill(args, hip, moe, SD, S, S.SKEW)
+    long = None if args.no_long else bench_long(args, hip, moe, SD, S, S.LONG)
+    torch.cuda.empty_cache()
     dec_q4 = pre_q4 = small_q4 = None
     if not args.no_q4:
         dq, keep = bench_decode(args, hip, moe, SD, S, q4=True)
@@ -530,6 +597,7 @@ def main():
                          "kernels_us": dec["kernels_us"]},
         "prefill": pre,
         "prefill_skew": skew,
+        "prefill_long": long,
         "decode_q4": dec_q4,
         "prefill_q4": pre_q4,
         "small_batch": {"config": {"workload": f"M token rows x {args.layers} decode layers (same weights), "

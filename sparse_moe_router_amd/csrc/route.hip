@@ -44,32 +44,30 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   // this tile's (chunk, expert) bitmask words start empty; top-k sets their bits
   if (cmask && tid < 64 && e0 + tid < E) cmask[(int64_t)blockIdx.x * E + e0 + tid] = 0ull;
 
-  // loader: 512 16-byte chunks per operand per step, two per thread
+  // loader: 512 16-byte chunks per operand per step, two per thread.  Rows
+  // past M (tokens) or E (experts) re-read row 0: they only reach output
+  // rows / columns that are never stored, so the loaded registers go to LDS
+  // untouched (a select on them would make every step wait for all loads).
   const u32x4_t* srcA[2];
   const u32x4_t* srcB[2];
-  bool okA[2], okB[2];
   int dst[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int c = tid + 256 * i, row = c >> 3, q = c & 7;
     const int64_t t = t0 + row;
     const int e = e0 + row;
-    okA[i] = t < M;
-    okB[i] = e < E;
-    srcA[i] = (const u32x4_t*)(x + (okA[i] ? t : 0) * (int64_t)H) + q;
-    srcB[i] = (const u32x4_t*)(wr + (int64_t)(okB[i] ? e : 0) * H) + q;
+    srcA[i] = (const u32x4_t*)(x + (t < M ? t : 0) * (int64_t)H) + q;
+    srcB[i] = (const u32x4_t*)(wr + (int64_t)(e < E ? e : 0) * H) + q;
     dst[i] = row * 8 + (q ^ (row & 7));
   }
   const int nsteps = H / 64;
-  const u32x4_t zero = {0, 0, 0, 0};
   u32x4_t ra[RD][2], rb[RD][2];
   auto gload = [&](u32x4_t (&a)[2], u32x4_t (&b)[2], int st) {
     const int c0 = (st < nsteps ? st : nsteps - 1) * 8;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const u32x4_t va = srcA[i][c0], vb = srcB[i][c0];
-      a[i] = okA[i] ? va : zero;
-      b[i] = okB[i] ? vb : zero;
+      a[i] = srcA[i][c0];
+      b[i] = srcB[i][c0];
     }
   };
   auto lstore = [&](const u32x4_t (&a)[2], const u32x4_t (&b)[2], int buf) {
@@ -92,14 +90,18 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
       const int s = s0 + u;
       const int buf = u & 1;
       if (s < nsteps) {
+        u32x4_t a[4], b[4];  // all operand reads of the step first, then the MFMAs
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int q = 2 * kk + half;
-          const u32x4_t a = sA[buf][arow * 8 + (q ^ (arow & 7))];
-          const u32x4_t b = sB[buf][brow * 8 + (q ^ (brow & 7))];
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                         __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+          a[kk] = sA[buf][arow * 8 + (q ^ (arow & 7))];
+          b[kk] = sB[buf][brow * 8 + (q ^ (brow & 7))];
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[kk]),
+                                                         __builtin_bit_cast(bf16x8_t, b[kk]), acc, 0, 0, 0);
       }
       gload(ra[u], rb[u], s + RD);
       lstore(ra[(u + 1) % RD], rb[(u + 1) % RD], buf ^ 1);
