@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-q4", action="store_true", help="skip the 4-bit expert-weight runs")
     ap.add_argument("--no-long", action="store_true", help="skip the chunked long-prefill run")
+    ap.add_argument("--layout", choices=("tiled", "row"), default="tiled",
+                    help="bf16 expert weights: tiled once by moe_tile_weights before timing (default), or "
+                         "row-major as generated")
     ap.add_argument("--layers", type=int, default=40, help=argparse.SUPPRESS)
     ap.add_argument("--trace-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -159,6 +162,17 @@ class LayerCall:
             raise RuntimeError(f"moe_layer_forward failed with status {st}")
 
 
+def layout_flag(args, moe, q4):
+    """MOE_FLAG_TILED_WEIGHTS when the bf16 expert weights were tiled (4-bit weights stay as they are)."""
+    return moe.FLAG_TILED_WEIGHTS if args.layout == "tiled" and not q4 else 0
+
+
+def layout_name(args, q4):
+    if q4:
+        return "4-bit codes + scale/bias words, row-major"
+    return "tiled (moe_tile_weights, once before timing)" if args.layout == "tiled" else "row-major"
+
+
 def kernel_times(hip, moe, calls_fn, n_calls_per_step, steps, kernels_per_call):
     """Run `steps` eager steps with per-kernel events; returns {kernel name: [ms per launch]}."""
     import torch
@@ -225,6 +239,8 @@ def bench_decode(args, hip, moe, SD, S, q4=False):
                 SD.fill(ex[e], S.expert_key(w, l, e), 0, w.w_sigma)
             sh = torch.empty(w.shared_elems(), dtype=torch.bfloat16, device=dev)
             SD.fill(sh, S.shared_key(w, l), 0, w.w_sigma)
+            if args.layout == "tiled":
+                ex, sh = moe.tile_weights(ex, H, I), moe.tile_weights(sh, H, w.I_shared)
         layers.append((r, ex, sh))
     out = torch.empty(L, H, dtype=torch.bfloat16, device=dev)
     wsn = moe.workspace_size(1, H, E, I, w.I_shared, k)
@@ -233,7 +249,8 @@ def bench_decode(args, hip, moe, SD, S, q4=False):
     gen_s = time.time() - t0
 
     xs = [xpool[i:i + 1] for i in range(w.x_pool)]
-    calls = [[LayerCall(moe, xs[i], r, ex, sh, k, out[l:l + 1], ws) for l, (r, ex, sh) in enumerate(layers)]
+    lay = layout_flag(args, moe, q4)
+    calls = [[LayerCall(moe, xs[i], r, ex, sh, k, out[l:l + 1], ws, flags=lay) for l, (r, ex, sh) in enumerate(layers)]
              for i in range(w.x_pool)]
 
     # eager reference for row 0, then one captured graph per pool row
@@ -315,7 +332,8 @@ def bench_small(args, hip, moe, S, layers, xpool, Ms=(2, 4, 8, 16, 32, 64)):
             out = torch.empty(L, M, H, dtype=torch.bfloat16, device="cuda")
             ids = torch.empty(L, M, k, dtype=torch.int32, device="cuda")
             ws = torch.empty(moe.workspace_size(M, H, E, I, Is, k, flags=flags), dtype=torch.uint8, device="cuda")
-            calls = [LayerCall(moe, x, r, ex, sh, k, out[l], ws, routing={"topk_ids": ids[l]}, flags=flags)
+            calls = [LayerCall(moe, x, r, ex, sh, k, out[l], ws, routing={"topk_ids": ids[l]},
+                               flags=flags | layout_flag(args, moe, q4))
                      for l, (r, ex, sh) in enumerate(layers)]
             for c in calls:
                 c()
@@ -414,13 +432,16 @@ def bench_prefill(args, hip, moe, SD, S, w, q4=False):
         ex, sh = (ec, esb), (sc, ssb)
     else:
         x, r, ex, sh = SD.layer_tensors(w)
+        if args.layout == "tiled":
+            ex, sh = moe.tile_weights(ex, w.H, w.I), moe.tile_weights(sh, w.H, w.I_shared)
     bias = None
     if w.zipf_s:
         bias = torch.from_numpy(S.zipf_router_bias(w)).cuda()
     out = torch.empty_like(x)
     ws = torch.empty(moe.workspace_size(w.M, w.H, w.E, w.I, w.I_shared, w.k), dtype=torch.uint8, device="cuda")
     counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
-    call = LayerCall(moe, x, r, ex, sh, w.k, out, ws, bias=bias, routing={"counts": counts})
+    call = LayerCall(moe, x, r, ex, sh, w.k, out, ws, bias=bias, routing={"counts": counts},
+                     flags=layout_flag(args, moe, q4))
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -443,6 +464,7 @@ def bench_prefill(args, hip, moe, SD, S, w, q4=False):
     res = dict(
         value=M / (ms * 1e-3), unit="tok/s", ms_per_step=ms, steps=steps,
         config=dict(workload=f"{w.name}: {w.describe()}, {'4-bit group-affine' if q4 else 'bf16'} experts",
+                    weights_layout=layout_name(args, q4),
                     nonempty_experts=nonempty,
                     max_group=int(c.max()), empty_groups=int((c == 0).sum())),
         hbm_frac=layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -460,12 +482,14 @@ def bench_long(args, hip, moe, SD, S, w):
     all chunks; reports the sustained rates over whole passes and the spread over chunks."""
     import torch
     x, r, ex, sh = SD.layer_tensors(w, x_rows=w.tokens)
+    if args.layout == "tiled":
+        ex, sh = moe.tile_weights(ex, w.H, w.I), moe.tile_weights(sh, w.H, w.I_shared)
     out = torch.empty_like(x)
     ws = torch.empty(moe.workspace_size(w.M, w.H, w.E, w.I, w.I_shared, w.k), dtype=torch.uint8, device="cuda")
     counts = torch.empty(w.chunks, w.E, dtype=torch.int32, device="cuda")
     M = w.M
     calls = [LayerCall(moe, x[c * M:(c + 1) * M], r, ex, sh, w.k, out[c * M:(c + 1) * M], ws,
-                       routing={"counts": counts[c]}) for c in range(w.chunks)]
+                       routing={"counts": counts[c]}, flags=layout_flag(args, moe, False)) for c in range(w.chunks)]
 
     def one_pass():
         for call in calls:
@@ -498,6 +522,7 @@ def bench_long(args, hip, moe, SD, S, w):
     res = dict(
         value=w.tokens / (ms * 1e-3), unit="tok/s", ms_per_pass=ms, passes=passes,
         config=dict(workload=f"{w.name}: {w.describe()}, bf16 experts, one workspace reused",
+                    weights_layout=layout_name(args, False),
                     nonempty_experts_min=int(nonempty.min()), max_group=int(c.max()),
                     empty_groups_max=int((c == 0).sum(dim=1).max())),
         mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
@@ -590,7 +615,8 @@ def main():
         "config": {"workload": f"decode batch-1: 1 token row x {args.layers} MoE layers, "
                                f"H={w.H} E={w.E} top-{w.k} + 1 shared, I={w.I}, bf16 weights "
                                f"({args.layers * (w.E + 1) * w.expert_elems() * 2 / 1e9:.1f} GB), "
-                               f"HIP-graph replay", "layers": args.layers},
+                               f"HIP-graph replay", "layers": args.layers,
+                   "weights_layout": layout_name(args, False)},
         "roofline": dec["roofline"],
         "cpu_baseline": cpu_d,
         "decode_layer": {"us_per_layer": round(dec["layer_us"], 3), "hbm_frac": round(dec["layer_hbm_frac"], 4),

@@ -90,6 +90,11 @@ typedef enum {
  * counts / offsets / perm. */
 #define MOE_FLAG_FORCE_GEMV 0x1u /* matrix-vector paths; requires M <= 64 */
 #define MOE_FLAG_FORCE_GEMM 0x2u /* grouped (matrix-matrix) path, also at M == 1 */
+/* expert_w and shared_w are in the tiled layout written by moe_tile_weights
+ * (bf16 weights only: moe_layer_forward_q4 rejects it with
+ * MOE_ERR_INVALID_ARG).  Every path reads it; results are bit-identical to
+ * the row-major layout's. */
+#define MOE_FLAG_TILED_WEIGHTS 0x4u
 
 typedef struct {
   int64_t M;                /* token rows in this call */
@@ -202,6 +207,29 @@ moe_status_t moe_layer_forward_q4(const moe_desc_t* d, const void* x, const void
                                   const moe_q4_t* experts, const moe_q4_t* shared, int top_k, void* out,
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   const moe_routing_t* routing, moe_trace_t* trace);
+
+/* Rewrites nblocks bf16 expert blocks (each 3*H*I elements in the row-major
+ * packing above: gate [I][H], up [I][H], down [H][I]) from src into the tiled
+ * layout at dst, the order in which the grouped GEMM streams its weight tiles
+ * ("Optimizing on-device inference for Apple Silicon", section "Dequantize
+ * weights during matrix multiplication": one small weight tile at a time is
+ * staged on chip), so that each tile's K-step is one contiguous block.
+ * Layout of a block (3*H*I elements, as before):
+ *   gate/up part, elements [0, 2*I*H): panel p = 0 .. ceil(I/128)-1 starts at
+ *     256*p*H and holds n = min(128, I - 128p) gate rows and the n up rows of
+ *     the same indices as 2n tile rows, gate (m = 0) or up (m = 1) row
+ *     128p + 32c + l (0 <= l < 32) being tile row 64c + 32m + l;
+ *   down part, elements [2*I*H, 3*I*H): panel p = 0 .. ceil(H/256)-1 starts
+ *     at 2*I*H + 256*p*I and holds the n = min(256, H - 256p) down rows
+ *     256p .. 256p+n-1 as tile rows 0 .. n-1;
+ *   a panel is its K/64 steps (K = H for gate/up, I for down) one after
+ *     another; a step is its tile rows in order, 64 elements each (the row's
+ *     elements 64s .. 64s+63), the 8-element chunk q of tile row R stored at
+ *     chunk position q ^ (R % 8).
+ * For the shared expert call with nblocks = 1 and I = I_shared.  src and dst
+ * are device pointers, 16-byte aligned, not overlapping; H and I follow the
+ * layer's shape rules.  Asynchronous on `stream` like the layer calls. */
+moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void* src, void* dst, void* stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t s);

@@ -32,10 +32,10 @@ namespace {
 constexpr int DB = 4;  // 16-byte chunks per lane per batch: 4 x 64 lanes x 8 = 2048 elements
 
 // dot(x[0:n], w[0:n]) and dot(x, w2) for one wave (n % 8 == 0), fp32 in all
-// lanes; w, w2 point at the rows' first element.
+// lanes; w, w2 are weight rows of format W.
 template <bool TWO, class W>
-__device__ __forceinline__ void wave_dots(const uint16_t* __restrict__ x, const W w, const W w2, int n, int lane,
-                                          float* d1, float* d2) {
+__device__ __forceinline__ void wave_dots(const uint16_t* __restrict__ x, const typename W::Row w,
+                                          const typename W::Row w2, int n, int lane, float* d1, float* d2) {
   float a1 = 0.0f, a2 = 0.0f;
   for (int base = 0; base < n; base += DB * 512) {
     u32x4_t xa[DB];
@@ -68,8 +68,8 @@ __global__ __launch_bounds__(256) void k_dec_router(const uint16_t* __restrict__
   const int e = blockIdx.x * 4 + wave;
   if (e >= E) return;
   float v, unused;
-  const WBf16 row{wr + (int64_t)e * H};
-  wave_dots<false>(x, row, row, H, lane, &v, &unused);
+  const WBf16::Row row{wr + (int64_t)e * H};
+  wave_dots<false, WBf16>(x, row, row, H, lane, &v, &unused);
   if (lane == 0) logits[e] = v + (bias ? bias[e] : 0.0f);
 }
 
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
     const int i = blockIdx.x * 4 + wave;
     if (i >= Is) return;
     float g, u;
-    wave_dots<true>(x, shared_w.at((int64_t)i * H), shared_w.at(((int64_t)Is + i) * H), H, lane, &g, &u);
+    wave_dots<true, W>(x, shared_w.gu(0, i, H, Is), shared_w.gu(1, i, H, Is), H, lane, &g, &u);
     if (lane == 0) h_s[i] = silu(g) * u;
     return;
   }
@@ -123,9 +123,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
   const int j = b / rblocks;
   const int i = (b % rblocks) * 4 + wave;
   if (j >= k || i >= I) return;
-  const W ew = expert_w.at((int64_t)s_ids[j] * 3 * I * H);
+  const W ew = expert_w.block((int64_t)s_ids[j] * 3 * I * H);
   float g, u;
-  wave_dots<true>(x, ew.at((int64_t)i * H), ew.at(((int64_t)I + i) * H), H, lane, &g, &u);
+  wave_dots<true, W>(x, ew.gu(0, i, H, I), ew.gu(1, i, H, I), H, lane, &g, &u);
   if (lane == 0) h_r[(int64_t)j * I + i] = silu(g) * u;
 }
 
@@ -154,10 +154,10 @@ __global__ __launch_bounds__(1024) void k_dec_down(const W expert_w, const W sha
     const float* hj;
     float wj = 1.0f;
     if (sh) {
-      wd = shared_w.at((int64_t)2 * Is * H);
+      wd = shared_w;
       hj = h_s;
     } else {
-      wd = expert_w.at((int64_t)ids[j] * 3 * I * H + (int64_t)2 * I * H);
+      wd = expert_w.block((int64_t)ids[j] * 3 * I * H);
       hj = h_r + (int64_t)j * I;
       wj = wts[j];
     }
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(1024) void k_dec_down(const W expert_w, const W sha
 #pragma unroll
       for (int r = 0; r < DR; ++r) {
         const int c = c0 + r < H ? c0 + r : H - 1;
-        b[r] = wd.load((int64_t)c * n + qq);
+        b[r] = wd.dn(c, H, n).load(qq);
       }
       const f32x4_t h0 = *(const f32x4_t*)(hj + qq);
       const f32x4_t h1 = *(const f32x4_t*)(hj + qq + 4);
@@ -235,13 +235,17 @@ hipError_t decode_down(const W ew, const W sw, const int32_t* ids, const float* 
 hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
                                 const float* logits, int32_t* ids, float* w, float* h_dec, const Plan& p,
                                 const Launch& lc) {
-  return decode_gateup(x, WBf16{expert_w}, WBf16{p.shared ? shared_w : nullptr}, logits, ids, w, h_dec, p, lc);
+  const uint16_t* sw = p.shared ? shared_w : nullptr;
+  if (p.tiled) return decode_gateup(x, WBf16T{expert_w}, WBf16T{sw}, logits, ids, w, h_dec, p, lc);
+  return decode_gateup(x, WBf16{expert_w}, WBf16{sw}, logits, ids, w, h_dec, p, lc);
 }
 
 hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w, const int32_t* ids,
                               const float* w, const float* h_dec, uint16_t* out, const Plan& p,
                               const Launch& lc) {
-  return decode_down(WBf16{expert_w}, WBf16{p.shared ? shared_w : nullptr}, ids, w, h_dec, out, p, lc);
+  const uint16_t* sw = p.shared ? shared_w : nullptr;
+  if (p.tiled) return decode_down(WBf16T{expert_w}, WBf16T{sw}, ids, w, h_dec, out, p, lc);
+  return decode_down(WBf16{expert_w}, WBf16{sw}, ids, w, h_dec, out, p, lc);
 }
 
 hipError_t launch_decode_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh,

@@ -60,6 +60,7 @@ struct GemmArgs {
   int H, E, I, Is, k;
   int npan;
   int max_tiles;
+  int tiled;  // bf16 weights in the tiled layout: a panel's K-step is one block (the stage image)
 };
 
 constexpr int BK = 64;        // K per pipeline step
@@ -185,6 +186,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   const char* gsrc = nullptr;  // 4-bit group words
   uint32_t woff[4];            // byte offsets within the expert block
   uint32_t goff = 0;
+  int wstep = 128;             // bytes from one weight step to the next
   if (Q4) {
     const int64_t eb = is_shared ? 0 : (int64_t)tl.g * 3 * p.I * p.H;  // expert block, elements
     wsrc = (const char*)(is_shared ? p.sh_codes : p.ex_codes) + eb / 2;
@@ -197,9 +199,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   } else {
     const uint16_t* W = is_shared ? p.shared_w : p.expert_w + (int64_t)tl.g * 3 * p.I * p.H;
     wsrc = (const char*)W;
-    // transfer i: rows 8i + lane/8 of col block rg, chunk lq
+    if (p.tiled) {
+      // tiled layout: step s of this panel is one block of trows tile rows
+      // x 128 bytes, already in stage order and swizzled, so transfer i
+      // copies the 1 KB of stage rows 8 (8 cg + 4 rg + i) .. +8 verbatim
+      // (rows past a partial panel re-read the first 1 KB: never stored)
+      const int n = MODE == 0 ? (Ig - panel * (NWR / 2) < NWR / 2 ? Ig - panel * (NWR / 2) : NWR / 2)
+                              : (p.H - panel * NWR < NWR ? p.H - panel * NWR : NWR);
+      const int trows = MODE == 0 ? 2 * n : n;
+      wstep = trows * 128;
+      const int64_t pbase = MODE == 0 ? (int64_t)NWR * panel * p.H : (int64_t)2 * Ig * p.H + (int64_t)NWR * panel * Ig;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) woff[i] = (uint32_t)((wrow_elem(rg, 8 * i + lr) + 8 * lq) * 2);
+      for (int i = 0; i < 4; ++i) {
+        const int blk = cg * 8 + rg * 4 + i;
+        woff[i] = (uint32_t)(pbase * 2 + (8 * blk < trows ? blk : 0) * 1024 + lane * 16);
+      }
+    } else {
+      // transfer i: rows 8i + lane/8 of col block rg, chunk lq
+#pragma unroll
+      for (int i = 0; i < 4; ++i) woff[i] = (uint32_t)((wrow_elem(rg, 8 * i + lr) + 8 * lq) * 2);
+    }
   }
 
   // ---- activation rows this wave moves: rows (wave*NRH + i)*8 + lane/8, chunk lq
@@ -228,7 +247,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
       if (rg == 0) dma4(gsrc + goff + (int64_t)s * 4, (uint32_t*)(st + 2 * NWR) + cg * 64);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(wsrc + woff[i] + (int64_t)s * 128, st + (cg * 8 + rg * 4 + i) * 64);
+      for (int i = 0; i < 4; ++i) dma16(wsrc + woff[i] + (int64_t)s * wstep, st + (cg * 8 + rg * 4 + i) * 64);
     }
   };
 
@@ -486,6 +505,7 @@ hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const
   const int maxI = pl.I > pl.Is ? pl.I : pl.Is;
   a.npan = (maxI + NWR / 2 - 1) / (NWR / 2);
   a.max_tiles = (int)pl.max_tiles;
+  a.tiled = pl.tiled ? 1 : 0;
   return launch(lc, k_grouped_gemm<0, false>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 
@@ -509,6 +529,7 @@ hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint
   a.k = pl.k;
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
+  a.tiled = pl.tiled ? 1 : 0;
   return launch(lc, k_grouped_gemm<1, false>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 

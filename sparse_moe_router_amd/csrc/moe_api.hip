@@ -100,7 +100,7 @@ namespace {
 moe_status_t check_desc(const moe_desc_t* d, int top_k, bool* gemv) {
   if (!d) return MOE_ERR_INVALID_ARG;
   if (d->M < 0) return MOE_ERR_INVALID_ARG;
-  const uint32_t known = MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GEMM;
+  const uint32_t known = MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GEMM | MOE_FLAG_TILED_WEIGHTS;
   if (d->flags & ~known) return MOE_ERR_INVALID_ARG;
   if ((d->flags & MOE_FLAG_FORCE_GEMV) && (d->flags & MOE_FLAG_FORCE_GEMM)) return MOE_ERR_INVALID_ARG;
   if (d->H < 64 || d->H > 16384 || d->H % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
@@ -223,6 +223,7 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   if (st != MOE_OK) return st;
   if (!x || !router_w || !out) return MOE_ERR_INVALID_ARG;
   if (wt.q4) {
+    if (d->flags & MOE_FLAG_TILED_WEIGHTS) return MOE_ERR_INVALID_ARG;  // bf16 weights only
     if (!wt.eq.codes || !wt.eq.groups) return MOE_ERR_INVALID_ARG;
     const bool has_sh = wt.sq.codes || wt.sq.groups;
     if ((d->I_shared > 0) != has_sh || (has_sh && (!wt.sq.codes || !wt.sq.groups))) return MOE_ERR_INVALID_ARG;
@@ -241,6 +242,7 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   if (d->M == 0) return MOE_OK;
   Plan p;
   if (!make_plan(&p, d->M, d->H, d->E, d->I, d->I_shared, top_k, gemv)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  p.tiled = (d->flags & MOE_FLAG_TILED_WEIGHTS) != 0;
   if (!workspace) return MOE_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return MOE_ERR_MISALIGNED;
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -406,6 +408,18 @@ moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w,
   }
   Tracer none{nullptr, s};
   return run_routing_grouped(p, d, x, router_w, workspace, routing, s, none);
+}
+
+moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void* src, void* dst, void* stream) {
+  if (nblocks < 0 || !src || !dst) return MOE_ERR_INVALID_ARG;
+  if (H < 64 || H > 16384 || H % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (I < 64 || I > 16384 || I % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_MISALIGNED;
+  const size_t bytes = (size_t)nblocks * 3 * I * H * 2;
+  if (overlap(src, bytes, dst, bytes)) return MOE_ERR_INVALID_ARG;
+  if (nblocks == 0) return MOE_OK;
+  const hipError_t e = launch_tile_weights((const uint16_t*)src, (uint16_t*)dst, nblocks, H, I, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
 const char* moe_status_string(moe_status_t s) {

@@ -59,6 +59,7 @@ struct Plan {
   int32_t H, E, I, Is, k;
   bool shared;
   bool gemv;  // decode path
+  bool tiled;  // bf16 expert weights in the tiled layout (WBf16T)
   int64_t A;  // assignments M*k
   int64_t nchunk;
   int64_t max_tiles;
@@ -182,5 +183,9 @@ hipError_t launch_small_gateup_q4(const uint16_t* x, const Q4Weights& ex, const 
                                   float* h, const Plan& p, const Launch& lc);
 hipError_t launch_small_down_q4(const Q4Weights& ex, const Q4Weights& sh, const float* w, const SmallUnion& un,
                                 const float* h, uint16_t* out, const Plan& p, const Launch& lc);
+
+// nblocks bf16 expert blocks (hidden H, intermediate I) from the row-major
+// packing to the tiled layout read with MOE_FLAG_TILED_WEIGHTS.
+hipError_t launch_tile_weights(const uint16_t* src, uint16_t* dst, int64_t nblocks, int H, int I, hipStream_t s);
 
 }  // namespace moe

@@ -41,7 +41,8 @@ constexpr int DRS = 4;  // output rows per down-projection workgroup
 // weight chunk is loaded once per batch and applied to all np rows; the
 // caller points xs[p] for p >= np at a valid row (its results are unused).
 template <bool TWO, class W>
-__device__ __forceinline__ void wave_dots_rows(const uint16_t* const (&xs)[NP], int np, const W w, const W w2,
+__device__ __forceinline__ void wave_dots_rows(const uint16_t* const (&xs)[NP], int np, const typename W::Row w,
+                                               const typename W::Row w2,
                                                int n, int lane, float (&d1)[NP], float (&d2)[NP]) {
   float a1[NP], a2[NP];
 #pragma unroll
@@ -99,14 +100,14 @@ __global__ __launch_bounds__(256) void k_sm_router(const uint16_t* __restrict__ 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.x * 4 + wave;
   if (e >= E) return;
-  const WBf16 row{wr + (int64_t)e * H};
+  const WBf16::Row row{wr + (int64_t)e * H};
   const int t0 = blockIdx.y * NP;
   const int np = M - t0 < NP ? M - t0 : NP;
   const uint16_t* xs[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) xs[p] = x + (int64_t)(t0 + (p < np ? p : 0)) * H;
   float d[NP], unused[NP];
-  wave_dots_rows<false>(xs, np, row, row, H, lane, d, unused);
+  wave_dots_rows<false, WBf16>(xs, np, row, row, H, lane, d, unused);
   if (lane == 0) {
     const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
@@ -211,12 +212,12 @@ __global__ __launch_bounds__(256) void k_sm_gateup(const uint16_t* __restrict__ 
   if ((int)blockIdx.x < nsb) {
     const int i = blockIdx.x * 4 + wave;
     if (i >= Is) return;
-    const W g = shared_w.at((int64_t)i * H), u = shared_w.at(((int64_t)Is + i) * H);
+    const typename W::Row g = shared_w.gu(0, i, H, Is), u = shared_w.gu(1, i, H, Is);
     for (int t0 = 0; t0 < M; t0 += NP) {
       const int np = M - t0 < NP ? M - t0 : NP;
 #pragma unroll
       for (int p = 0; p < NP; ++p) xs[p] = x + (int64_t)(t0 + (p < np ? p : 0)) * H;
-      wave_dots_rows<true>(xs, np, g, u, H, lane, dg, du);
+      wave_dots_rows<true, W>(xs, np, g, u, H, lane, dg, du);
       if (lane == 0) {
 #pragma unroll
         for (int p = 0; p < NP; ++p)
@@ -229,8 +230,8 @@ __global__ __launch_bounds__(256) void k_sm_gateup(const uint16_t* __restrict__ 
   const int b = blockIdx.x - nsb;
   const int ui = b / rblocks, i = (b - ui * rblocks) * 4 + wave;
   if (ui >= un[0] || i >= I) return;
-  const W we = expert_w.at((int64_t)uexp[ui] * 3 * I * H);
-  const W g = we.at((int64_t)i * H), u = we.at(((int64_t)I + i) * H);
+  const W we = expert_w.block((int64_t)uexp[ui] * 3 * I * H);
+  const typename W::Row g = we.gu(0, i, H, I), u = we.gu(1, i, H, I);
   const int a0 = uoff[ui], a1 = uoff[ui + 1];
   for (int q0 = a0; q0 < a1; q0 += NP) {
     const int np = a1 - q0 < NP ? a1 - q0 : NP;
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(256) void k_sm_gateup(const uint16_t* __restrict__ 
       as[p] = upair[q0 + (p < np ? p : 0)];
       xs[p] = x + (int64_t)(as[p] / k) * H;
     }
-    wave_dots_rows<true>(xs, np, g, u, H, lane, dg, du);
+    wave_dots_rows<true, W>(xs, np, g, u, H, lane, dg, du);
     if (lane == 0) {
 #pragma unroll
       for (int p = 0; p < NP; ++p)
@@ -279,11 +280,11 @@ __global__ __launch_bounds__(1024) void k_sm_down(const W expert_w, const W shar
     W wd;
     if (sh) {
       n = Is;
-      wd = shared_w.at((int64_t)2 * Is * H);
+      wd = shared_w;
       q1 = M;
     } else {
       n = I;
-      wd = expert_w.at((int64_t)uexp[item - 1] * 3 * I * H + (int64_t)2 * I * H);
+      wd = expert_w.block((int64_t)uexp[item - 1] * 3 * I * H);
       q1 = uoff[item];
     }
     const int np = q1 - q0 < NP ? q1 - q0 : NP;
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(1024) void k_sm_down(const W expert_w, const W shar
 #pragma unroll
       for (int r = 0; r < DRS; ++r) {
         const int c = c0 + r < H ? c0 + r : H - 1;
-        b[r] = wd.load((int64_t)c * n + qq);
+        b[r] = wd.dn(c, H, n).load(qq);
       }
       f32x4_t h0[NP], h1[NP];
 #pragma unroll
@@ -402,12 +403,16 @@ hipError_t launch_small_topk(const float* logits, int32_t* ids, float* w, const 
 
 hipError_t launch_small_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
                                const SmallUnion& un, float* h, const Plan& p, const Launch& lc) {
-  return small_gateup(x, WBf16{expert_w}, WBf16{p.shared ? shared_w : nullptr}, un, h, p, lc);
+  const uint16_t* sw = p.shared ? shared_w : nullptr;
+  if (p.tiled) return small_gateup(x, WBf16T{expert_w}, WBf16T{sw}, un, h, p, lc);
+  return small_gateup(x, WBf16{expert_w}, WBf16{sw}, un, h, p, lc);
 }
 
 hipError_t launch_small_down(const uint16_t* expert_w, const uint16_t* shared_w, const float* w,
                              const SmallUnion& un, const float* h, uint16_t* out, const Plan& p, const Launch& lc) {
-  return small_down(WBf16{expert_w}, WBf16{p.shared ? shared_w : nullptr}, w, un, h, out, p, lc);
+  const uint16_t* sw = p.shared ? shared_w : nullptr;
+  if (p.tiled) return small_down(WBf16T{expert_w}, WBf16T{sw}, w, un, h, out, p, lc);
+  return small_down(WBf16{expert_w}, WBf16{sw}, w, un, h, out, p, lc);
 }
 
 hipError_t launch_small_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const SmallUnion& un,

@@ -1,11 +1,23 @@
 // Expert weight formats read by the decode (matrix-vector) kernels.
 //
-// Both address an expert block by element index: expert e's block holds
-// gate [I][H], up [I][H], down [H][I] (rows along the reduction dimension),
-// and element offsets of rows and 8-element chunks are multiples of 8 (of
-// 64 for row starts).
+// An expert block holds gate [I][H], up [I][H], down [H][I] (rows along the
+// reduction dimension).  block(e) is the block at element offset e; gu(m, i)
+// is row i of gate (m = 0) or up (m = 1), dn(c) row c of down; a row's
+// load(k) returns its 8-element chunk k .. k+7 (k % 8 == 0).
 //
-//  - WBf16: one bf16 per element.
+//  - WBf16: one bf16 per element, rows stored one after another.
+//  - WBf16T: the same bf16 weights in the tiled layout the grouped GEMM
+//    streams (each K-step of a weight tile one contiguous block): in the
+//    gate/up part, panel p holds gate and up rows [128p, 128p + n) (n =
+//    min(128, I - 128p)) as 2n tile rows, gate/up row 128p + 32c + l at tile
+//    row 64c + 32m + l; in the down part, panel p holds rows [256p, 256p + n)
+//    (n = min(256, H - 256p)) as tile rows 0 .. n-1.  A panel stores its
+//    K-steps of 64 one after another, each as its tile rows of 64 elements,
+//    whose eight 8-element chunks sit XOR-swizzled (chunk q of tile row R at
+//    position q ^ (R % 8)).  A row's chunk is found at
+//    panel + step * (tile rows * 64) + R * 64 + 8 * (q ^ (R % 8)); the eight
+//    chunks of a step stay inside one 128-byte line, so loads that cover a
+//    row's 64 elements stay coalesced.
 //  - WQ4: the 4-bit group-affine format of "Optimizing on-device inference
 //    for Apple Silicon", section "Dequantize weights during matrix
 //    multiplication": each weight is an unsigned 4-bit code q, and each group
@@ -22,8 +34,13 @@ namespace moe {
 struct WBf16 {
   const uint16_t* p;
   typedef u32x4_t chunk_t;  // 8 elements
-  __device__ __forceinline__ WBf16 at(int64_t e) const { return {p + e}; }
-  __device__ __forceinline__ chunk_t load(int64_t e) const { return *(const u32x4_t*)(p + e); }
+  struct Row {
+    const uint16_t* p;
+    __device__ __forceinline__ chunk_t load(int64_t k) const { return *(const u32x4_t*)(p + k); }
+  };
+  __device__ __forceinline__ WBf16 block(int64_t e) const { return {p + e}; }
+  __device__ __forceinline__ Row gu(int m, int i, int H, int I) const { return {p + ((int64_t)m * I + i) * H}; }
+  __device__ __forceinline__ Row dn(int c, int H, int I) const { return {p + (int64_t)2 * I * H + (int64_t)c * I}; }
   // sum_i w_i x_i over the 8 elements, x as 8 bf16
   __device__ __forceinline__ static float dot(const chunk_t& w, const u32x4_t& x) {
     float a = 0.0f;
@@ -38,14 +55,50 @@ struct WBf16 {
   }
 };
 
+struct WBf16T {
+  const uint16_t* p;
+  typedef u32x4_t chunk_t;
+  struct Row {
+    const uint16_t* p;  // tile row R of the row's first K-step
+    int step;           // elements per K-step of its panel
+    int swz;            // R % 8
+    __device__ __forceinline__ chunk_t load(int64_t k) const {
+      return *(const u32x4_t*)(p + (k >> 6) * step + 8 * (((int)(k >> 3) & 7) ^ swz));
+    }
+  };
+  __device__ __forceinline__ WBf16T block(int64_t e) const { return {p + e}; }
+  __device__ __forceinline__ Row gu(int m, int i, int H, int I) const {
+    const int pn = i >> 7, j = i & 127, n = I - 128 * pn < 128 ? I - 128 * pn : 128;
+    const int R = 64 * (j >> 5) + 32 * m + (j & 31);
+    return {p + (int64_t)256 * pn * H + 64 * R, 128 * n, R & 7};
+  }
+  __device__ __forceinline__ Row dn(int c, int H, int I) const {
+    const int pn = c >> 8, R = c & 255, n = H - 256 * pn < 256 ? H - 256 * pn : 256;
+    return {p + (int64_t)2 * I * H + (int64_t)256 * pn * I + 64 * R, 64 * n, R & 7};
+  }
+  __device__ __forceinline__ static float dot(const chunk_t& w, const u32x4_t& x) { return WBf16::dot(w, x); }
+  __device__ __forceinline__ static float dot(const chunk_t& w, const f32x4_t& x0, const f32x4_t& x1) {
+    return WBf16::dot(w, x0, x1);
+  }
+};
+
 struct WQ4 {
   const uint32_t* c;  // codes, 8 per word
   const uint32_t* g;  // (scale, bias) per 64 elements
   struct chunk_t {
     uint32_t c, g;
   };
-  __device__ __forceinline__ WQ4 at(int64_t e) const { return {c + (e >> 3), g + (e >> 6)}; }
-  __device__ __forceinline__ chunk_t load(int64_t e) const { return {c[e >> 3], g[e >> 6]}; }
+  struct Row {
+    const uint32_t* c;
+    const uint32_t* g;
+    __device__ __forceinline__ chunk_t load(int64_t k) const { return {c[k >> 3], g[k >> 6]}; }
+  };
+  __device__ __forceinline__ WQ4 block(int64_t e) const { return {c + (e >> 3), g + (e >> 6)}; }
+  __device__ __forceinline__ Row at_elem(int64_t e) const { return {c + (e >> 3), g + (e >> 6)}; }
+  __device__ __forceinline__ Row gu(int m, int i, int H, int I) const { return at_elem(((int64_t)m * I + i) * H); }
+  __device__ __forceinline__ Row dn(int c, int H, int I) const {
+    return at_elem((int64_t)2 * I * H + (int64_t)c * I);
+  }
   __device__ __forceinline__ static float code(uint32_t c, int j) {
     return (float)__builtin_amdgcn_ubfe(c, 4 * j, 4);
   }

@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(_HERE, "libmoe_layer.so")
 
 FLAG_FORCE_GEMV = 0x1
 FLAG_FORCE_GEMM = 0x2
+FLAG_TILED_WEIGHTS = 0x4
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_MISALIGNED", 5: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_layer_forward", "moe_route", "moe_layer_forward_traced",
-           "moe_layer_forward_q4", "moe_status_string", "moe_last_hip_error")
+           "moe_layer_forward_q4", "moe_tile_weights", "moe_status_string", "moe_last_hip_error")
 
 # moe_kernel_t
 KERNELS = {1: "router_scores", 2: "topk", 3: "route_scan", 4: "route_scatter", 5: "gemm_gateup",
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route.argtypes = [ctypes.POINTER(MoeDesc), vp, vp, ctypes.c_int, vp, sz, vp,
                                 ctypes.POINTER(MoeRouting)]
         L.moe_route.restype = ctypes.c_int
+        L.moe_tile_weights.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+        L.moe_tile_weights.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_hip_error.argtypes = []
@@ -217,6 +220,20 @@ def forward_q4(x: torch.Tensor, router_w: torch.Tensor, codes: torch.Tensor, sca
                                     _stream(stream), None if r is None else ctypes.byref(r),
                                     None if trace is None else ctypes.byref(trace))
     _check(st, "moe_layer_forward_q4")
+    return out
+
+
+def tile_weights(w: torch.Tensor, H: int, I: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_tile_weights: bf16 expert blocks (w.numel() // (3*I*H) of them, row-major packing) rewritten
+    into the tiled layout read with FLAG_TILED_WEIGHTS; returns a tensor of w's shape."""
+    n = w.numel() // (3 * I * H)
+    if n * 3 * I * H != w.numel():
+        raise ValueError("w must hold whole expert blocks of 3*I*H elements")
+    if out is None:
+        out = torch.empty_like(w)
+    st = lib().moe_tile_weights(n, int(H), int(I), _ptr(w, torch.bfloat16, "w"), _ptr(out, torch.bfloat16, "out"),
+                                _stream(stream))
+    _check(st, "moe_tile_weights")
     return out
 
 

@@ -155,3 +155,23 @@ def test_forward_q4_rejects_bad_arguments():
     assert fwd_q4(_desc(I=96)) == SHAPE
     assert fwd_q4(d, k=17) == SHAPE
     assert fwd_q4(_desc(M=0), ws=None, wsb=0) == OK
+
+
+def test_tiled_flag_and_tile_weights_arguments():
+    L = moe.lib()
+    # the tiled layout holds bf16 weights: the 4-bit entry point rejects the flag
+    assert fwd_q4(_desc(flags=moe.FLAG_TILED_WEIGHTS)) == INVALID
+    assert ws_size(_desc(flags=moe.FLAG_TILED_WEIGHTS), 2) == ws_size(_desc(), 2)
+    assert ws_size(_desc(flags=moe.FLAG_TILED_WEIGHTS | moe.FLAG_FORCE_GEMM), 2) > 0
+    dst = FAKE + (1 << 28)
+    tw = L.moe_tile_weights
+    assert tw(-1, 256, 128, FAKE, dst, None) == INVALID
+    assert tw(2, 256, 128, None, dst, None) == INVALID
+    assert tw(2, 256, 128, FAKE, None, None) == INVALID
+    assert tw(2, 100, 128, FAKE, dst, None) == SHAPE
+    assert tw(2, 256, 96, FAKE, dst, None) == SHAPE
+    assert tw(2, 256, 32768, FAKE, dst, None) == SHAPE
+    assert tw(2, 256, 128, FAKE + 8, dst, None) == MISALIGNED
+    assert tw(2, 256, 128, FAKE, dst + 4, None) == MISALIGNED
+    assert tw(2, 256, 128, FAKE, FAKE + 1024, None) == INVALID  # dst overlaps src
+    assert tw(0, 256, 128, FAKE, dst, None) == OK  # no blocks: nothing enqueued
