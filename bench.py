@@ -57,9 +57,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 # source files each kernel is built from (traffic figures taken from other sources are stale)
 KERNEL_SOURCES = {
-    "k_dec": ("decode.hip", "wave_topk.h", "weights.h", "moe_internal.h"),
-    "k_sm": ("smallm.hip", "wave_topk.h", "weights.h", "moe_internal.h"),
-    "k_grouped_gemm": ("grouped_gemm.hip", "moe_internal.h"),
+    "k_dec": ("decode.hip", "wave_topk.h", "weights.h", "moe_internal.h", "tiling.hip"),
+    "k_sm": ("smallm.hip", "wave_topk.h", "weights.h", "moe_internal.h", "tiling.hip"),
+    "k_grouped_gemm": ("grouped_gemm.hip", "moe_internal.h", "tiling.hip"),
     "k_combine": ("grouped_gemm.hip", "moe_internal.h"),
     "k_router_logits": ("route.hip", "moe_internal.h"),
     "k_topk": ("route.hip", "wave_topk.h", "moe_internal.h"),
