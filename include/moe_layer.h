@@ -225,7 +225,7 @@ moe_status_t moe_layer_forward_q4(const moe_desc_t* d, const void* x, const void
  *   a panel is its K/64 steps (K = H for gate/up, I for down) one after
  *     another; a step is its tile rows in order, 64 elements each (the row's
  *     elements 64s .. 64s+63), the 8-element chunk q of tile row R stored at
- *     chunk position q ^ (R % 8).
+ *     chunk position q ^ ((R / 2) % 8).
  * For the shared expert call with nblocks = 1 and I = I_shared.  src and dst
  * are device pointers, 16-byte aligned, not overlapping; H and I follow the
  * layer's shape rules.  Asynchronous on `stream` like the layer calls. */

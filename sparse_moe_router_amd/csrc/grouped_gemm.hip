@@ -133,8 +133,11 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t c, uint32_t g) {
 // wave's transfers of step s are done), refills the stages consumed at step
 // s-1 and multiplies from the stages of step s.  Rows of a stage are 128
 // bytes with the 16-byte chunks XOR-swizzled by the row (chunk q of row r at
-// position q ^ (r & 7)), realised by choosing each lane's source chunk, so
-// the MFMA operand reads are conflict-free.  MFMA sub-step kk and lane half
+// position q ^ ((r >> 1) & 7)), realised by choosing each lane's source
+// chunk: the LDS serves a 16-byte read 16 lanes at a time, here 16
+// consecutive rows, two per 256-byte line of its 64 banks, and the swizzle
+// gives them 16 distinct bank groups (with q ^ (r & 7), rows r and r + 8
+// collide and every operand read takes twice as long).  MFMA sub-step kk and lane half
 // h take the 8 K-values 32h+8kk .. 32h+8kk+7 on both operands, a consistent
 // permutation of K.
 //
@@ -150,7 +153,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cg = wave & 3, rg = wave >> 2;
-  const int lr = lane >> 3, lq = (lane & 7) ^ lr;  // transfers: row within 8, swizzled source chunk
+  const int lr = lane >> 3;  // transfers: row within 8
+  // source chunk of this lane in a transfer that fills stage rows 8 blk .. +8
+  auto srcq = [&](int blk) { return (lane & 7) ^ ((4 * (blk & 1) + (lr >> 1)) & 7); };
 
   int K, N, ncol0, ldw;
   if (MODE == 0) {
@@ -215,13 +220,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
         woff[i] = (uint32_t)(pbase * 2 + (8 * blk < trows ? blk : 0) * 1024 + lane * 16);
       }
     } else {
-      // transfer i: rows 8i + lane/8 of col block rg, chunk lq
+      // transfer i: rows 8i + lane/8 of col block rg (stage block 8 cg + 4 rg + i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) woff[i] = (uint32_t)((wrow_elem(rg, 8 * i + lr) + 8 * lq) * 2);
+      for (int i = 0; i < 4; ++i)
+        woff[i] = (uint32_t)((wrow_elem(rg, 8 * i + lr) + 8 * srcq(cg * 8 + rg * 4 + i)) * 2);
     }
   }
 
-  // ---- activation rows this wave moves: rows (wave*NRH + i)*8 + lane/8, chunk lq
+  // ---- activation rows this wave moves: rows (wave*NRH + i)*8 + lane/8
   const char* asrc[NRH];
 #pragma unroll
   for (int i = 0; i < NRH; ++i) {
@@ -234,7 +240,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
     } else {
       rowp = (is_shared ? p.a_s : p.a_r) + ((int64_t)tl.pos0 + r) * Ig;
     }
-    asrc[i] = (const char*)(rowp + 8 * lq);
+    asrc[i] = (const char*)(rowp + 8 * srcq(wave * NRH + i));
   }
 
   auto load_a = [&](u32x4_t* st, int s) {
@@ -258,8 +264,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
     for (int cb = 0; cb < 2; ++cb) acc[j][cb] = (f32x16_t){};
 
   // operand reads: activation row 32 (2j + rg) + l32, weight row 64 cg + 32 cb
-  // + l32, chunk 4 half + kk, swizzled by the row (both rows are = l32 mod 8)
-  const int swr = l32 & 7;
+  // + l32, chunk 4 half + kk, swizzled by the row (both rows are = l32 mod 16)
+  const int swr = (l32 >> 1) & 7;
   // One K-step from stages (sa, sw).  The step's transfers (activation step
   // a_next into na, weight step w_next into nw) are issued between the MFMA
   // sub-steps: a wave that stalls issuing them leaves its SIMD to the other

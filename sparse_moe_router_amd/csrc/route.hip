@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
     const int e = e0 + row;
     srcA[i] = (const u32x4_t*)(x + (t < M ? t : 0) * (int64_t)H) + q;
     srcB[i] = (const u32x4_t*)(wr + (int64_t)(e < E ? e : 0) * H) + q;
-    dst[i] = row * 8 + (q ^ (row & 7));
+    dst[i] = row * 8 + (q ^ ((row >> 1) & 7));
   }
   const int nsteps = H / 64;
   u32x4_t ra[RD][2], rb[RD][2];
@@ -94,8 +94,8 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int q = 2 * kk + half;
-          a[kk] = sA[buf][arow * 8 + (q ^ (arow & 7))];
-          b[kk] = sB[buf][brow * 8 + (q ^ (brow & 7))];
+          a[kk] = sA[buf][arow * 8 + (q ^ ((arow >> 1) & 7))];
+          b[kk] = sB[buf][brow * 8 + (q ^ ((brow >> 1) & 7))];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

@@ -20,7 +20,7 @@
 //     = min(256, H - 256p) rows 256p .. as tile rows 0 .. n-1;
 //   a panel is K/64 steps one after another (K = H for gate/up, I for
 //   down), a step being its tile rows in order, 64 elements each, with the
-//   8-element chunk q of tile row R at chunk position q ^ (R % 8).
+//   8-element chunk q of tile row R at chunk position q ^ ((R / 2) % 8).
 #include "moe_internal.h"
 
 namespace moe {
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void k_tile_bf16(const u32x4_t* __restrict__ s
       const int64_t per = (int64_t)128 * n;  // elements per step: 2n tile rows x 64
       const int64_t s = rem / per;
       const int w = (int)(rem - s * per);
-      const int R = w >> 6, q = ((w >> 3) & 7) ^ (R & 7);
+      const int R = w >> 6, q = ((w >> 3) & 7) ^ ((R >> 1) & 7);
       const int m = (R >> 5) & 1;
       const int64_t row = 128 * pn + 32 * (R >> 6) + (R & 31);
       from = ((int64_t)m * I + row) * H + 64 * s + 8 * q;
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void k_tile_bf16(const u32x4_t* __restrict__ s
       const int64_t per = (int64_t)64 * n;
       const int64_t s = rem / per;
       const int w = (int)(rem - s * per);
-      const int R = w >> 6, q = ((w >> 3) & 7) ^ (R & 7);
+      const int R = w >> 6, q = ((w >> 3) & 7) ^ ((R >> 1) & 7);
       from = gu + (256 * pn + R) * (int64_t)I + 64 * s + 8 * q;
     }
     dst[d] = src[b * block_chunks + (from >> 3)];

@@ -14,8 +14,8 @@
 //    (n = min(256, H - 256p)) as tile rows 0 .. n-1.  A panel stores its
 //    K-steps of 64 one after another, each as its tile rows of 64 elements,
 //    whose eight 8-element chunks sit XOR-swizzled (chunk q of tile row R at
-//    position q ^ (R % 8)).  A row's chunk is found at
-//    panel + step * (tile rows * 64) + R * 64 + 8 * (q ^ (R % 8)); the eight
+//    position q ^ ((R / 2) % 8)).  A row's chunk is found at
+//    panel + step * (tile rows * 64) + R * 64 + 8 * (q ^ ((R / 2) % 8)); the eight
 //    chunks of a step stay inside one 128-byte line, so loads that cover a
 //    row's 64 elements stay coalesced.
 //  - WQ4: the 4-bit group-affine format of "Optimizing on-device inference
@@ -61,7 +61,7 @@ struct WBf16T {
   struct Row {
     const uint16_t* p;  // tile row R of the row's first K-step
     int step;           // elements per K-step of its panel
-    int swz;            // R % 8
+    int swz;            // (R / 2) % 8
     __device__ __forceinline__ chunk_t load(int64_t k) const {
       return *(const u32x4_t*)(p + (k >> 6) * step + 8 * (((int)(k >> 3) & 7) ^ swz));
     }
@@ -70,11 +70,11 @@ struct WBf16T {
   __device__ __forceinline__ Row gu(int m, int i, int H, int I) const {
     const int pn = i >> 7, j = i & 127, n = I - 128 * pn < 128 ? I - 128 * pn : 128;
     const int R = 64 * (j >> 5) + 32 * m + (j & 31);
-    return {p + (int64_t)256 * pn * H + 64 * R, 128 * n, R & 7};
+    return {p + (int64_t)256 * pn * H + 64 * R, 128 * n, (R >> 1) & 7};
   }
   __device__ __forceinline__ Row dn(int c, int H, int I) const {
     const int pn = c >> 8, R = c & 255, n = H - 256 * pn < 256 ? H - 256 * pn : 256;
-    return {p + (int64_t)2 * I * H + (int64_t)256 * pn * I + 64 * R, 64 * n, R & 7};
+    return {p + (int64_t)2 * I * H + (int64_t)256 * pn * I + 64 * R, 64 * n, (R >> 1) & 7};
   }
   __device__ __forceinline__ static float dot(const chunk_t& w, const u32x4_t& x) { return WBf16::dot(w, x); }
   __device__ __forceinline__ static float dot(const chunk_t& w, const f32x4_t& x0, const f32x4_t& x1) {

@@ -34,13 +34,13 @@ def host_tile(blocks: np.ndarray, H: int, I: int) -> np.ndarray:
             p, j = divmod(i, 128)
             rows_p = min(128, I - 128 * p)
             R = 64 * (j // 32) + 32 * m + j % 32
-            pos = 256 * p * H + (k // 64) * (2 * rows_p * 64) + 64 * R + 8 * (((k // 8) % 8) ^ (R % 8)) + k % 8
+            pos = 256 * p * H + (k // 64) * (2 * rows_p * 64) + 64 * R + 8 * (((k // 8) % 8) ^ ((R // 2) % 8)) + k % 8
             dst[:, pos] = blocks[:, (m * I + i) * H + k]
     k = np.arange(I)
     for c in range(H):  # down: row c -> panel c // 256, tile row c % 256
         p, R = divmod(c, 256)
         rows_p = min(256, H - 256 * p)
-        pos = 2 * I * H + 256 * p * I + (k // 64) * (rows_p * 64) + 64 * R + 8 * (((k // 8) % 8) ^ (R % 8)) + k % 8
+        pos = 2 * I * H + 256 * p * I + (k // 64) * (rows_p * 64) + 64 * R + 8 * (((k // 8) % 8) ^ ((R // 2) % 8)) + k % 8
         dst[:, pos] = blocks[:, 2 * I * H + c * I + k]
     return dst
 
