@@ -312,38 +312,29 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, float* L,
                                 uint64_t* cmask, int64_t M, int H, int E, const Launch& lc) {
   dim3 grid((unsigned)((M + 63) / 64), (unsigned)((E + 63) / 64));
-  launch(lc, k_router_logits, grid, dim3(256), x, wr, bias, L, cmask, M, H, E);
-  return hipGetLastError();
+  return launch(lc, k_router_logits, grid, dim3(256), x, wr, bias, L, cmask, M, H, E);
 }
 
 hipError_t launch_topk(const float* L, int32_t* ids, float* w, uint64_t* cmask, int64_t M, int E, int k,
                        const Launch& lc) {
   dim3 grid((unsigned)((M + 3) / 4));
-  if (E <= 64)
-    launch(lc, k_topk<1>, grid, dim3(256), L, ids, w, cmask, M, E, k);
-  else if (E <= 128)
-    launch(lc, k_topk<2>, grid, dim3(256), L, ids, w, cmask, M, E, k);
-  else if (E <= 256)
-    launch(lc, k_topk<4>, grid, dim3(256), L, ids, w, cmask, M, E, k);
-  else if (E <= 512)
-    launch(lc, k_topk<8>, grid, dim3(256), L, ids, w, cmask, M, E, k);
-  else
-    launch(lc, k_topk<16>, grid, dim3(256), L, ids, w, cmask, M, E, k);
-  return hipGetLastError();
+  if (E <= 64) return launch(lc, k_topk<1>, grid, dim3(256), L, ids, w, cmask, M, E, k);
+  if (E <= 128) return launch(lc, k_topk<2>, grid, dim3(256), L, ids, w, cmask, M, E, k);
+  if (E <= 256) return launch(lc, k_topk<4>, grid, dim3(256), L, ids, w, cmask, M, E, k);
+  if (E <= 512) return launch(lc, k_topk<8>, grid, dim3(256), L, ids, w, cmask, M, E, k);
+  return launch(lc, k_topk<16>, grid, dim3(256), L, ids, w, cmask, M, E, k);
 }
 
 hipError_t launch_route_scan(const uint64_t* cmask, int32_t* cbase, int32_t* counts, int32_t* offsets,
                              Tile* tiles, int32_t* ntiles, int64_t M, int E, int k, bool shared, const Launch& lc) {
-  launch(lc, k_route_scan, dim3(1), dim3(1024), cmask, cbase, counts, offsets, tiles, ntiles,
-                     M, E, k, shared ? 1 : 0);
-  return hipGetLastError();
+  return launch(lc, k_route_scan, dim3(1), dim3(1024), cmask, cbase, counts, offsets, tiles, ntiles, M, E, k,
+                shared ? 1 : 0);
 }
 
 hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const int32_t* cbase,
                                 int32_t* perm, int32_t* inv, int64_t M, int E, int k, const Launch& lc) {
   dim3 grid((unsigned)((M + kChunk - 1) / kChunk));
-  launch(lc, k_route_scatter, grid, dim3(256), ids, cmask, cbase, perm, inv, M, E, k);
-  return hipGetLastError();
+  return launch(lc, k_route_scatter, grid, dim3(256), ids, cmask, cbase, perm, inv, M, E, k);
 }
 
 }  // namespace moe
