@@ -7,7 +7,7 @@ import torch
 
 import oracle.moe_oracle as O
 from gpu_util import (HostLayer, bits_to_dev, check, device_layer, edge_case as _edge, moe, oracle_fn,
-                      run_gpu, S, SD, f32)
+                      routing_buffers, run_gpu, S, SD, f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,6 +92,31 @@ def test_long_prefill_chunk():
     w = S.LONG
     g, st = _full_case(w, x_row0=5 * w.M, nsample=6)
     print("long chunk 5", st)
+
+
+def test_long_prompt_single_call():
+    """The 131,072-token prompt in one call (the largest configuration): bit-identical to the
+    same rows in 16 calls of 8,192, and sampled tokens against the oracle."""
+    w = S.LONG
+    big = S.reduced(w, M=w.tokens, chunks=1)
+    x, r, ex, sh = device_layer(big)
+    rb = routing_buffers(big.M, w.E, w.k, grouped=False)
+    one = moe.forward(x, r, ex, sh, w.k, routing=rb)
+    chunked = torch.empty_like(x)
+    for c in range(w.chunks):
+        moe.forward(x[c * w.M:(c + 1) * w.M], r, ex, sh, w.k, out=chunked[c * w.M:(c + 1) * w.M])
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), chunked.view(torch.int16)), "one call != 16 chunks"
+    del ex, chunked
+    rng = np.random.default_rng(17)
+    sample = sorted(set(rng.choice(big.M, 6, replace=False).tolist()) | {0, big.M - 1})
+    hl = HostLayer(big)
+    xs = np.concatenate([hl.x(t, 1) for t in sample])
+    g = {n: t[sample].cpu().numpy() for n, t in rb.items()}
+    g["out"] = one[sample].float().cpu().numpy()
+    hl.prefetch(g["topk_ids"].ravel())
+    st = check(g, oracle_fn(hl, xs), w.k, w.E, grouped=False, label="long prompt, one call")
+    print("long prompt one call", st)
 
 
 def test_decode_full_shape():
