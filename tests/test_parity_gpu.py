@@ -181,6 +181,15 @@ def test_hidden_not_multiple_of_128():
     _edge(1, 192, 16, 2, 64, 64, seed=9)
 
 
+@pytest.mark.parametrize("M,flags", [(1, 0), (5, moe.FLAG_FORCE_GEMV), (70, 0)])
+def test_largest_dimensions(M, flags):
+    """H and I at the supported maximum (16384) on every path: 256 K-steps in the grouped GEMMs
+    and the router scores, 16384-element rows in the matrix-vector kernels."""
+    _edge(M, 16384, 4, 2, 64, 64, flags=flags, seed=M)      # H = 16384
+    _edge(M, 64, 2, 1, 16384, 0, flags=flags, seed=M + 1)  # I = 16384 (down K), no shared expert
+    _edge(M, 64, 2, 1, 64, 16384, flags=flags, seed=M + 2)  # shared I = 16384
+
+
 def test_decode_topk_32():
     _edge(1, 128, 64, 32, 64, 64, seed=10)
     _edge(40, 128, 64, 32, 64, 64, seed=11)
