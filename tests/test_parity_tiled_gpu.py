@@ -123,3 +123,10 @@ def test_tiled_skewed_prefill():
     x, r, ex, sh = device_layer(w)
     bias = torch.from_numpy(S.zipf_router_bias(w)).cuda()
     _assert_same(_both(x, r, ex, sh, w.k, bias=bias), "skew M=4096")
+
+
+def test_tiled_long_prompt_chunk():
+    """An 8192-token chunk of the long prompt (groups of ~288 rows: two tiles each)."""
+    w = S.LONG
+    x, r, ex, sh = device_layer(w, x_row0=3 * w.M)
+    _assert_same(_both(x, r, ex, sh, w.k), "long chunk M=8192")
