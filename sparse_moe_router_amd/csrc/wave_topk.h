@@ -123,13 +123,15 @@ __device__ __forceinline__ uint64_t wave_topk_radix(const float (&f)[EPL], int E
 }
 
 // The same selection (same results) with far fewer ballots, which dominate
-// the cost: a radix select over the 64 lane maxima alone (one ballot per
-// bit) finds T1, the k-th largest lane maximum.  k distinct lanes hold a
-// value >= T1, so the k-th largest value is >= T1 and every winner is among
-// the candidates {values >= T1}, normally a dozen or so.  The candidates are
+// the cost: a radix select over the 64 lane maxima alone finds T, the
+// k-th largest lane maximum T1 with its low 16 bits cleared (sign, exponent
+// and 7 mantissa bits: 8 rounds of three independent ballots, two bits per
+// round).  k distinct lanes hold a value >= T1 >= T, so every winner is
+// among the candidates {values >= T}: the winners plus the few values
+// within 2^-7 of T1, normally a dozen or so in all.  The candidates are
 // compacted into LDS and each ranks itself among them by (score, lower
-// index); ranks < k are the selection.  When more than 64 values tie at or
-// above T1, the full radix select above takes over.
+// index); ranks < k are the selection.  When more than 64 values lie at or
+// above T (ties), the full radix select above takes over.
 template <int EPL>
 __device__ __forceinline__ uint64_t wave_topk(const float (&f)[EPL], int E, int k, int lane, uint64_t* top,
                                               uint64_t* s_keys) {
@@ -140,10 +142,12 @@ __device__ __forceinline__ uint64_t wave_topk(const float (&f)[EPL], int E, int 
 #pragma unroll
   for (int q = 1; q < EPL; ++q) m = v[q] > m ? v[q] : m;
   uint32_t T = 0;
-#pragma unroll 8
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    if (__popcll(__ballot(m >= cand)) >= k) T = cand;
+#pragma unroll
+  for (int bit = 30; bit >= 16; bit -= 2) {
+    const uint32_t c1 = T | (1u << bit), c2 = T | (2u << bit), c3 = T | (3u << bit);
+    const int n1 = __popcll(__ballot(m >= c1)), n2 = __popcll(__ballot(m >= c2));
+    const int n3 = __popcll(__ballot(m >= c3));
+    T = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : T;
   }
   int C = 0;
 #pragma unroll

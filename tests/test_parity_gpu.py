@@ -159,6 +159,24 @@ def test_zero_router_exact_ties():
     assert np.allclose(g["topk_w"], 0.25, rtol=0, atol=1e-7)
 
 
+@pytest.mark.parametrize("M", [1, 5, 70])
+@pytest.mark.parametrize("cluster", [40, 100])
+def test_clustered_scores_select_exactly(M, cluster):
+    """Scores set by a router bias (zero router weights): `cluster` experts on 16 levels within
+    2^-8 of 1.0 (many exact ties), the rest near -4.  With 40 such experts the selection's
+    prefilter keeps them all as candidates and ranks them; with 100 (more than a wave's 64 lanes)
+    its full radix select takes over.  On the decode, small-batch and grouped paths the ids must be
+    exactly the first k of (score descending, expert index ascending)."""
+    E, k = 256, 8
+    rng = np.random.default_rng(cluster + M)
+    bias = (rng.standard_normal(E) - 4.0).astype(np.float32)
+    members = rng.choice(E, cluster, replace=False)
+    bias[members] = (1.0 + rng.integers(0, 16, cluster) * 2.0 ** -12).astype(np.float32)
+    g, _ = _edge(M, 128, E, k, 64, 64, zero_router=True, bias=bias, seed=cluster)
+    want = np.lexsort((np.arange(E), -bias.astype(np.float64)))[:k]
+    assert (g["topk_ids"] == want[None, :]).all()
+
+
 def test_hot_expert_bias():
     g, _ = _edge(520, 256, 32, 4, 64, 64, hot=5)
     assert (g["topk_ids"][:, 0] == 5).all() and g["counts"][5] == 520
