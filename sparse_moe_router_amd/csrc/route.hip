@@ -201,41 +201,9 @@ __global__ __launch_bounds__(1024) void k_route_scan(const uint64_t* __restrict_
   const int64_t c0 = active ? (int64_t)part * cpp : 0;
   const int64_t c1 = active ? (c0 + cpp < nchunk ? c0 + cpp : nchunk) : 0;
 
-  // pass 1: partial counts per (part, expert).  A part of at most kScanReg
-  // chunks (every call up to kScanReg * 64 * P tokens: 8192 at E = 256)
-  // issues its loads in batches of 16 and keeps the popcounts (four per
-  // word, each <= 64) for pass 2; longer parts stream in batches of eight
-  // and pass 2 reads them again.
+  // pass 1: partial counts per (part, expert)
   int psum = 0;
-  constexpr int kScanReg = 32, kScanBatch = 16;
-  const bool in_regs = cpp <= kScanReg;  // uniform
-  uint32_t pc4[kScanReg / 4];
-  if (in_regs) {
-    // unconditional loads (chunks past the part re-read its last one, or
-    // chunk 0), counted only inside the part: no branch between the loads
-    const int64_t clast = c1 > 0 ? c1 - 1 : 0;
-#pragma unroll
-    for (int h = 0; h < kScanReg / kScanBatch; ++h) {
-      if (h > 0 && cpp <= h * kScanBatch) {
-#pragma unroll
-        for (int w = h * kScanBatch / 4; w < kScanReg / 4; ++w) pc4[w] = 0u;
-        break;
-      }
-      uint64_t v[kScanBatch];
-#pragma unroll
-      for (int j = 0; j < kScanBatch; ++j) {
-        const int64_t c = c0 + h * kScanBatch + j;
-        v[j] = cmask[(c < clast ? c : clast) * E + e];
-      }
-#pragma unroll
-      for (int j = 0; j < kScanBatch; ++j) {
-        const int jj = h * kScanBatch + j;
-        const uint32_t n = c0 + jj < c1 ? (uint32_t)__popcll(v[j]) : 0u;
-        psum += (int)n;
-        pc4[jj / 4] = jj % 4 == 0 ? n : pc4[jj / 4] | (n << (8 * (jj % 4)));
-      }
-    }
-  } else {
+  {
     int64_t c = c0;
     for (; c + 8 <= c1; c += 8) {  // eight independent loads in flight
       uint64_t v[8];
@@ -294,14 +262,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(const uint64_t* __restrict_
     }
   }
   __syncthreads();
-  if (active && in_regs) {
-    int run = s_part[tid];
-#pragma unroll
-    for (int j = 0; j < kScanReg; ++j) {
-      if (c0 + j < c1) cbase[(c0 + j) * E + e] = run;
-      run += (int)((pc4[j / 4] >> (8 * (j % 4))) & 0xFFu);
-    }
-  } else if (active) {
+  if (active) {
     int run = s_part[tid];
     int64_t c = c0;
     for (; c + 8 <= c1; c += 8) {
