@@ -7,7 +7,9 @@ workspaces are independent.
     other work on the device in between (decode, small-batch and grouped
     paths; bf16, tiled bf16 and 4-bit weights);
   - calls on two streams with two workspaces, interleaved, give the bits of
-    the same calls made one after another."""
+    the same calls made one after another;
+  - a traced call (per-kernel events) gives the bits of the untraced one and
+    records its path's kernels in launch order, up to the trace's capacity."""
 import numpy as np
 import pytest
 import torch
@@ -100,3 +102,41 @@ def test_two_streams_two_workspaces(M):
     for i in range(4):
         assert torch.equal(outs_a[i].view(torch.int16), ref_a.view(torch.int16)), f"stream a call {i}"
         assert torch.equal(outs_b[i].view(torch.int16), ref_b.view(torch.int16)), f"stream b call {i}"
+
+
+PATH_KERNELS = {1: [8, 9, 10], 8: [11, 12, 13, 14], 300: [1, 2, 3, 4, 5, 6, 7]}  # moe_kernel_t ids
+
+
+@pytest.mark.parametrize("kind", ["bf16", "q4"])
+@pytest.mark.parametrize("M", [1, 8, 300])
+def test_traced_call_matches_and_records_kernels(kind, M):
+    """With a trace the call gives the bits of the untraced call and records each kernel of its
+    path once, in launch order, with a finite duration; with a trace shorter than the path the
+    rest of the kernels run untimed and unrecorded (count stops at capacity)."""
+    import ctypes
+    import bench
+    hip = bench.Hip()
+    r, wts, flags = _weights(kind, seed=7)
+    x = upload(np.random.default_rng(30 + M).standard_normal((M, H)).astype(np.float32))
+    ws = torch.empty(moe.workspace_size(M, H, E, I, IS, K, flags=flags), dtype=torch.uint8, device="cuda")
+    ref = _call(x, r, wts, flags, torch.empty_like(x), ws).clone()
+    torch.cuda.synchronize()
+    want = PATH_KERNELS[M]
+    for cap in (16, 2):
+        begin, end = hip.events(16), hip.events(16)
+        kid = (ctypes.c_int32 * 16)(*([-1] * 16))
+        tr = moe.MoeTrace(ctypes.cast(begin, ctypes.POINTER(ctypes.c_void_p)),
+                          ctypes.cast(end, ctypes.POINTER(ctypes.c_void_p)), kid, cap, 0)
+        out = torch.empty_like(x)
+        if kind == "q4":
+            moe.forward_q4(x, r, *wts, K, out=out, flags=flags, workspace=ws, trace=tr)
+        else:
+            moe.forward(x, r, wts[0], wts[1], K, out=out, flags=flags, workspace=ws, trace=tr)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"capacity {cap}"
+        n = min(len(want), cap)
+        assert tr.count == n and list(kid[:16]) == want[:n] + [-1] * (16 - n), f"capacity {cap}"
+        for i in range(n):
+            assert 0.0 <= hip.elapsed_ms(begin[i], end[i]) < 1000.0
+        hip.destroy(begin)
+        hip.destroy(end)
