@@ -11,10 +11,17 @@ layer (same shapes; near-uniform and Zipf-skewed routing), one step = one
 layer call; and a long prompt of 131,072 tokens through one layer as 16
 calls of 8,192 rows with one reused workspace, one step = all 16 calls.
 
+Timing: every leg runs its steps in 5 rounds, each bracketed by a device
+synchronisation and timed with events; the reported time per step is the
+median over the rounds (the headline leg times exactly K steps in all).
+The CPU oracle's rounds run between the GPU rounds of the same leg, in the
+same process.  Rooflines count algorithmic bytes and FLOPs only (the
+weights of the experts that received rows, the router, x and out; no
+intermediates, no padding) and are given against the datasheet peaks and
+against the rates the measurement kernels of include/moe_peaks.h sustain.
+
 Inputs are seeded synthetic tensors generated on the device before timing.
-Printed: one JSON line with throughput, the dominant kernel's roofline
-position (per-launch algorithmic bytes over its event-timed duration), and
-the CPU oracle timed on a bounded sample of the same workload.
+Printed: one JSON line.
 """
 from __future__ import annotations
 
@@ -22,6 +29,7 @@ import argparse
 import ctypes
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -31,6 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, datasheet
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, datasheet
 METRIC = "MoE-layer tokens/s: prefill M=4096 & decode M=1; % of MFMA / HBM roofline"
+ROUNDS = 5
 
 
 def parse():
@@ -41,6 +50,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-q4", action="store_true", help="skip the 4-bit expert-weight runs")
     ap.add_argument("--no-long", action="store_true", help="skip the chunked long-prefill run")
+    ap.add_argument("--no-small", action="store_true", help="skip the small-batch runs")
     ap.add_argument("--layout", choices=("tiled", "row"), default="tiled",
                     help="bf16 expert weights: tiled once by moe_tile_weights before timing (default), or "
                          "row-major as generated")
@@ -192,6 +202,10 @@ def kernel_times(hip, moe, calls_fn, n_calls_per_step, steps, kernels_per_call):
     return res
 
 
+def kernels_us(kt):
+    return {n: round(1000.0 * sum(v) / len(v), 3) for n, v in kt.items()}
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -199,6 +213,115 @@ def blas_threads():
         return max(n) if n else 1
     except Exception:
         return os.cpu_count() or 1
+
+
+def round_sizes(total: int, rounds: int = ROUNDS):
+    """`total` steps split into at most `rounds` rounds of (nearly) equal size."""
+    r = max(1, min(rounds, total))
+    return [total // r + (1 if i < total % r else 0) for i in range(r)]
+
+
+def timed_rounds(step, total, between=None, rounds=ROUNDS):
+    """Times exactly `total` calls of step(i) in rounds, each bracketed by a device synchronisation
+    and timed with events on the current stream; between(r) runs after round r, untimed (the CPU
+    oracle's arm of the same leg).  Returns the per-round milliseconds per call."""
+    import torch
+    per = []
+    i = 0
+    for r, n in enumerate(round_sizes(total, rounds)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            step(i)
+            i += 1
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / n)
+        if between is not None:
+            between(r)
+    return per
+
+
+def spread(per):
+    return {"median": round(statistics.median(per), 5), "min": round(min(per), 5), "max": round(max(per), 5),
+            "rounds": len(per)}
+
+
+def roofline_obj(kernel, avg_ms, nbytes, flops, peaks, traffic=None, layer=None):
+    """Roofline position of one kernel from its algorithmic bytes / FLOPs per launch and its average
+    launch duration: the bound is the resource that work needs longer on at datasheet peaks."""
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    tfs = flops / (avg_ms * 1e-3) / 1e12 if flops else 0.0
+    mfma_bound = flops and flops / BF16_PEAK_TFLOPS / 1e12 > nbytes / HBM_PEAK_GBS / 1e9
+    if mfma_bound:
+        r = dict(bound="mfma", achieved=round(tfs, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                 frac=round(tfs / BF16_PEAK_TFLOPS, 4), traffic=traffic,
+                 peak_measured=peaks.get("mfma_tflops"), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+        if peaks.get("mfma_tflops"):
+            r["frac_measured"] = round(tfs / peaks["mfma_tflops"], 4)
+    else:
+        r = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                 frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic,
+                 peak_measured=peaks.get("hbm_gbs"), mfma_frac=round(tfs / BF16_PEAK_TFLOPS, 4))
+        if peaks.get("hbm_gbs"):
+            r["frac_measured"] = round(gbs / peaks["hbm_gbs"], 4)
+    r.update(kernel=kernel, bytes_per_launch=int(nbytes), flops_per_launch=int(flops), avg_us=round(avg_ms * 1e3, 3))
+    if layer is not None:
+        r["layer"] = layer
+    return r
+
+
+def layer_fracs(nbytes, flops, ms, peaks):
+    """Both roofline fractions of a whole layer (or step) from its algorithmic bytes and FLOPs."""
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = flops / (ms * 1e-3) / 1e12
+    d = dict(achieved_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+             achieved_tflops=round(tfs, 1), mfma_frac=round(tfs / BF16_PEAK_TFLOPS, 4),
+             bound="mfma" if flops / BF16_PEAK_TFLOPS / 1e12 > nbytes / HBM_PEAK_GBS / 1e9 else "hbm")
+    if peaks.get("hbm_gbs"):
+        d["hbm_frac_measured"] = round(gbs / peaks["hbm_gbs"], 4)
+    if peaks.get("mfma_tflops"):
+        d["mfma_frac_measured"] = round(tfs / peaks["mfma_tflops"], 4)
+    return d
+
+
+# ------------------------------------------------------------------ measured peaks
+
+def measure_peaks():
+    """Sustainable rates from the two kernels of include/moe_peaks.h: a 4 GiB streaming read (16 times
+    the last-level cache) and a loop of independent bf16 MFMAs on every SIMD; median of 5 rounds."""
+    import torch
+    path = os.path.join(ROOT, "sparse_moe_router_amd", "libmoe_peaks.so")
+    L = ctypes.CDLL(path)
+    L.moe_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    L.moe_peak_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.empty(L.moe_peak_stream_blocks(), dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fsink = torch.empty(cus * 8, dtype=torch.float32, device="cuda")
+    iters = 4096
+    flops = cus * 8 * iters * 8 * 32 * 32 * 16 * 2
+
+    def read(_):
+        s = torch.cuda.current_stream().cuda_stream
+        assert L.moe_peak_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), s) == 0
+
+    def mfma(_):
+        s = torch.cuda.current_stream().cuda_stream
+        assert L.moe_peak_mfma_loop(cus, iters, fsink.data_ptr(), s) == 0
+
+    for f in (read, mfma):
+        f(0)
+    r_ms = statistics.median(timed_rounds(read, 15))
+    m_ms = statistics.median(timed_rounds(mfma, 15))
+    del buf
+    torch.cuda.empty_cache()
+    return dict(hbm_gbs=round(nbytes / (r_ms * 1e-3) / 1e9, 1), mfma_tflops=round(flops / (m_ms * 1e-3) / 1e12, 1),
+                stream_read={"bytes": nbytes, "us": round(r_ms * 1e3, 2)},
+                mfma_loop={"flops": flops, "us": round(m_ms * 1e3, 2), "cus": cus})
 
 
 # ------------------------------------------------------------------ decode
@@ -218,7 +341,42 @@ def q4_layer(SD, S, w, l, dev="cuda"):
     return (codes, sb), (sc, ssb)
 
 
-def bench_decode(args, hip, moe, SD, S, q4=False):
+class CpuDecode:
+    """The oracle's arm of the decode leg: per round, `rows` single-token (M=1) calls through one
+    layer (layer r of the 40), the selected experts' weights regenerated on the host before the
+    timed part.  tok/s = 1 / (mean time per token-layer x layers)."""
+
+    def __init__(self, S, O, rows=24):
+        self.S, self.O, self.rows = S, O, rows
+        self.t = []
+
+    def __call__(self, r):
+        import concurrent.futures as cf
+        S, O, w = self.S, self.O, self.S.DECODE
+        f = S.bf16_bits_to_f32
+        xs = f(S.x_rows(w, r * self.rows, self.rows, 0))
+        rw = f(S.router_weight(w, r))
+        sh = f(S.shared_weight(w, r))
+        ids = O.topk_ids(O.selection_logits(O.router_logits(xs, rw)), w.k)
+        need = sorted(set(int(e) for e in ids.ravel()))
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+            cache = dict(zip(need, ex.map(lambda e: O.unpack_expert(f(S.expert_weight(w, r, e)), w.I, w.H), need)))
+        t = time.perf_counter()
+        for i in range(self.rows):
+            O.moe_forward(xs[i:i + 1], rw, lambda e: cache[e], sh, w.k, w.I)
+        self.t.append((time.perf_counter() - t) / self.rows)
+
+    def result(self, layers):
+        per = statistics.median(self.t)
+        return dict(value=round(1.0 / (per * layers), 4), unit="tok/s", cores=blas_threads(), kind="oracle",
+                    sample=f"{len(self.t)} rounds interleaved with the GPU rounds, each {self.rows} single-token "
+                           f"calls through one of the {layers} layers (float64 NumPy oracle; the selected experts' "
+                           f"weights regenerated outside the timing); tok/s = 1 / (median time per token-layer "
+                           f"x {layers})",
+                    seconds=round(sum(self.t) * self.rows, 3))
+
+
+def bench_decode(args, hip, moe, SD, S, peaks, q4=False, cpu=None):
     import torch
     w = S.DECODE
     L = args.layers
@@ -274,14 +432,8 @@ def bench_decode(args, hip, moe, SD, S, q4=False):
 
     for s in range(args.warmup):
         graphs[s % w.x_pool].replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for s in range(args.steps):
-        graphs[s % w.x_pool].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    per = timed_rounds(lambda i: graphs[i % w.x_pool].replay(), args.steps, between=cpu)
+    ms = statistics.median(per)
 
     # per-kernel durations (eager, traced)
     def step(s, tr):
@@ -293,20 +445,21 @@ def bench_decode(args, hip, moe, SD, S, q4=False):
     # 4-byte scale/bias word per 64 elements = 0.5625 bytes per element)
     wb = 0.5625 if q4 else 2
     layer_bytes = int((k + 1) * w.expert_elems() * wb) + E * H * 2 + 2 * H * 2
-    # the gate/up kernel streams the selected experts' and the shared expert's gate/up rows
-    gateup_bytes = int((k * I + w.I_shared) * 2 * H * wb) + H * 2 + E * 4 + (k * I + w.I_shared) * 4
+    layer_flops = 2 * H * E + (k + 1) * 3 * 2 * H * I
+    # the gate/up kernel streams the selected experts' and the shared expert's gate/up rows and x
+    gateup_bytes = int((k * I + w.I_shared) * 2 * H * wb) + H * 2
+    gateup_flops = (k * I + w.I_shared) * 2 * 2 * H
     dom = "dec_gateup"
     avg_ms = sum(kt[dom]) / len(kt[dom])
-    achieved = gateup_bytes / (avg_ms * 1e-3) / 1e9
+    lay_f = layer_fracs(layer_bytes * L, layer_flops * L, ms, peaks)
     res = dict(
-        value=1000.0 / ms, ms_per_step=ms, gen_s=gen_s,
-        layer_us=ms * 1000.0 / L,
-        layer_hbm_frac=layer_bytes * L / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        kernels_us={n: round(1000.0 * sum(v) / len(v), 3) for n, v in kt.items()},
-        roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_for("k_dec_gateup<q4>" if q4 else "k_dec_gateup"),
-                      kernel="k_dec_gateup" + ("<q4>" if q4 else ""),
-                      bytes_per_launch=gateup_bytes, avg_us=round(avg_ms * 1000, 3)),
+        value=1000.0 / ms, ms_per_step=ms, ms_rounds=spread(per), gen_s=gen_s,
+        layer_us=ms * 1000.0 / L, layer_bytes=layer_bytes, layer=lay_f,
+        kernels_us=kernels_us(kt),
+        roofline=roofline_obj("k_dec_gateup" + ("<q4>" if q4 else ""), avg_ms, gateup_bytes, gateup_flops, peaks,
+                              traffic=traffic_for("k_dec_gateup<q4>" if q4 else "k_dec_gateup"),
+                              layer={"hbm_frac": lay_f["hbm_frac"], "frac_measured": lay_f.get("hbm_frac_measured"),
+                                     "us_per_layer": round(ms * 1000.0 / L, 3), "bytes_per_layer": layer_bytes}),
     )
     return res, (layers, xpool)
 
@@ -344,20 +497,14 @@ def bench_small(args, hip, moe, S, layers, xpool, Ms=(2, 4, 8, 16, 32, 64)):
                     c()
             for _ in range(2):
                 g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(steps):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / steps
+            per = timed_rounds(lambda i: g.replay(), steps)
+            ms = statistics.median(per)
             union = sum(len(torch.unique(ids[l]).tolist()) for l in range(L)) / L
             layer_bytes = (union + 1) * w.expert_elems() * wb + E * H * 2 + 2 * M * H * 2
             kt = kernel_times(hip, moe, lambda s, tr: [c(tr) for c in calls], L, 3, 7)
             entry[name] = {"tok_s": round(M * 1000.0 / ms, 1), "us_per_layer": round(ms * 1000.0 / L, 3),
                            "hbm_frac": round(layer_bytes * L / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "kernels_us": {n: round(1000.0 * sum(v) / len(v), 3) for n, v in kt.items()}}
+                           "kernels_us": kernels_us(kt)}
             entry["union_experts"] = round(union, 2)
             if name == "small":
                 small_out = out.clone()
@@ -369,63 +516,63 @@ def bench_small(args, hip, moe, S, layers, xpool, Ms=(2, 4, 8, 16, 32, 64)):
     return res
 
 
-def cpu_decode(S, O, layers_sample=2, rows=128):
-    """Oracle on a bounded sample of the decode workload: `rows` single-token (M=1)
-    calls through each of `layers_sample` layers; the selected experts' weights are
-    regenerated on the host outside the timing."""
-    import concurrent.futures as cf
-    w = S.DECODE
-    f = S.bf16_bits_to_f32
-    xs = f(S.x_rows(w, 0, rows, 0))
-    t_total = 0.0
-    for l in range(layers_sample):
-        r = f(S.router_weight(w, l))
-        sh = f(S.shared_weight(w, l))
-        ids = O.topk_ids(O.selection_logits(O.router_logits(xs, r)), w.k)
-        need = sorted(set(int(e) for e in ids.ravel()))
-        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
-            cache = dict(zip(need, ex.map(lambda e: O.unpack_expert(f(S.expert_weight(w, l, e)), w.I, w.H), need)))
-        t = time.perf_counter()
-        for i in range(rows):
-            O.moe_forward(xs[i:i + 1], r, lambda e: cache[e], sh, w.k, w.I)
-        t_total += time.perf_counter() - t
-    per_layer = t_total / (layers_sample * rows)
-    return dict(value=1.0 / (per_layer * w.layers), unit="tok/s", cores=blas_threads(), kind="oracle",
-                sample=f"{rows} single-token calls through each of {layers_sample} of the {w.layers} layers "
-                       f"(fp64 NumPy oracle; selected experts regenerated outside the timing); "
-                       f"tok/s = 1 / (mean time per token-layer x {w.layers})",
-                seconds=round(t_total, 3))
-
-
 # ------------------------------------------------------------------ prefill
 
-def gateup_roofline(kt, w, M, nonempty, q4):
+def gateup_roofline(kt, w, M, nonempty, q4, peaks=None):
     """Roofline position of the gate/up grouped GEMM (k_grouped_gemm<0>) for M rows: algorithmic
-    bytes (weights of the experts that received rows + the shared expert, x once, h written) or
-    flops per launch over its average event-timed duration; the bound is the resource that work
-    needs longer on at peak."""
+    bytes (the gate/up weights of the experts that received rows and of the shared expert, x
+    read once; no intermediates) and FLOPs (2 * 2*I*H per assignment and per token for the
+    shared expert) per launch over its average event-timed duration; the bound is the resource
+    that work needs longer on at datasheet peaks."""
     H, I, k = w.H, w.I, w.k
     wb = 0.5625 if q4 else 2  # weight bytes per element
-    gu_bytes = int((nonempty + 1) * 2 * I * H * wb) + M * H * 2 + (M * k + M) * I * 2
+    gu_bytes = int((nonempty + 1) * 2 * I * H * wb) + M * H * 2
     gu_flops = (M * k + M) * 2 * I * H * 2
     avg = sum(kt["gemm_gateup"]) / len(kt["gemm_gateup"])
-    ach = gu_bytes / (avg * 1e-3) / 1e9
-    ach_tf = gu_flops / (avg * 1e-3) / 1e12
-    mfma_bound = gu_flops / BF16_PEAK_TFLOPS / 1e12 > gu_bytes / HBM_PEAK_GBS / 1e9
     kname = "k_grouped_gemm<0, q4> (gate/up + SwiGLU)" if q4 else "k_grouped_gemm<0> (gate/up + SwiGLU)"
     traffic = traffic_for(f"k_grouped_gemm<0,q4>@{w.name}" if q4 else f"k_grouped_gemm<0>@{w.name}")
-    if mfma_bound:
-        return dict(bound="mfma", achieved=round(ach_tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach_tf / BF16_PEAK_TFLOPS, 4), traffic=traffic, kernel=kname,
-                    flops_per_launch=gu_flops, bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
-                    hbm_frac=round(ach / HBM_PEAK_GBS, 4))
-    return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic, kernel=kname,
-                bytes_per_launch=gu_bytes, avg_us=round(avg * 1000, 2),
-                mfma_frac=round(ach_tf / BF16_PEAK_TFLOPS, 4))
+    return roofline_obj(kname, avg, gu_bytes, gu_flops, peaks or {}, traffic=traffic)
 
 
-def bench_prefill(args, hip, moe, SD, S, w, q4=False):
+class CpuPrefill:
+    """The oracle's arm of a prefill leg: per round, all tokens of the layer (or the first
+    m_sample); every selected expert's weights regenerated on the host once, before the first
+    round."""
+
+    def __init__(self, S, O, w, m_sample=None):
+        import concurrent.futures as cf
+        self.S, self.O, self.w = S, O, w
+        self.m = m_sample or w.M
+        f = S.bf16_bits_to_f32
+        self.x = f(S.x_rows(w, 0, self.m))
+        self.r = f(S.router_weight(w))
+        self.sh = f(S.shared_weight(w))
+        self.bias = S.zipf_router_bias(w)
+        ids = O.topk_ids(O.selection_logits(O.router_logits(self.x, self.r, self.bias)), w.k)
+        self.need = sorted(set(int(e) for e in ids.ravel()))
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+            self.blocks = dict(zip(self.need, ex.map(
+                lambda e: O.unpack_expert(f(S.expert_weight(w, 0, e)), w.I, w.H), self.need)))
+        self.t = []
+
+    def __call__(self, r):
+        w = self.w
+        t = time.perf_counter()
+        self.O.moe_forward(self.x, self.r, lambda e: self.blocks[e], self.sh, w.k, w.I, bias=self.bias)
+        self.t.append(time.perf_counter() - t)
+
+    def result(self):
+        dt = statistics.median(self.t)
+        w = self.w
+        return dict(value=round(self.m / dt, 2), unit="tok/s", cores=blas_threads(), kind="oracle",
+                    sample=(f"first {self.m} of the {w.M} tokens" if self.m < w.M else f"all {w.M} tokens") +
+                           f" through the layer per round, {len(self.t)} rounds interleaved with the GPU rounds "
+                           f"(float64 NumPy oracle; {len(self.need)} experts' weights regenerated outside the "
+                           f"timing); tok/s from the median round",
+                    seconds=round(sum(self.t), 3))
+
+
+def bench_prefill(args, hip, moe, SD, S, w, peaks, q4=False, cpu=None):
     import torch
     if q4:
         x, r, ec, esb, sc, ssb = SD.layer_tensors_q4(w)
@@ -444,39 +591,35 @@ def bench_prefill(args, hip, moe, SD, S, w, q4=False):
                      flags=layout_flag(args, moe, q4))
     for _ in range(args.warmup):
         call()
-    torch.cuda.synchronize()
-    steps = max(10, args.steps // 4)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    kt = kernel_times(hip, moe, lambda s, tr: call(tr), 1, args.trace_steps, 7)
+    per_round = max(20, args.steps // ROUNDS)
+    per = timed_rounds(lambda i: call(), per_round * ROUNDS, between=cpu)
+    ms = statistics.median(per)
+    kt = kernel_times(hip, moe, lambda s, tr: call(tr), 1, args.trace_steps, 8)
     c = counts.cpu()
     nonempty = int((c > 0).sum())
     M, H, E, I, k = w.M, w.H, w.E, w.I, w.k
     wb = 0.5625 if q4 else 2  # weight bytes per element
     layer_bytes = int((nonempty + 1) * w.expert_elems() * wb) + E * H * 2 + 2 * M * H * 2
     flops = M * (2 * H * E + (k + 1) * 3 * 2 * H * I)
-    roof = gateup_roofline(kt, w, M, nonempty, q4)
+    lay_f = layer_fracs(layer_bytes, flops, ms, peaks)
+    roof = gateup_roofline(kt, w, M, nonempty, q4, peaks)
+    roof["layer"] = {"hbm_frac": lay_f["hbm_frac"], "mfma_frac": lay_f["mfma_frac"], "bound": lay_f["bound"]}
     res = dict(
-        value=M / (ms * 1e-3), unit="tok/s", ms_per_step=ms, steps=steps,
+        value=M / (ms * 1e-3), unit="tok/s", ms_per_step=ms, steps=per_round * ROUNDS, ms_rounds=spread(per),
         config=dict(workload=f"{w.name}: {w.describe()}, {'4-bit group-affine' if q4 else 'bf16'} experts",
                     weights_layout=layout_name(args, q4),
                     nonempty_experts=nonempty,
                     max_group=int(c.max()), empty_groups=int((c == 0).sum())),
-        hbm_frac=layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        kernels_us={n: round(1000.0 * sum(v) / len(v), 2) for n, v in kt.items()},
+        layer_bytes=layer_bytes, layer_flops=flops, layer=lay_f,
+        hbm_frac=lay_f["hbm_frac"], mfma_frac=lay_f["mfma_frac"],
+        kernels_us=kernels_us(kt),
         roofline=roof,
     )
     del x, r, ex, sh, ws
     return res
 
 
-def bench_long(args, hip, moe, SD, S, w):
+def bench_long(args, hip, moe, SD, S, w, peaks):
     """Long prefill: w.tokens token rows through one layer as w.chunks calls of w.M rows on
     consecutive slices of one input, with one workspace sized for a chunk and reused.  One pass =
     all chunks; reports the sustained rates over whole passes and the spread over chunks."""
@@ -491,20 +634,14 @@ def bench_long(args, hip, moe, SD, S, w):
     calls = [LayerCall(moe, x[c * M:(c + 1) * M], r, ex, sh, w.k, out[c * M:(c + 1) * M], ws,
                        routing={"counts": counts[c]}, flags=layout_flag(args, moe, False)) for c in range(w.chunks)]
 
-    def one_pass():
+    def one_pass(_=None):
         for call in calls:
             call()
 
     one_pass()
-    torch.cuda.synchronize()
-    passes = max(2, args.steps // 50)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(passes):
-        one_pass()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / passes
+    passes_per_round = 2  # 32 chunk calls per round
+    per = timed_rounds(one_pass, passes_per_round * ROUNDS)
+    ms = statistics.median(per)
     # one more pass with an event between chunks: the per-chunk spread
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(w.chunks + 1)]
     ev[0].record()
@@ -513,50 +650,28 @@ def bench_long(args, hip, moe, SD, S, w):
         ev[c + 1].record()
     torch.cuda.synchronize()
     chunk_ms = [ev[c].elapsed_time(ev[c + 1]) for c in range(w.chunks)]
-    kt = kernel_times(hip, moe, lambda s, tr: calls[s % w.chunks](tr), 1, max(args.trace_steps, w.chunks), 7)
+    kt = kernel_times(hip, moe, lambda s, tr: calls[s % w.chunks](tr), 1, max(args.trace_steps, w.chunks), 8)
     c = counts.cpu()
     nonempty = (c > 0).sum(dim=1)
     H, E, I, k = w.H, w.E, w.I, w.k
     flops = w.tokens * (2 * H * E + (k + 1) * 3 * 2 * H * I)
     layer_bytes = sum(int((int(n) + 1) * w.expert_elems() * 2) + E * H * 2 + 2 * M * H * 2 for n in nonempty)
+    lay_f = layer_fracs(layer_bytes, flops, ms, peaks)
     res = dict(
-        value=w.tokens / (ms * 1e-3), unit="tok/s", ms_per_pass=ms, passes=passes,
+        value=w.tokens / (ms * 1e-3), unit="tok/s", ms_per_pass=ms, passes=passes_per_round * ROUNDS,
+        ms_rounds=spread(per),
         config=dict(workload=f"{w.name}: {w.describe()}, bf16 experts, one workspace reused",
                     weights_layout=layout_name(args, False),
                     nonempty_experts_min=int(nonempty.min()), max_group=int(c.max()),
                     empty_groups_max=int((c == 0).sum(dim=1).max())),
-        mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        hbm_frac=layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        layer=lay_f, mfma_frac=lay_f["mfma_frac"], hbm_frac=lay_f["hbm_frac"],
         chunk_us={"mean": round(1000.0 * sum(chunk_ms) / len(chunk_ms), 1),
                   "min": round(1000.0 * min(chunk_ms), 1), "max": round(1000.0 * max(chunk_ms), 1)},
-        kernels_us={n: round(1000.0 * sum(v) / len(v), 2) for n, v in kt.items()},
-        roofline=gateup_roofline(kt, w, M, int(nonempty.float().mean().round()), False),
+        kernels_us=kernels_us(kt),
+        roofline=gateup_roofline(kt, w, M, int(nonempty.float().mean().round()), False, peaks),
     )
     del x, out, r, ex, sh, ws
     return res
-
-
-def cpu_prefill(S, O, w, m_sample=None):
-    """Oracle on the first m_sample tokens (default: all) of the workload through the layer."""
-    import concurrent.futures as cf
-    m_sample = m_sample or w.M
-    f = S.bf16_bits_to_f32
-    x = f(S.x_rows(w, 0, m_sample))
-    r = f(S.router_weight(w))
-    sh = f(S.shared_weight(w))
-    bias = S.zipf_router_bias(w)
-    ids = O.topk_ids(O.selection_logits(O.router_logits(x, r, bias)), w.k)
-    need = sorted(set(int(e) for e in ids.ravel()))
-    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
-        blocks = dict(zip(need, ex.map(lambda e: O.unpack_expert(f(S.expert_weight(w, 0, e)), w.I, w.H), need)))
-    t = time.perf_counter()
-    O.moe_forward(x, r, lambda e: blocks[e], sh, w.k, w.I, bias=bias)
-    dt = time.perf_counter() - t
-    return dict(value=m_sample / dt, unit="tok/s", cores=blas_threads(), kind="oracle",
-                sample=(f"first {m_sample} of the {w.M} tokens" if m_sample < w.M else f"all {w.M} tokens") +
-                       f" through the layer (fp64 NumPy oracle; {len(need)} experts' weights regenerated "
-                       f"outside the timing)",
-                seconds=round(dt, 3))
 
 
 def main():
@@ -571,6 +686,7 @@ def main():
     from synth import inputs as S
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.lib()  # fails loudly when the library is not built
     hip = Hip()
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -580,32 +696,35 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    dec, keep = bench_decode(args, hip, moe, SD, S)
-    small = bench_small(args, hip, moe, S, *keep)
+    peaks = measure_peaks()
+    O = None
+    if not args.no_cpu:
+        import oracle.moe_oracle as O  # the oracle's arms only (CPU baseline)
+    cpu_d = None if O is None else CpuDecode(S, O)
+    dec, keep = bench_decode(args, hip, moe, SD, S, peaks, cpu=cpu_d)
+    small = None if args.no_small else bench_small(args, hip, moe, S, *keep)
     del keep
     torch.cuda.empty_cache()
-    pre = bench_prefill(args, hip, moe, SD, S, S.PREFILL)
-    skew = bench_prefill(args, hip, moe, SD, S, S.SKEW)
-    long = None if args.no_long else bench_long(args, hip, moe, SD, S, S.LONG)
+    cpu_p = None if O is None else CpuPrefill(S, O, S.PREFILL)
+    pre = bench_prefill(args, hip, moe, SD, S, S.PREFILL, peaks, cpu=cpu_p)
+    if cpu_p is not None:
+        pre["cpu_baseline"] = cpu_p.result()
+        del cpu_p
+    skew = bench_prefill(args, hip, moe, SD, S, S.SKEW, peaks)
+    long = None if args.no_long else bench_long(args, hip, moe, SD, S, S.LONG, peaks)
     torch.cuda.empty_cache()
     dec_q4 = pre_q4 = small_q4 = None
     if not args.no_q4:
-        dq, keep = bench_decode(args, hip, moe, SD, S, q4=True)
-        small_q4 = bench_small(args, hip, moe, S, *keep, Ms=(2, 8, 16))
+        dq, keep = bench_decode(args, hip, moe, SD, S, peaks, q4=True)
+        small_q4 = None if args.no_small else bench_small(args, hip, moe, S, *keep, Ms=(2, 8, 16))
         del keep
         torch.cuda.empty_cache()
         dec_q4 = {"value": round(dq["value"], 2), "unit": "tok/s", "ms_per_step": round(dq["ms_per_step"], 4),
-                  "us_per_layer": round(dq["layer_us"], 3), "hbm_frac": round(dq["layer_hbm_frac"], 4),
+                  "ms_rounds": dq["ms_rounds"], "us_per_layer": round(dq["layer_us"], 3), "layer": dq["layer"],
                   "kernels_us": dq["kernels_us"], "roofline": dq["roofline"],
                   "config": {"workload": f"decode batch-1, {args.layers} layers, 4-bit group-affine experts "
                                          f"(g=64, bf16 scale+bias), bf16 router/x/out"}}
-        pre_q4 = bench_prefill(args, hip, moe, SD, S, S.PREFILL, q4=True)
-    cpu_d = cpu_p = None
-    if not args.no_cpu:
-        import oracle.moe_oracle as O
-        cpu_d = cpu_decode(S, O)
-        cpu_p = cpu_prefill(S, O, S.PREFILL)
-        pre["cpu_baseline"] = cpu_p
+        pre_q4 = bench_prefill(args, hip, moe, SD, S, S.PREFILL, peaks, q4=True)
     w = S.DECODE
     line = {
         "metric": METRIC, "value": round(dec["value"], 2), "unit": "tok/s", "n_gpus": 1,
@@ -616,19 +735,22 @@ def main():
                                f"H={w.H} E={w.E} top-{w.k} + 1 shared, I={w.I}, bf16 weights "
                                f"({args.layers * (w.E + 1) * w.expert_elems() * 2 / 1e9:.1f} GB), "
                                f"HIP-graph replay", "layers": args.layers,
-                   "weights_layout": layout_name(args, False)},
+                   "weights_layout": layout_name(args, False),
+                   "timing": f"{args.steps} steps in {len(round_sizes(args.steps))} rounds, median round"},
         "roofline": dec["roofline"],
-        "cpu_baseline": cpu_d,
-        "decode_layer": {"us_per_layer": round(dec["layer_us"], 3), "hbm_frac": round(dec["layer_hbm_frac"], 4),
-                         "kernels_us": dec["kernels_us"]},
+        "cpu_baseline": None if cpu_d is None else cpu_d.result(args.layers),
+        "peaks_measured": peaks,
+        "decode_layer": {"us_per_layer": round(dec["layer_us"], 3), "layer": dec["layer"],
+                         "ms_rounds": dec["ms_rounds"], "kernels_us": dec["kernels_us"]},
         "prefill": pre,
         "prefill_skew": skew,
         "prefill_long": long,
         "decode_q4": dec_q4,
         "prefill_q4": pre_q4,
-        "small_batch": {"config": {"workload": f"M token rows x {args.layers} decode layers (same weights), "
-                                               f"matrix-vector path over the union of selected experts "
-                                               f"vs grouped path"}, "bf16": small, "q4": small_q4},
+        "small_batch": None if args.no_small else {
+            "config": {"workload": f"M token rows x {args.layers} decode layers (same weights), "
+                                   f"matrix-vector path over the union of selected experts vs grouped path"},
+            "bf16": small, "q4": small_q4},
     }
     print(json.dumps(line), flush=True)
 

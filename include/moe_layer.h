@@ -53,8 +53,11 @@
  *   router_w   bf16 [E][H]
  *   expert_w   bf16 [E][3*I*H]; expert e = gate [I][H], up [I][H], down [H][I]
  *   shared_w   bf16 [3*I_shared*H], same packing, or NULL when I_shared == 0
- *   out        bf16 [M][H]; must not overlap any input
+ *   out        bf16 [M][H]
  *   router_bias fp32 [E] or NULL
+ * Outputs (out, the workspace, the routing buffers) must not overlap any
+ * input (x, router_w, the expert and shared weights, router_bias) nor each
+ * other; a call that breaks this returns MOE_ERR_INVALID_ARG.
  *
  * Supported shapes: M >= 0 (M == 0 is a no-op returning MOE_OK),
  * H % 64 == 0 and 64 <= H <= 16384, I % 64 == 0 and 64 <= I <= 16384,
@@ -70,6 +73,11 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* The HIP stream handle, declared exactly as <hip/hip_runtime_api.h>
+ * declares it, so that this header needs no HIP include (an identical
+ * repeated typedef is valid C11 and C++).  NULL is the default stream. */
+typedef struct ihipStream_t* hipStream_t;
 
 typedef enum {
   MOE_OK = 0,
@@ -115,7 +123,22 @@ typedef struct {
   int32_t* offsets;  /* [E+1] exclusive prefix sum of counts (grouped path only) */
   int32_t* perm;     /* [M*top_k] perm[p] = t*top_k + j of the assignment at group
                         position p (grouped path only) */
+  int32_t* tiles;    /* [moe_block_map_capacity()][4] the block map of the grouped
+                        GEMMs (grouped path only; section "Keep expert routing on
+                        the GPU": the list of fixed-size row blocks the grouped
+                        GEMM works on): per tile (group g, first row r0 in the
+                        group, rows, group position of row r0); routed groups
+                        g < E in expert order, then the shared expert (g == E,
+                        its rows are the tokens in order); a group of c rows
+                        is cut into ceil(c / 256) tiles, all of 256 rows but
+                        the last, which holds the rest */
+  int32_t* num_tiles; /* [1] tiles in the block map (grouped path only) */
 } moe_routing_t;
+
+/* Capacity, in tiles, that moe_routing_t.tiles must have for this
+ * descriptor and top_k: ceil(M*top_k/256) + E, plus ceil(M/256) with a
+ * shared expert; 0 when the arguments are invalid.  Pure host computation. */
+int64_t moe_block_map_capacity(const moe_desc_t* d, int top_k);
 
 /* Bytes of device workspace moe_layer_forward / moe_route need for this
  * descriptor and top_k on the path the descriptor selects; 0 when the
@@ -129,13 +152,13 @@ size_t moe_workspace_size(const moe_desc_t* d, int top_k);
  * routing: NULL, or buffers that receive the routing decisions. */
 moe_status_t moe_layer_forward(const moe_desc_t* d, const void* x, const void* router_w,
                                const void* expert_w, const void* shared_w, int top_k, void* out,
-                               void* workspace, size_t workspace_bytes, void* stream,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream,
                                const moe_routing_t* routing);
 
 /* Routing only (scores, top-k, weights and, on the grouped path, the
  * histogram / scan / scatter tables), written to `routing` (non-NULL). */
 moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w, int top_k,
-                       void* workspace, size_t workspace_bytes, void* stream,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream,
                        const moe_routing_t* routing);
 
 /* Kernels of the layer, as reported by moe_layer_forward_traced. */
@@ -175,7 +198,7 @@ typedef struct {
 moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const void* router_w,
                                       const void* expert_w, const void* shared_w, int top_k,
                                       void* out, void* workspace, size_t workspace_bytes,
-                                      void* stream, const moe_routing_t* routing,
+                                      hipStream_t stream, const moe_routing_t* routing,
                                       moe_trace_t* trace);
 
 /* 4-bit group-affine expert weights ("Optimizing on-device inference for
@@ -205,7 +228,7 @@ typedef struct {
  * for the MFMA operands, the decode path multiplies in fp32. */
 moe_status_t moe_layer_forward_q4(const moe_desc_t* d, const void* x, const void* router_w,
                                   const moe_q4_t* experts, const moe_q4_t* shared, int top_k, void* out,
-                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
                                   const moe_routing_t* routing, moe_trace_t* trace);
 
 /* Rewrites nblocks bf16 expert blocks (each 3*H*I elements in the row-major
@@ -229,7 +252,7 @@ moe_status_t moe_layer_forward_q4(const moe_desc_t* d, const void* x, const void
  * For the shared expert call with nblocks = 1 and I = I_shared.  src and dst
  * are device pointers, 16-byte aligned, not overlapping; H and I follow the
  * layer's shape rules.  Asynchronous on `stream` like the layer calls. */
-moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void* src, void* dst, void* stream);
+moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void* src, void* dst, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t s);

@@ -3,8 +3,11 @@
     python -m sparse_moe_router_amd.build
 
 produces ``sparse_moe_router_amd/libmoe_layer.so`` (the layer's C ABI and
-kernels) and ``synth/libsynth.so`` (the device twin of the seeded input
-generator used by tests and the benchmark).
+kernels), ``synth/libsynth.so`` (the device twin of the seeded input
+generator used by tests and the benchmark) and ``synth/libsynth_host.so``
+(its host twin in C, built with gcc) and
+``sparse_moe_router_amd/libmoe_peaks.so`` (the two measurement kernels of
+``include/moe_peaks.h``: sustainable HBM read and bf16 MFMA rates).
 """
 from __future__ import annotations
 
@@ -29,6 +32,8 @@ CFLAGS = [
 
 LIB = os.path.join(PKG, "libmoe_layer.so")
 SYNTH_LIB = os.path.join(ROOT, "synth", "libsynth.so")
+SYNTH_HOST_LIB = os.path.join(ROOT, "synth", "libsynth_host.so")
+PEAKS_LIB = os.path.join(PKG, "libmoe_peaks.so")
 
 
 def _run(cmd):
@@ -73,8 +78,24 @@ def build_synth() -> str:
     return SYNTH_LIB
 
 
+def build_synth_host() -> str:
+    tmp = SYNTH_HOST_LIB + ".tmp"
+    _run(["gcc", "-O3", "-fPIC", "-shared", "-ffp-contract=off", "-std=c11",
+          os.path.join(ROOT, "synth", "csrc", "synth_host.c"), "-o", tmp])
+    os.replace(tmp, SYNTH_HOST_LIB)
+    return SYNTH_HOST_LIB
+
+
+def build_peaks() -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    obj = os.path.join(BUILD, "peaks.o")
+    _compile(os.path.join(PKG, "peaks", "peaks.hip"), obj, ["-I", os.path.join(ROOT, "include")])
+    _link([obj], PEAKS_LIB)
+    return PEAKS_LIB
+
+
 def build_all(verbose=False):
-    return build_layer(verbose), build_synth()
+    return build_layer(verbose), build_synth(), build_synth_host(), build_peaks()
 
 
 if __name__ == "__main__":

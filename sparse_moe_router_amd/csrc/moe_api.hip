@@ -36,6 +36,32 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// Byte ranges of one call's buffers.  Every output range must be disjoint
+// from every input range and from every other output range.
+struct Region {
+  const void* p;
+  size_t n;
+};
+struct Regions {
+  Region in[8], out[12];
+  int nin = 0, nout = 0;
+  void input(const void* p, size_t n) {
+    if (p && n) in[nin++] = Region{p, n};
+  }
+  void output(const void* p, size_t n) {
+    if (p && n) out[nout++] = Region{p, n};
+  }
+  bool disjoint() const {
+    for (int i = 0; i < nout; ++i) {
+      for (int j = 0; j < nin; ++j)
+        if (overlap(out[i].p, out[i].n, in[j].p, in[j].n)) return false;
+      for (int j = i + 1; j < nout; ++j)
+        if (overlap(out[i].p, out[i].n, out[j].p, out[j].n)) return false;
+    }
+    return true;
+  }
+};
+
 }  // namespace
 
 bool make_plan(Plan* p, int64_t M, int H, int E, int I, int Is, int k, bool gemv) {
@@ -120,10 +146,24 @@ moe_status_t check_desc(const moe_desc_t* d, int top_k, bool* gemv) {
 
 moe_status_t check_routing(const moe_routing_t* r) {
   if (!r) return MOE_OK;
-  const void* ps[] = {r->topk_ids, r->topk_w, r->logits, r->counts, r->offsets, r->perm};
+  const void* ps[] = {r->topk_ids, r->topk_w, r->logits, r->counts, r->offsets, r->perm, r->tiles, r->num_tiles};
   for (const void* p : ps)
     if (p && !aligned(p, 4)) return MOE_ERR_MISALIGNED;
   return MOE_OK;
+}
+
+// The routing outputs' byte ranges.
+void routing_regions(Regions* rg, const moe_routing_t* r, int64_t M, int E, int k, int64_t max_tiles) {
+  if (!r) return;
+  const size_t A = (size_t)M * k;
+  rg->output(r->topk_ids, A * 4);
+  rg->output(r->topk_w, A * 4);
+  rg->output(r->logits, (size_t)M * E * 4);
+  rg->output(r->counts, (size_t)E * 4);
+  rg->output(r->offsets, (size_t)(E + 1) * 4);
+  rg->output(r->perm, A * 4);
+  rg->output(r->tiles, (size_t)max_tiles * sizeof(Tile));
+  rg->output(r->num_tiles, 4);
 }
 
 template <class T>
@@ -169,6 +209,8 @@ moe_status_t run_routing_grouped(const Plan& p, const moe_desc_t* d, const void*
   int32_t* counts = (r && r->counts) ? r->counts : ws_ptr<int32_t>(ws, p.counts);
   int32_t* offsets = (r && r->offsets) ? r->offsets : ws_ptr<int32_t>(ws, p.offsets);
   int32_t* perm = (r && r->perm) ? r->perm : ws_ptr<int32_t>(ws, p.perm);
+  Tile* tiles = (r && r->tiles) ? (Tile*)r->tiles : ws_ptr<Tile>(ws, p.tiles);
+  int32_t* ntiles = (r && r->num_tiles) ? r->num_tiles : ws_ptr<int32_t>(ws, p.ntiles);
   hipError_t e;
   uint64_t* cmask = ws_ptr<uint64_t>(ws, p.cmask);
   if ((e = tr.run(MOE_K_ROUTER_SCORES, [&](const Launch& lc) {
@@ -179,8 +221,8 @@ moe_status_t run_routing_grouped(const Plan& p, const moe_desc_t* d, const void*
   if ((e = tr.run(MOE_K_TOPK, [&](const Launch& lc) { return launch_topk(L, ids, w, cmask, p.M, p.E, p.k, lc); })) != hipSuccess)
     return hip_fail(e);
   if ((e = tr.run(MOE_K_ROUTE_SCAN, [&](const Launch& lc) {
-         return launch_route_scan(cmask, ws_ptr<int32_t>(ws, p.cbase), counts, offsets, ws_ptr<Tile>(ws, p.tiles),
-                                  ws_ptr<int32_t>(ws, p.ntiles), p.M, p.E, p.k, p.shared, lc);
+         return launch_route_scan(cmask, ws_ptr<int32_t>(ws, p.cbase), counts, offsets, tiles, ntiles, p.M, p.E,
+                                  p.k, p.shared, lc);
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = tr.run(MOE_K_ROUTE_SCATTER, [&](const Launch& lc) {
@@ -203,6 +245,14 @@ size_t moe_workspace_size(const moe_desc_t* d, int top_k) {
   return p.total;
 }
 
+int64_t moe_block_map_capacity(const moe_desc_t* d, int top_k) {
+  bool gemv = false;
+  if (check_desc(d, top_k, &gemv) != MOE_OK) return 0;
+  Plan p;
+  if (!make_plan(&p, d->M, d->H, d->E, d->I, d->I_shared, top_k, false)) return 0;
+  return p.max_tiles;
+}
+
 }  // extern "C"
 
 namespace {
@@ -216,7 +266,7 @@ struct Weights {
 };
 
 moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router_w, const Weights& wt, int top_k,
-                          void* out, void* workspace, size_t workspace_bytes, void* stream,
+                          void* out, void* workspace, size_t workspace_bytes, hipStream_t stream,
                           const moe_routing_t* routing, moe_trace_t* trace) {
   bool gemv = false;
   moe_status_t st = check_desc(d, top_k, &gemv);
@@ -237,8 +287,6 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   }
   if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(out, 16)) return MOE_ERR_MISALIGNED;
   if ((st = check_routing(routing)) != MOE_OK) return st;
-  const size_t xbytes = (size_t)d->M * d->H * 2;
-  if (overlap(x, xbytes, out, xbytes)) return MOE_ERR_INVALID_ARG;
   if (d->M == 0) return MOE_OK;
   Plan p;
   if (!make_plan(&p, d->M, d->H, d->E, d->I, d->I_shared, top_k, gemv)) return MOE_ERR_UNSUPPORTED_SHAPE;
@@ -246,13 +294,33 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   if (!workspace) return MOE_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return MOE_ERR_MISALIGNED;
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (overlap(workspace, p.total, out, xbytes) || overlap(workspace, p.total, x, xbytes))
-    return MOE_ERR_INVALID_ARG;
+  {
+    // outputs (out, workspace, routing buffers) disjoint from the inputs and from each other
+    Regions rg;
+    const size_t xbytes = (size_t)d->M * d->H * 2;
+    const size_t eel = (size_t)d->E * 3 * d->I * d->H, sel = (size_t)3 * d->I_shared * d->H;
+    rg.input(x, xbytes);
+    rg.input(router_w, (size_t)d->E * d->H * 2);
+    rg.input(d->router_bias, (size_t)d->E * 4);
+    if (wt.q4) {
+      rg.input(wt.eq.codes, eel / 2);
+      rg.input(wt.eq.groups, eel / 16);
+      rg.input(wt.sq.codes, sel / 2);
+      rg.input(wt.sq.groups, sel / 16);
+    } else {
+      rg.input(wt.ew, eel * 2);
+      rg.input(wt.sw, sel * 2);
+    }
+    rg.output(out, xbytes);
+    rg.output(workspace, p.total);
+    routing_regions(&rg, routing, d->M, d->E, top_k, p.max_tiles);
+    if (!rg.disjoint()) return MOE_ERR_INVALID_ARG;
+  }
 
   if (trace && (trace->capacity < 0 || trace->count < 0 ||
                 (trace->capacity > 0 && (!trace->begin || !trace->end))))
     return MOE_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   Tracer tr{trace, s};
   const uint16_t* xb = (const uint16_t*)x;
   hipError_t e;
@@ -335,7 +403,7 @@ extern "C" {
 moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const void* router_w,
                                       const void* expert_w, const void* shared_w, int top_k,
                                       void* out, void* workspace, size_t workspace_bytes,
-                                      void* stream, const moe_routing_t* routing,
+                                      hipStream_t stream, const moe_routing_t* routing,
                                       moe_trace_t* trace) {
   Weights wt{};
   wt.q4 = false;
@@ -346,7 +414,7 @@ moe_status_t moe_layer_forward_traced(const moe_desc_t* d, const void* x, const 
 
 moe_status_t moe_layer_forward_q4(const moe_desc_t* d, const void* x, const void* router_w,
                                   const moe_q4_t* experts, const moe_q4_t* shared, int top_k, void* out,
-                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
                                   const moe_routing_t* routing, moe_trace_t* trace) {
   if (!experts) return MOE_ERR_INVALID_ARG;
   Weights wt{};
@@ -358,14 +426,14 @@ moe_status_t moe_layer_forward_q4(const moe_desc_t* d, const void* x, const void
 
 moe_status_t moe_layer_forward(const moe_desc_t* d, const void* x, const void* router_w,
                                const void* expert_w, const void* shared_w, int top_k, void* out,
-                               void* workspace, size_t workspace_bytes, void* stream,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream,
                                const moe_routing_t* routing) {
   return moe_layer_forward_traced(d, x, router_w, expert_w, shared_w, top_k, out, workspace,
                                   workspace_bytes, stream, routing, nullptr);
 }
 
 moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w, int top_k,
-                       void* workspace, size_t workspace_bytes, void* stream,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream,
                        const moe_routing_t* routing) {
   bool gemv = false;
   moe_status_t st = check_desc(d, top_k, &gemv);
@@ -379,7 +447,16 @@ moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w,
   if (!workspace) return MOE_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return MOE_ERR_MISALIGNED;
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  hipStream_t s = (hipStream_t)stream;
+  {
+    Regions rg;
+    rg.input(x, (size_t)d->M * d->H * 2);
+    rg.input(router_w, (size_t)d->E * d->H * 2);
+    rg.input(d->router_bias, (size_t)d->E * 4);
+    rg.output(workspace, p.total);
+    routing_regions(&rg, routing, d->M, d->E, top_k, p.max_tiles);
+    if (!rg.disjoint()) return MOE_ERR_INVALID_ARG;
+  }
+  hipStream_t s = stream;
   if (gemv) {
     Plan q = p;  // selection only: no shared rows, no expert rows
     q.shared = false;
@@ -410,7 +487,7 @@ moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w,
   return run_routing_grouped(p, d, x, router_w, workspace, routing, s, none);
 }
 
-moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void* src, void* dst, void* stream) {
+moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void* src, void* dst, hipStream_t stream) {
   if (nblocks < 0 || !src || !dst) return MOE_ERR_INVALID_ARG;
   if (H < 64 || H > 16384 || H % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (I < 64 || I > 16384 || I % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
@@ -418,7 +495,7 @@ moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void*
   const size_t bytes = (size_t)nblocks * 3 * I * H * 2;
   if (overlap(src, bytes, dst, bytes)) return MOE_ERR_INVALID_ARG;
   if (nblocks == 0) return MOE_OK;
-  const hipError_t e = launch_tile_weights((const uint16_t*)src, (uint16_t*)dst, nblocks, H, I, (hipStream_t)stream);
+  const hipError_t e = launch_tile_weights((const uint16_t*)src, (uint16_t*)dst, nblocks, H, I, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

@@ -23,7 +23,7 @@ FLAG_TILED_WEIGHTS = 0x4
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_MISALIGNED", 5: "MOE_ERR_HIP"}
 
-EXPORTS = ("moe_workspace_size", "moe_layer_forward", "moe_route", "moe_layer_forward_traced",
+EXPORTS = ("moe_workspace_size", "moe_block_map_capacity", "moe_layer_forward", "moe_route", "moe_layer_forward_traced",
            "moe_layer_forward_q4", "moe_tile_weights", "moe_status_string", "moe_last_hip_error")
 
 # moe_kernel_t
@@ -40,7 +40,8 @@ class MoeDesc(ctypes.Structure):
 
 class MoeRouting(ctypes.Structure):
     _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("logits", ctypes.c_void_p),
-                ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p)]
+                ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+                ("tiles", ctypes.c_void_p), ("num_tiles", ctypes.c_void_p)]
 
 
 class MoeTrace(ctypes.Structure):
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         L.moe_workspace_size.argtypes = [ctypes.POINTER(MoeDesc), ctypes.c_int]
         L.moe_workspace_size.restype = sz
+        L.moe_block_map_capacity.argtypes = [ctypes.POINTER(MoeDesc), ctypes.c_int]
+        L.moe_block_map_capacity.restype = ctypes.c_int64
         L.moe_layer_forward.argtypes = [ctypes.POINTER(MoeDesc), vp, vp, vp, vp, ctypes.c_int, vp, vp, sz, vp,
                                         ctypes.POINTER(MoeRouting)]
         L.moe_layer_forward.restype = ctypes.c_int
@@ -104,6 +107,12 @@ def workspace_size(M, H, E, I, I_shared, top_k, flags=0, with_bias=False) -> int
     return int(lib().moe_workspace_size(ctypes.byref(d), int(top_k)))
 
 
+def block_map_capacity(M, H, E, I, I_shared, top_k, flags=0) -> int:
+    """Tiles the routing output ``tiles`` ([capacity, 4] int32) must hold."""
+    d = make_desc(M, H, E, I, I_shared, flags)
+    return int(lib().moe_block_map_capacity(ctypes.byref(d), int(top_k)))
+
+
 def _ptr(t: torch.Tensor, dtype, name) -> int:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
@@ -119,11 +128,16 @@ def _ptr(t: torch.Tensor, dtype, name) -> int:
 _ws_cache: dict = {}
 
 
-def _workspace(nbytes: int, device) -> torch.Tensor:
-    key = (device.type, device.index)
+def _workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """A cached workspace for calls that pass none: one buffer per (device, stream), so calls on
+    different streams never share one (calls sharing a workspace must be ordered, and calls on one
+    stream are).  The buffer is allocated on `stream`; when it grows, the old buffer goes back to
+    torch's caching allocator, which reuses it only after the work queued on that stream so far."""
+    key = (device.type, device.index, stream.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 
@@ -132,13 +146,18 @@ def _routing_struct(routing: Optional[dict]) -> Optional[MoeRouting]:
     if not routing:
         return None
     spec = {"topk_ids": torch.int32, "topk_w": torch.float32, "logits": torch.float32,
-            "counts": torch.int32, "offsets": torch.int32, "perm": torch.int32}
+            "counts": torch.int32, "offsets": torch.int32, "perm": torch.int32, "tiles": torch.int32,
+            "num_tiles": torch.int32}
     r = MoeRouting()
     for k, v in routing.items():
         if k not in spec:
             raise KeyError(f"unknown routing output {k}")
         setattr(r, k, _ptr(v, spec[k], k))
     return r
+
+
+def _stream_obj(stream, device):
+    return torch.cuda.current_stream(device) if stream is None else stream
 
 
 def _stream(stream) -> int:
@@ -161,6 +180,7 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, expert_w: torch.Tensor,
             trace: Optional[MoeTrace] = None) -> torch.Tensor:
     """moe_layer_forward (moe_layer_forward_traced when a trace is given).  x [M,H] bf16; router_w [E,H] bf16; expert_w [E, 3*I*H] bf16
     (gate [I,H], up [I,H], down [H,I] per expert); shared_w [3*I_s*H] bf16 or None."""
+    _ptr(x, torch.bfloat16, "x")  # a CPU tensor fails here, before any stream or workspace is touched
     M, H = x.shape
     E = router_w.shape[0]
     I = expert_w.numel() // (3 * E * H)
@@ -171,7 +191,7 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, expert_w: torch.Tensor,
     need = lib().moe_workspace_size(ctypes.byref(d), int(top_k))
     if need == 0 and M > 0:
         raise MoeError(2, "moe_workspace_size rejected the shapes")
-    ws = workspace if workspace is not None else _workspace(need, x.device)
+    ws = workspace if workspace is not None else _workspace(need, x.device, _stream_obj(stream, x.device))
     r = _routing_struct(routing)
     args = (ctypes.byref(d), _ptr(x, torch.bfloat16, "x"), _ptr(router_w, torch.bfloat16, "router_w"),
             _ptr(expert_w, torch.bfloat16, "expert_w"),
@@ -194,6 +214,7 @@ def forward_q4(x: torch.Tensor, router_w: torch.Tensor, codes: torch.Tensor, sca
     """moe_layer_forward_q4.  codes uint8 [E, 3*I*H/2] (two 4-bit codes per byte, low nibble first);
     scale_bias int32 [E, 3*I*H/64] (bf16 scale in the low half, bf16 bias in the high half of each
     word); shared_codes / shared_scale_bias the same for the shared expert (E = 1), or None."""
+    _ptr(x, torch.bfloat16, "x")  # a CPU tensor fails here, before any stream or workspace is touched
     M, H = x.shape
     E = router_w.shape[0]
     I = codes.numel() * 2 // (3 * E * H)
@@ -208,7 +229,7 @@ def forward_q4(x: torch.Tensor, router_w: torch.Tensor, codes: torch.Tensor, sca
     need = lib().moe_workspace_size(ctypes.byref(d), int(top_k))
     if need == 0 and M > 0:
         raise MoeError(2, "moe_workspace_size rejected the shapes")
-    ws = workspace if workspace is not None else _workspace(need, x.device)
+    ws = workspace if workspace is not None else _workspace(need, x.device, _stream_obj(stream, x.device))
     r = _routing_struct(routing)
     ex = MoeQ4(_ptr(codes, torch.uint8, "codes"), _ptr(scale_bias, torch.int32, "scale_bias"))
     sh = None if shared_codes is None else MoeQ4(_ptr(shared_codes, torch.uint8, "shared_codes"),
@@ -241,13 +262,14 @@ def route(x: torch.Tensor, router_w: torch.Tensor, top_k: int, routing: dict,
           router_bias: Optional[torch.Tensor] = None, flags: int = 0, I: int = 64, I_shared: int = 0,
           workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """moe_route: routing decisions only, written into the tensors of ``routing``."""
+    _ptr(x, torch.bfloat16, "x")  # a CPU tensor fails here, before any stream or workspace is touched
     M, H = x.shape
     E = router_w.shape[0]
     d = make_desc(M, H, E, I, I_shared, flags, router_bias)
     need = lib().moe_workspace_size(ctypes.byref(d), int(top_k))
     if need == 0 and M > 0:
         raise MoeError(2, "moe_workspace_size rejected the shapes")
-    ws = workspace if workspace is not None else _workspace(need, x.device)
+    ws = workspace if workspace is not None else _workspace(need, x.device, _stream_obj(stream, x.device))
     r = _routing_struct(routing)
     st = lib().moe_route(ctypes.byref(d), _ptr(x, torch.bfloat16, "x"), _ptr(router_w, torch.bfloat16, "router_w"),
                          int(top_k), _ptr(ws, torch.uint8, "workspace"), ws.numel(), _stream(stream),

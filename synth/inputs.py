@@ -41,8 +41,10 @@ low half.
 """
 from __future__ import annotations
 
+import ctypes
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -135,9 +137,40 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def normal_bf16(key: int, start: int, n: int, sigma: float) -> np.ndarray:
-    """Elements of stream ``key`` rounded to bfloat16 (returned as uint16 bits)."""
+def normal_bf16_np(key: int, start: int, n: int, sigma: float) -> np.ndarray:
+    """Elements of stream ``key`` rounded to bfloat16 (uint16 bits): the NumPy definition."""
     return f32_to_bf16_bits(normal_f32(key, start, n, sigma))
+
+
+_HOST_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsynth_host.so")
+_host = None
+
+
+def _host_lib():
+    """The C twin of ``normal_bf16_np`` (``synth/csrc/synth_host.c``), or None if not built."""
+    global _host
+    if _host is None:
+        if not os.path.exists(_HOST_LIB):
+            return None
+        L = ctypes.CDLL(_HOST_LIB)
+        L.synth_host_normal_bf16.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                             ctypes.c_float]
+        L.synth_host_normal_bf16.restype = None
+        _host = L
+    return _host
+
+
+def normal_bf16(key: int, start: int, n: int, sigma: float) -> np.ndarray:
+    """Elements of stream ``key`` rounded to bfloat16 (returned as uint16 bits).
+
+    Computed by the C twin when it is built (bit-identical, about 100x faster;
+    ctypes releases the GIL, so threads run it in parallel), else by NumPy."""
+    L = _host_lib()
+    if L is None or n == 0:
+        return normal_bf16_np(key, start, n, sigma)
+    out = np.empty(n, dtype=np.uint16)
+    L.synth_host_normal_bf16(out.ctypes.data, key & MASK64, start, n, ctypes.c_float(float(scale_f32(sigma))))
+    return out
 
 
 # ----------------------------------------------------------------------------

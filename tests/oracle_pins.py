@@ -421,6 +421,27 @@ def check_q4_layer_is_dense_on_dequantised(O):
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------ the parity metric
+
+def check_rel_err_per_token(O):
+    """The per-token error metric used by every output comparison, on values computed by hand:
+    max over a row of |y - ref| divided by max over the same row of |ref|.
+
+    Row 0 is negative-dominant: its largest |ref| is 10 at a negative entry, while its
+    largest ref is 4; |y - ref| = (0.5, 1, 3), so the value is 3 / 10.  Row 1:
+    |y - ref| = (0, 0.25, 0) over max |ref| = 1.  Row 2 is all zeros on both sides and
+    must give 0, not NaN.  A per-column reduction, a mean for the max, a dropped absolute
+    value or the denominator taken from y each change one of these numbers (or the shape).
+    """
+    ref = np.array([[2.0, -10.0, 4.0], [1.0, 0.5, -0.25], [0.0, 0.0, 0.0]])
+    y = np.array([[2.5, -9.0, 1.0], [1.0, 0.25, -0.25], [0.0, 0.0, 0.0]])
+    got = O.rel_err_per_token(y, ref)
+    assert got.shape == (3,), got.shape
+    assert got[0] == 3.0 / 10.0 and got[1] == 0.25 and got[2] == 0.0, got
+    # invariant: scaling both sides by a power of two leaves every row's value unchanged
+    assert np.array_equal(O.rel_err_per_token(8.0 * y, 8.0 * ref), got)
+
+
 ALL_CHECKS = [
     check_topk_bruteforce, check_zero_router, check_planted_router, check_router_bias,
     check_k_equals_E_is_softmax, check_k1_weight_one, check_weights_closed_form,
@@ -429,5 +450,5 @@ ALL_CHECKS = [
     check_planted_combine, check_dense_equals_grouped, check_token_permutation,
     check_chunk_invariance, check_down_linearity, check_subset_tokens, check_forced_routing,
     check_q4_hand_example, check_q4_groups_and_affinity, check_q4_bf16_decoding,
-    check_q4_layer_is_dense_on_dequantised,
+    check_q4_layer_is_dense_on_dequantised, check_rel_err_per_token,
 ]

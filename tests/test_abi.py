@@ -71,6 +71,7 @@ FAKE = 0x7F0000000000  # never dereferenced: every call below fails its checks f
 
 def fwd(d, k=2, x=FAKE, r=FAKE + (1 << 24), ex=FAKE + (2 << 24), sh=FAKE + (3 << 24), out=FAKE + (4 << 24),
         ws=FAKE + (5 << 24), wsb=1 << 40, routing=None):
+    # x, router, experts, shared, out and workspace 16 MiB apart (each smaller at _desc's shapes)
     return moe.lib().moe_layer_forward(ctypes.byref(d), x, r, ex, sh, k, out, ws, wsb, None,
                                        None if routing is None else ctypes.byref(routing))
 
@@ -175,3 +176,82 @@ def test_tiled_flag_and_tile_weights_arguments():
     assert tw(2, 256, 128, FAKE, dst + 4, None) == MISALIGNED
     assert tw(2, 256, 128, FAKE, FAKE + 1024, None) == INVALID  # dst overlaps src
     assert tw(0, 256, 128, FAKE, dst, None) == OK  # no blocks: nothing enqueued
+
+
+def _routing(**kw):
+    r = moe.MoeRouting()
+    for k, v in kw.items():
+        setattr(r, k, v)
+    return r
+
+
+def test_outputs_must_not_overlap_inputs_or_each_other():
+    """moe_layer.h: out, the workspace and the routing buffers are disjoint from every input
+    (x, router, experts, shared expert, router bias) and from each other."""
+    d = _desc()
+    bias = FAKE + (6 << 24)
+    db = _desc(bias=bias)
+    # out over each input
+    assert fwd(d, out=FAKE + (1 << 24)) == INVALID            # router
+    assert fwd(d, out=FAKE + (2 << 24) + 4096) == INVALID     # inside the expert weights
+    assert fwd(d, out=FAKE + (3 << 24) + 256) == INVALID      # shared expert
+    assert fwd(db, out=bias - 64) == INVALID                  # router bias
+    # workspace over each input
+    assert fwd(d, ws=FAKE + (1 << 24)) == INVALID
+    assert fwd(d, ws=FAKE + (2 << 24) + (1 << 20)) == INVALID
+    assert fwd(d, ws=FAKE + (3 << 24)) == INVALID
+    # workspace over out
+    assert fwd(d, ws=FAKE + (4 << 24) + 256) == INVALID
+    # routing buffers over inputs, out, the workspace, each other
+    assert fwd(d, routing=_routing(topk_ids=FAKE + 64)) == INVALID
+    assert fwd(d, routing=_routing(logits=FAKE + (2 << 24))) == INVALID
+    assert fwd(d, routing=_routing(perm=FAKE + (4 << 24))) == INVALID
+    assert fwd(d, routing=_routing(counts=FAKE + (5 << 24) + 1024)) == INVALID
+    assert fwd(db, routing=_routing(topk_w=bias)) == INVALID
+    assert fwd(d, routing=_routing(topk_ids=FAKE + (7 << 24), topk_w=FAKE + (7 << 24) + 64)) == INVALID
+    assert fwd(d, routing=_routing(tiles=FAKE + (7 << 24), num_tiles=FAKE + (7 << 24) + 16)) == INVALID
+    # 4-bit weights: out over the codes or the group words
+    assert fwd_q4(d, out=FAKE + (2 << 24) + 512) == INVALID
+    assert fwd_q4(d, out=FAKE + (8 << 24)) == INVALID
+    assert fwd_q4(d, out=FAKE + (9 << 24)) == INVALID
+    # routing only: outputs over x or the router
+    L = moe.lib()
+    for r in (_routing(topk_ids=FAKE), _routing(logits=FAKE + (1 << 24) + 128)):
+        assert L.moe_route(ctypes.byref(d), FAKE, FAKE + (1 << 24), 2, FAKE + (5 << 24), 1 << 40, None,
+                           ctypes.byref(r)) == INVALID
+    assert L.moe_route(ctypes.byref(d), FAKE, FAKE + (1 << 24), 2, FAKE + 4096, 1 << 40, None,
+                       ctypes.byref(_routing(topk_ids=FAKE + (7 << 24)))) == INVALID  # workspace over x
+
+
+def test_block_map_capacity():
+    L = moe.lib()
+    cap = lambda d, k: L.moe_block_map_capacity(ctypes.byref(d), k)
+    # ceil(M*k / 256) + E (+ ceil(M / 256) with a shared expert), whatever path the shapes select
+    assert cap(_desc(M=4096, H=2048, E=256, I=512, Is=512), 8) == 128 + 256 + 16
+    assert cap(_desc(M=300, E=16, Is=0), 4) == 5 + 16
+    assert cap(_desc(M=1, E=16), 2) == 1 + 16 + 1
+    assert cap(_desc(H=100), 2) == 0 and cap(_desc(), 0) == 0
+
+
+def test_header_compiles_as_c_and_with_hip():
+    """The header is plain C11 (no HIP include needed) and agrees with HIP's own declaration of
+    hipStream_t when both are included."""
+    import shutil
+    import subprocess
+    import tempfile
+    gcc, gxx = shutil.which("gcc"), shutil.which("g++")
+    if not gcc or not gxx:
+        pytest.skip("no host compiler")
+    inc = os.path.join(ROOT, "include")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "use.c")
+        with open(c, "w") as f:
+            f.write('#include "moe_layer.h"\nint main(void) { moe_desc_t d = {0}; hipStream_t s = 0;\n'
+                    '  return (int)moe_workspace_size(&d, 1) + (s != 0); }\n')
+        subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-I", inc, "-c", c, "-o", c + ".o"], check=True)
+        cc = os.path.join(d, "use.cc")
+        with open(cc, "w") as f:
+            f.write('#include <hip/hip_runtime_api.h>\n#include "moe_layer.h"\n'
+                    'int main() { hipStream_t s = nullptr; return s != nullptr; }\n')
+        subprocess.run([gxx, "-std=c++17", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+                        "-I", inc, "-c", cc, "-o", cc + ".o"], check=True)

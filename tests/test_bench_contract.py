@@ -43,12 +43,24 @@ def test_gateup_roofline_bound_at_prefill(q4, bound):
     """At M = 4096 with every expert non-empty the bf16 gate/up GEMM needs longer on HBM than on
     MFMA at datasheet peaks (1.13 GB vs 155 GFLOP), the 4-bit one longer on MFMA (0.36 GB)."""
     w = S.PREFILL
-    r = bench.gateup_roofline({"gemm_gateup": [0.25, 0.25]}, w, w.M, w.E, q4)
+    peaks = {"hbm_gbs": 6400.0, "mfma_tflops": 2000.0}
+    r = bench.gateup_roofline({"gemm_gateup": [0.25, 0.25]}, w, w.M, w.E, q4, peaks)
     assert r["bound"] == bound and r["avg_us"] == 250.0
     flops = (w.M * w.k + w.M) * 2 * w.I * w.H * 2
     wb = 0.5625 if q4 else 2
-    nbytes = int((w.E + 1) * 2 * w.I * w.H * wb) + w.M * w.H * 2 + (w.M * w.k + w.M) * w.I * 2
+    # algorithmic bytes only: gate/up weights of the non-empty experts + the shared expert, x once
+    nbytes = int((w.E + 1) * 2 * w.I * w.H * wb) + w.M * w.H * 2
+    assert r["bytes_per_launch"] == nbytes and r["flops_per_launch"] == flops
     if bound == "hbm":
         assert r["frac"] == pytest.approx(nbytes / 250e-6 / 1e9 / bench.HBM_PEAK_GBS, abs=1e-4)
+        assert r["frac_measured"] == pytest.approx(nbytes / 250e-6 / 1e9 / 6400.0, abs=1e-4)
     else:
         assert r["frac"] == pytest.approx(flops / 250e-6 / 1e12 / bench.BF16_PEAK_TFLOPS, abs=1e-4)
+        assert r["frac_measured"] == pytest.approx(flops / 250e-6 / 1e12 / 2000.0, abs=1e-4)
+
+
+@pytest.mark.parametrize("total", [1, 4, 5, 20, 23, 200])
+def test_rounds_cover_exactly_the_steps(total):
+    """The timed steps are split into at most 5 rounds that together run exactly `total` steps."""
+    sizes = bench.round_sizes(total)
+    assert sum(sizes) == total and len(sizes) == min(5, total) and max(sizes) - min(sizes) <= 1

@@ -1,0 +1,105 @@
+"""The grouped GEMMs' block map, read back through the routing outputs.
+
+"Optimizing on-device inference for Apple Silicon", section "Keep expert
+routing on the GPU": after the histogram, prefix scan and scatter, a block
+map lists the fixed-size blocks of rows the grouped matrix multiplication
+works on.  Here a group of c rows is cut into ceil(c / 256) tiles (all of
+256 rows but the last), routed groups in expert order, then the shared
+expert's tokens in order; the tile count is the sum of ceil(c_g / 256) plus
+ceil(M / 256), and every row of every group lies in exactly one tile."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from gpu_util import HostLayer, device_layer, moe, rand_case, routing_buffers, upload, S
+
+pytestmark = pytest.mark.gpu
+TILE = 256
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    moe.lib()
+    yield
+
+
+def expected_tiles(counts, offsets, M, shared):
+    E = len(counts)
+    want = []
+    for g in range(E):
+        for r0 in range(0, int(counts[g]), TILE):
+            want.append((g, r0, min(TILE, int(counts[g]) - r0), int(offsets[g]) + r0))
+    if shared:
+        for r0 in range(0, M, TILE):
+            want.append((E, r0, min(TILE, M - r0), r0))
+    return np.array(want, dtype=np.int64).reshape(-1, 4)
+
+
+def run_blockmap(x, r, ex, sh, k, bias=None, I=None, Is=None):
+    M, H = x.shape
+    E = r.shape[0]
+    cap = moe.block_map_capacity(M, H, E, I, Is, k, flags=moe.FLAG_FORCE_GEMM)
+    rb = routing_buffers(M, E, k)
+    rb["tiles"] = torch.full((cap, 4), -1, dtype=torch.int32, device="cuda")
+    rb["num_tiles"] = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    moe.forward(x, r, ex, sh, k, routing=rb, router_bias=bias, flags=moe.FLAG_FORCE_GEMM)
+    torch.cuda.synchronize()
+    return {n: t.cpu().numpy() for n, t in rb.items()}, cap
+
+
+def check_blockmap(g, cap, M, k, shared):
+    counts, offsets = g["counts"], g["offsets"]
+    E = len(counts)
+    assert counts.sum() == M * k and offsets[E] == M * k
+    n = int(g["num_tiles"][0])
+    want = expected_tiles(counts, offsets, M, shared)
+    assert n == len(want) == int(np.sum((counts + TILE - 1) // TILE)) + (-(-M // TILE) if shared else 0)
+    assert n <= cap
+    got = g["tiles"][:n].astype(np.int64)
+    assert np.array_equal(got, want), "block map differs"
+    # every row of every group in exactly one tile
+    cover = np.zeros(M * k + (M if shared else 0), dtype=np.int64)
+    for gg, r0, rows, pos0 in got:
+        assert 0 < rows <= TILE
+        base = 0 if gg < E else M * k
+        cover[base + pos0: base + pos0 + rows] += 1
+    assert (cover == 1).all()
+    return n
+
+
+def test_block_map_uniform_prefill():
+    w = S.PREFILL
+    x, r, ex, sh = device_layer(w)
+    g, cap = run_blockmap(x, r, ex, sh, w.k, I=w.I, Is=w.I_shared)
+    n = check_blockmap(g, cap, w.M, w.k, True)
+    print("uniform: tiles", n, "groups", (g["counts"] > 0).sum())
+
+
+def test_block_map_skewed_prefill():
+    w = S.SKEW
+    hl = HostLayer(w)
+    x, r, ex, sh = device_layer(w)
+    g, cap = run_blockmap(x, r, ex, sh, w.k, bias=torch.from_numpy(hl.bias).cuda(), I=w.I, Is=w.I_shared)
+    assert g["counts"].max() > 1000
+    n = check_blockmap(g, cap, w.M, w.k, True)
+    # the routing the block map was built from is the oracle's (counts bit-exact; near-ties aside)
+    ids = O.topk_ids(O.selection_logits(O.router_logits(hl.x(0, w.M), hl.router, hl.bias)), w.k)
+    flagged = O.near_tie_flags(O.selection_logits(O.router_logits(hl.x(0, w.M), hl.router, hl.bias)), w.k)
+    if not flagged.any():
+        assert np.array_equal(g["counts"], O.route_tables(ids, w.E)[0])
+    print("skew: tiles", n, "max group", g["counts"].max())
+
+
+@pytest.mark.parametrize("M,E,k,shared", [(520, 32, 4, True), (600, 1, 1, False), (1, 16, 2, True),
+                                          (257, 8, 8, True), (4100, 4, 2, False)])
+def test_block_map_hot_and_edge(M, E, k, shared):
+    """A bias that sends every token to expert 5 first (or a single expert), one row, k = E, and
+    groups just over a multiple of the tile height."""
+    x, r, ex, s, bias = rand_case(M, 128, E, k, 64, 64 if shared else 0, seed=M, hot=5 if E > 5 else None)
+    g, cap = run_blockmap(upload(x), upload(r), upload(ex), upload(s) if shared else None, k,
+                          bias=None if bias is None else torch.from_numpy(bias).cuda(), I=64, Is=64 if shared else 0)
+    check_blockmap(g, cap, M, k, shared)
+    if E > 5:
+        assert g["counts"][5] == M

@@ -140,3 +140,30 @@ def test_traced_call_matches_and_records_kernels(kind, M):
             assert 0.0 <= hip.elapsed_ms(begin[i], end[i]) < 1000.0
         hip.destroy(begin)
         hip.destroy(end)
+
+
+def test_two_streams_cached_workspaces():
+    """Calls that pass no workspace take the binding's cached one, one per (device, stream): calls
+    interleaved on two streams, some of them growing their stream's buffer, give the bits of the
+    same calls made one after another with their own workspaces."""
+    r, wts, flags = _weights("bf16", seed=6)
+    Ms = [8, 300, 40, 700, 1]
+    xs = [upload(np.random.default_rng(40 + i).standard_normal((M, H)).astype(np.float32)) for i, M in enumerate(Ms)]
+    refs = []
+    for x in xs:
+        ws = torch.empty(moe.workspace_size(x.shape[0], H, E, I, IS, K), dtype=torch.uint8, device="cuda")
+        refs.append(_call(x, r, wts, flags, torch.empty_like(x), ws).clone())
+    torch.cuda.synchronize()
+    moe._ws_cache.clear()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for i, x in enumerate(xs):
+        for s in (sa, sb):
+            out = torch.empty_like(x)
+            _call(x, r, wts, flags, out, None, stream=s)
+            outs.append((i, out))
+    torch.cuda.synchronize()
+    for i, out in outs:
+        assert torch.equal(out.view(torch.int16), refs[i].view(torch.int16)), f"call {i}"
+    keys = [kk for kk in moe._ws_cache if kk[2] in (sa.cuda_stream, sb.cuda_stream)]
+    assert len(keys) == 2, keys

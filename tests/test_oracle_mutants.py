@@ -53,6 +53,11 @@ MUTANTS = [
      "q = q4_codes(packed).astype(np.int8).astype(np.float64) - 8.0 * (q4_codes(packed) > 7)"),
     ("q4_bf16_low_bits", "hi = (np.asarray(bits, dtype=np.uint64) & np.uint64(0xFFFF)).astype(np.uint32) << np.uint32(16)",
      "hi = (np.asarray(bits, dtype=np.uint64) & np.uint64(0xFFFF)).astype(np.uint32) << np.uint32(15)"),
+    ("rel_err_per_column", "num = np.abs(y - ref).max(axis=1)", "num = np.abs(y - ref).max(axis=0)"),
+    ("rel_err_mean_for_max", "num = np.abs(y - ref).max(axis=1)", "num = np.abs(y - ref).mean(axis=1)"),
+    ("rel_err_no_abs_numerator", "num = np.abs(y - ref).max(axis=1)", "num = (y - ref).max(axis=1)"),
+    ("rel_err_no_abs_denominator", "den = np.abs(ref).max(axis=1)", "den = ref.max(axis=1)"),
+    ("rel_err_denominator_from_y", "den = np.abs(ref).max(axis=1)", "den = np.abs(y).max(axis=1)"),
     ("drop_last_group_row", "pos = np.arange(offsets[e], offsets[e + 1])", "pos = np.arange(offsets[e], max(offsets[e], offsets[e + 1] - 1))"),
 ]
 

@@ -2,6 +2,9 @@
 the oracle: the oracle rebuilds every weight from its code and its group's
 scale and bias (dequant_q4) and runs the same layer in float64, on the
 seeded synthetic workloads (4-bit variant) and on the edge shapes."""
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -35,10 +38,19 @@ class HostLayerQ4:
     def x(self, row0, n):
         return f32(S.x_rows(self.w, row0, n, self.layer))
 
+    def _gen(self, e):
+        c, g = S.q4_expert(self.w, self.layer, e)
+        return O.unpack_expert(O.dequant_q4(c, g), self.w.I, self.w.H)
+
+    def prefetch(self, experts):
+        todo = sorted(set(int(e) for e in experts) - set(self._experts))
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+            for e, v in zip(todo, ex.map(self._gen, todo)):
+                self._experts[e] = v
+
     def expert(self, e):
         if e not in self._experts:
-            c, g = S.q4_expert(self.w, self.layer, e)
-            self._experts[e] = O.unpack_expert(O.dequant_q4(c, g), self.w.I, self.w.H)
+            self._experts[e] = self._gen(e)
         return self._experts[e]
 
     def oracle(self, x_host, tokens=None):
@@ -94,29 +106,35 @@ def test_q4_tiny_single_rows(flags):
 
 
 def test_q4_decode_full_shape():
+    """4-bit decode at full shape: 8 token rows (one call each) through all 40 layers."""
     w = S.DECODE
-    for layer, row in [(0, 0), (11, 5)]:
+    rows = (0, 9, 18, 27, 36, 45, 54, 63)
+    for layer in range(w.layers):
         hl = HostLayerQ4(w, layer)
-        x1 = bits_to_dev(S.x_rows(w, row, 1, layer))
         _, r, ex, esb, sh, ssb = SD.layer_tensors_q4(w, layer, x_rows=1)
-        g = run_q4(x1, r, ex, esb, sh, ssb, w.k)
+        gs = [run_q4(bits_to_dev(S.x_rows(w, row, 1, layer)), r, ex, esb, sh, ssb, w.k) for row in rows]
         del ex, esb
-        check(g, hl.oracle(hl.x(row, 1)), w.k, w.E, grouped=False, label=f"q4 decode layer {layer}")
+        g = {n: np.concatenate([one[n] for one in gs]) for n in gs[0]}
+        hl.prefetch(g["topk_ids"].ravel())
+        xh = np.concatenate([hl.x(row, 1) for row in rows])
+        check(g, hl.oracle(xh), w.k, w.E, grouped=False, label=f"q4 decode layer {layer}")
 
 
 @pytest.mark.parametrize("name", ["PREFILL", "SKEW"])
-def test_q4_prefill_full_sampled(name):
+def test_q4_prefill_full(name):
+    """Full-size 4-bit prefill: every token's routing and output against the oracle."""
     w = getattr(S, name)
     hl = HostLayerQ4(w)
     x, r, ex, esb, sh, ssb = SD.layer_tensors_q4(w)
     bias = None if hl.bias is None else torch.from_numpy(hl.bias).cuda()
     g = run_q4(x, r, ex, esb, sh, ssb, w.k, bias=bias)
     del ex, esb
-    rng = np.random.default_rng(17)
-    sample = sorted(set(rng.choice(w.M, 6, replace=False).tolist()) | {0, w.M - 1})
-    st = check(g, hl.oracle(hl.x(0, w.M), tokens=sample), w.k, w.E, rows=sample, label=f"q4 {name}")
+    xh = hl.x(0, w.M)
+    ids_o = O.topk_ids(O.selection_logits(O.router_logits(xh, hl.router, hl.bias)), w.k)
+    hl.prefetch(np.union1d(ids_o.ravel(), g["topk_ids"].ravel()))
+    st = check(g, hl.oracle(xh), w.k, w.E, label=f"q4 {name}")
     assert g["counts"].sum() == w.M * w.k
-    print(name, st)
+    print(name, "all tokens", st)
 
 
 def _q4_random(E, n, rng, sigma=0.02):

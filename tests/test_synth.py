@@ -87,3 +87,13 @@ def test_q4_generator():
     assert codes.size * 2 == S.TINY.expert_elems() and words.size * 64 == S.TINY.expert_elems()
     assert abs(wts.mean()) < 0.1 * S.TINY.w_sigma
     assert abs(wts.std() / S.TINY.w_sigma - 1) < 0.1
+
+
+def test_host_c_twin_matches_numpy():
+    """The C twin of the generator (used when built) gives the NumPy definition's bits."""
+    if S._host_lib() is None:
+        import pytest
+        pytest.skip("synth/libsynth_host.so not built")
+    for key, start, n, sigma in [(S.stream_key(1, 2, 3, 4), 0, 100_003, 0.02), (12345, 777, 4096, 1.0),
+                                 (S.x_key(S.PREFILL), 4095 * 2048, 2048, 1.0), (2 ** 64 - 1, 2 ** 40, 999, 0.5)]:
+        assert np.array_equal(S.normal_bf16(key, start, n, sigma), S.normal_bf16_np(key, start, n, sigma))
