@@ -254,6 +254,30 @@ moe_status_t moe_layer_forward_q4(const moe_desc_t* d, const void* x, const void
  * layer's shape rules.  Asynchronous on `stream` like the layer calls. */
 moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void* src, void* dst, hipStream_t stream);
 
+/* moe_layer_forward for callers that cannot allocate or pass device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same layer, arguments and results, with the workspace
+ * taken from a static per-device scratch array of the library instead of
+ * a caller buffer.  Nothing is allocated: no hipMalloc, hipFree or
+ * allocating library call.
+ *   - The scratch holds MOE_NOALLOC_SCRATCH_BYTES (64 MiB) on every
+ *     device the library runs on, for the life of the process; a call whose
+ *     moe_workspace_size() is larger returns MOE_ERR_WORKSPACE_TOO_SMALL and
+ *     enqueues nothing (at H=2048, E=256, top-8, I=512: up to about 1,400
+ *     rows on the grouped path; the decode and small-batch paths always fit).
+ *   - The scratch of the current device is used (hipGetDevice): make the
+ *     stream's device current.  The first call on a device looks up that
+ *     device's scratch address once (hipGetSymbolAddress); make that first
+ *     call outside graph capture.
+ *   - All calls on one device share its scratch and leave their contents in
+ *     it: calls that overlap in time on one device race (order them on one
+ *     stream, or synchronise them).  No result depends on what a previous
+ *     call left there. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_layer_forward_noalloc(const moe_desc_t* d, const void* x, const void* router_w,
+                                       const void* expert_w, const void* shared_w, int top_k, void* out,
+                                       hipStream_t stream, const moe_routing_t* routing);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t s);
 

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 #include "moe_layer.h"
 
@@ -257,6 +259,38 @@ int64_t moe_block_map_capacity(const moe_desc_t* d, int top_k) {
 
 namespace {
 
+// Static scratch of moe_layer_forward_noalloc: the workspace of callers that
+// cannot allocate.  Each device holds its own copy of this array for the
+// life of the process.  On the host its name is only a stand-in: the device
+// address of each device's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is passed on.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device); nullptr and *err set when the lookup fails.
+void* scratch_for_current_device(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // The expert weights of one call: bf16 blocks, or 4-bit codes + group words.
 struct Weights {
   bool q4;
@@ -267,7 +301,7 @@ struct Weights {
 
 moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router_w, const Weights& wt, int top_k,
                           void* out, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                          const moe_routing_t* routing, moe_trace_t* trace) {
+                          const moe_routing_t* routing, moe_trace_t* trace, bool use_scratch = false) {
   bool gemv = false;
   moe_status_t st = check_desc(d, top_k, &gemv);
   if (st != MOE_OK) return st;
@@ -291,9 +325,13 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   Plan p;
   if (!make_plan(&p, d->M, d->H, d->E, d->I, d->I_shared, top_k, gemv)) return MOE_ERR_UNSUPPORTED_SHAPE;
   p.tiled = (d->flags & MOE_FLAG_TILED_WEIGHTS) != 0;
-  if (!workspace) return MOE_ERR_INVALID_ARG;
-  if (!aligned(workspace, 256)) return MOE_ERR_MISALIGNED;
-  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (use_scratch) {
+    if (p.total > kScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;  // beyond the static scratch
+  } else {
+    if (!workspace) return MOE_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return MOE_ERR_MISALIGNED;
+    if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
   {
     // outputs (out, workspace, routing buffers) disjoint from the inputs and from each other
     Regions rg;
@@ -320,6 +358,11 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   if (trace && (trace->capacity < 0 || trace->count < 0 ||
                 (trace->capacity > 0 && (!trace->begin || !trace->end))))
     return MOE_ERR_INVALID_ARG;
+  if (use_scratch) {  // every argument checked: the current device's static scratch is the workspace
+    hipError_t err;
+    workspace = scratch_for_current_device(&err);
+    if (!workspace) return hip_fail(err);
+  }
   hipStream_t s = stream;
   Tracer tr{trace, s};
   const uint16_t* xb = (const uint16_t*)x;
@@ -430,6 +473,16 @@ moe_status_t moe_layer_forward(const moe_desc_t* d, const void* x, const void* r
                                const moe_routing_t* routing) {
   return moe_layer_forward_traced(d, x, router_w, expert_w, shared_w, top_k, out, workspace,
                                   workspace_bytes, stream, routing, nullptr);
+}
+
+moe_status_t moe_layer_forward_noalloc(const moe_desc_t* d, const void* x, const void* router_w,
+                                       const void* expert_w, const void* shared_w, int top_k, void* out,
+                                       hipStream_t stream, const moe_routing_t* routing) {
+  Weights wt{};
+  wt.q4 = false;
+  wt.ew = (const uint16_t*)expert_w;
+  wt.sw = (const uint16_t*)shared_w;
+  return forward_impl(d, x, router_w, wt, top_k, out, nullptr, 0, stream, routing, nullptr, true);
 }
 
 moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w, int top_k,

@@ -24,7 +24,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_MISALIGNED", 5: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_block_map_capacity", "moe_layer_forward", "moe_route", "moe_layer_forward_traced",
-           "moe_layer_forward_q4", "moe_tile_weights", "moe_status_string", "moe_last_hip_error")
+           "moe_layer_forward_q4", "moe_tile_weights", "moe_layer_forward_noalloc", "moe_status_string",
+           "moe_last_hip_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 # moe_kernel_t
 KERNELS = {1: "router_scores", 2: "topk", 3: "route_scan", 4: "route_scatter", 5: "gemm_gateup",
@@ -84,6 +86,9 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(MoeQ4), ctypes.c_int, vp, vp, sz, vp,
                                            ctypes.POINTER(MoeRouting), ctypes.POINTER(MoeTrace)]
         L.moe_layer_forward_q4.restype = ctypes.c_int
+        L.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(MoeDesc), vp, vp, vp, vp, ctypes.c_int, vp, vp,
+                                                ctypes.POINTER(MoeRouting)]
+        L.moe_layer_forward_noalloc.restype = ctypes.c_int
         L.moe_route.argtypes = [ctypes.POINTER(MoeDesc), vp, vp, ctypes.c_int, vp, sz, vp,
                                 ctypes.POINTER(MoeRouting)]
         L.moe_route.restype = ctypes.c_int
@@ -203,6 +208,30 @@ def forward(x: torch.Tensor, router_w: torch.Tensor, expert_w: torch.Tensor,
     else:
         st = lib().moe_layer_forward_traced(*args, ctypes.byref(trace))
     _check(st, "moe_layer_forward")
+    return out
+
+
+def forward_noalloc(x: torch.Tensor, router_w: torch.Tensor, expert_w: torch.Tensor,
+                    shared_w: Optional[torch.Tensor], top_k: int, out: torch.Tensor,
+                    router_bias: Optional[torch.Tensor] = None, routing: Optional[dict] = None, flags: int = 0,
+                    stream=None) -> torch.Tensor:
+    """moe_layer_forward_noalloc: the layer with the library's static per-device scratch as its
+    workspace.  ``out`` must be given (nothing is allocated here either); the current device must
+    be the tensors' device."""
+    _ptr(x, torch.bfloat16, "x")
+    M, H = x.shape
+    E = router_w.shape[0]
+    I = expert_w.numel() // (3 * E * H)
+    I_s = 0 if shared_w is None else shared_w.numel() // (3 * H)
+    d = make_desc(M, H, E, I, I_s, flags, router_bias)
+    r = _routing_struct(routing)
+    st = lib().moe_layer_forward_noalloc(ctypes.byref(d), _ptr(x, torch.bfloat16, "x"),
+                                         _ptr(router_w, torch.bfloat16, "router_w"),
+                                         _ptr(expert_w, torch.bfloat16, "expert_w"),
+                                         None if shared_w is None else _ptr(shared_w, torch.bfloat16, "shared_w"),
+                                         int(top_k), _ptr(out, torch.bfloat16, "out"), _stream(stream),
+                                         None if r is None else ctypes.byref(r))
+    _check(st, "moe_layer_forward_noalloc")
     return out
 
 

@@ -255,3 +255,23 @@ def test_header_compiles_as_c_and_with_hip():
                     'int main() { hipStream_t s = nullptr; return s != nullptr; }\n')
         subprocess.run([gxx, "-std=c++17", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
                         "-I", inc, "-c", cc, "-o", cc + ".o"], check=True)
+
+
+def test_noalloc_rejects_before_touching_the_device():
+    """moe_layer_forward_noalloc checks every argument, and that the call's workspace fits the
+    64 MiB static scratch, before it looks up the device's scratch (none of these calls reach it)."""
+    L = moe.lib()
+
+    def na(d, k=2, x=FAKE, r=FAKE + (1 << 24), ex=FAKE + (2 << 24), sh=FAKE + (3 << 24), out=FAKE + (4 << 24)):
+        return L.moe_layer_forward_noalloc(ctypes.byref(d), x, r, ex, sh, k, out, None, None)
+
+    big = _desc(M=4096, H=2048, E=256, I=512, Is=512)
+    assert ws_size(big, 8) > moe.NOALLOC_SCRATCH_BYTES
+    assert na(big, k=8, r=FAKE + (1 << 30), ex=FAKE + (2 << 30), sh=FAKE + (8 << 30), out=FAKE + (9 << 30)) == WS
+    d = _desc()
+    assert ws_size(d, 2) <= moe.NOALLOC_SCRATCH_BYTES
+    assert na(d, x=None) == INVALID
+    assert na(d, out=FAKE) == INVALID  # out over x
+    assert na(d, x=FAKE + 2) == MISALIGNED
+    assert na(_desc(H=100)) == SHAPE
+    assert na(_desc(M=0)) == OK  # nothing to do
