@@ -446,18 +446,26 @@ def bench_decode(args, hip, moe, SD, S, peaks, q4=False, cpu=None):
     wb = 0.5625 if q4 else 2
     layer_bytes = int((k + 1) * w.expert_elems() * wb) + E * H * 2 + 2 * H * 2
     layer_flops = 2 * H * E + (k + 1) * 3 * 2 * H * I
-    # the gate/up kernel streams the selected experts' and the shared expert's gate/up rows and x
-    gateup_bytes = int((k * I + w.I_shared) * 2 * H * wb) + H * 2
-    gateup_flops = (k * I + w.I_shared) * 2 * 2 * H
-    dom = "dec_gateup"
+    Is = w.I_shared
+    if "dec_experts" in kt:
+        # two launches: the second streams the selected experts' gate/up rows and every down row
+        # (selected and shared), reads x and writes out
+        dom, kname = "dec_experts", "k_dec_experts"
+        dom_bytes = int((k * 2 * I * H + (k * I + Is) * H) * wb) + 2 * H * 2
+        dom_flops = 2 * H * (k * 2 * I + k * I + Is)
+    else:
+        # three launches: the gate/up kernel streams the selected and shared experts' gate/up rows and x
+        dom, kname = "dec_gateup", "k_dec_gateup"
+        dom_bytes = int((k * I + Is) * 2 * H * wb) + H * 2
+        dom_flops = (k * I + Is) * 2 * 2 * H
     avg_ms = sum(kt[dom]) / len(kt[dom])
     lay_f = layer_fracs(layer_bytes * L, layer_flops * L, ms, peaks)
     res = dict(
         value=1000.0 / ms, ms_per_step=ms, ms_rounds=spread(per), gen_s=gen_s,
         layer_us=ms * 1000.0 / L, layer_bytes=layer_bytes, layer=lay_f,
         kernels_us=kernels_us(kt),
-        roofline=roofline_obj("k_dec_gateup" + ("<q4>" if q4 else ""), avg_ms, gateup_bytes, gateup_flops, peaks,
-                              traffic=traffic_for("k_dec_gateup<q4>" if q4 else "k_dec_gateup"),
+        roofline=roofline_obj(kname + ("<q4>" if q4 else ""), avg_ms, dom_bytes, dom_flops, peaks,
+                              traffic=traffic_for(kname + ("<q4>" if q4 else "")),
                               layer={"hbm_frac": lay_f["hbm_frac"], "frac_measured": lay_f.get("hbm_frac_measured"),
                                      "us_per_layer": round(ms * 1000.0 / L, 3), "bytes_per_layer": layer_bytes}),
     )

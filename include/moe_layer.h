@@ -103,6 +103,22 @@ typedef enum {
  * MOE_ERR_INVALID_ARG).  Every path reads it; results are bit-identical to
  * the row-major layout's. */
 #define MOE_FLAG_TILED_WEIGHTS 0x4u
+/* Decode path (M == 1) in two launches instead of three, when I and
+ * I_shared <= 512, H <= 4096 and (top_k * I + I_shared) * 4 <= 64 KiB (else
+ * the three launches run).  Launch 1: router scores and the shared expert's
+ * gated activations side by side; launch 2: the selection, the routed
+ * experts' gated activations and the down projections + combine, the down
+ * workgroups loading their weights at the start and waiting inside the
+ * launch for the gated activations (section "Keep each decode step on the
+ * GPU": steps wait only where a dependency requires it).  Same results,
+ * bit for bit, as the three launches, which are faster on MI355X: both
+ * phases are bound by HBM, and the in-launch wait costs about as much as a
+ * kernel boundary. */
+#define MOE_FLAG_DECODE_TWO_LAUNCH 0x10u
+/* Test hook, never set in normal use: the in-launch wait of the two-launch
+ * decode path (see moe_routing_t.wait_status) waits for a condition that
+ * never occurs, with a short bound, so that it takes its give-up path. */
+#define MOE_FLAG_WAIT_PROBE 0x8u
 
 typedef struct {
   int64_t M;                /* token rows in this call */
@@ -133,6 +149,14 @@ typedef struct {
                         is cut into ceil(c / 256) tiles, all of 256 rows but
                         the last, which holds the rest */
   int32_t* num_tiles; /* [1] tiles in the block map (grouped path only) */
+  int32_t* wait_status; /* [1] 0 when every wait inside the call's kernels ended
+                           normally; 1 when one gave up, in which case out holds
+                           NaN rows.  Only the two-launch decode path
+                           (MOE_FLAG_DECODE_TWO_LAUNCH) waits inside a launch:
+                           its second launch waits for the routed experts'
+                           gated activations before their down projections
+                           (bounded: about a second); the other paths have no
+                           such wait and write 0. */
 } moe_routing_t;
 
 /* Capacity, in tiles, that moe_routing_t.tiles must have for this
@@ -176,7 +200,9 @@ typedef enum {
   MOE_K_SM_ROUTER = 11,        /* small batch: router scores */
   MOE_K_SM_TOPK = 12,          /* small batch: top-k, weights, union of the selected experts */
   MOE_K_SM_GATEUP = 13,        /* small batch: shared and union experts' gate/up + activation */
-  MOE_K_SM_DOWN = 14           /* small batch: down projections + combine */
+  MOE_K_SM_DOWN = 14,          /* small batch: down projections + combine */
+  MOE_K_DEC_ROUTE = 15,        /* decode, two launches: router scores, shared expert gate/up */
+  MOE_K_DEC_EXPERTS = 16       /* decode, two launches: top-k, routed gate/up, all down projections, combine */
 } moe_kernel_t;
 
 /* Instrumentation for moe_layer_forward_traced: caller-created hipEvent_t

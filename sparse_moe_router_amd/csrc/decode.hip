@@ -63,8 +63,10 @@ __device__ __forceinline__ void wave_dots(const uint16_t* __restrict__ x, const 
 __global__ __launch_bounds__(256) void k_dec_router(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ wr,
                                                     const float* __restrict__ bias,
-                                                    float* __restrict__ logits, int H, int E) {
+                                                    float* __restrict__ logits, int32_t* __restrict__ status,
+                                                    int H, int E) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (status && blockIdx.x == 0 && threadIdx.x == 0) *status = 0;  // three launches: no waits
   const int e = blockIdx.x * 4 + wave;
   if (e >= E) return;
   float v, unused;
@@ -195,11 +197,237 @@ __global__ __launch_bounds__(1024) void k_dec_down(const W expert_w, const W sha
   }
 }
 
+// ---------------------------------------------------------------- the layer in two launches
+//
+// Launch 1 (k_dec_route): the router scores (one wave per expert), the
+// shared expert's gated activations (one wave per (gate, up) row pair: they
+// do not depend on the routing, so they stream beside the router rows), and
+// the reset of the per-slot arrival counters and the status word.
+//
+// Launch 2 (k_dec_experts): every workgroup selects the top k from the
+// scores.  The first k * ceil(I / kDW) workgroups compute the selected
+// experts' gated activations, one wave per row pair (the arithmetic of
+// k_dec_gateup).  The last ndown workgroups own kDRW output rows per wave:
+// they issue the loads of those rows of the down projections of every
+// selected expert and of the shared expert at once, before any h exists,
+// then wait until every gate/up workgroup of every slot has arrived, read h,
+// and sum the slots in slot order (shared last), the arithmetic of
+// k_dec_down.  Publication: h is written with agent-scope stores (through
+// the L2, which is not coherent between the XCDs); every wave waits until
+// its store is complete, and after a workgroup barrier one thread adds the
+// workgroup's arrival to its slot's counter.  A down workgroup polls the
+// counters with agent-scope loads, then reads h with agent-scope loads,
+// which return every value stored before the arrivals it saw.  Only down
+// workgroups wait, and only for gate/up workgroups, which wait for nothing
+// and come first in the grid: workgroups are dispatched in the order of
+// their index, so every gate/up workgroup holds a compute unit before any
+// down workgroup does, whatever the grid size and whatever else runs on the
+// device.  The wait is also bounded: after kDecSpinLimit polls a down
+// workgroup gives up, writes NaN to its output rows and 1 to the status
+// word.
+constexpr int kDW = 8;                 // waves per workgroup of the expert launch
+constexpr int kDRW = 2;                // output rows per wave of a down workgroup
+constexpr int kDSB = 9;                // slots whose down rows are loaded at once (top-8 + shared)
+constexpr int kDecSpinLimit = 1 << 20;  // polls (each a memory round trip + a short sleep): about a second
+constexpr int kDecProbeSpins = 64;      // polls of the wait probe (a condition that never occurs)
+
+template <class W>
+__global__ __launch_bounds__(256) void k_dec_route(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                   const float* __restrict__ bias, float* __restrict__ logits,
+                                                   const W shared_w, float* __restrict__ h_s,
+                                                   uint32_t* __restrict__ arrivals, int32_t* __restrict__ status,
+                                                   int H, int E, int Is, int k, int nrouter) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (blockIdx.x == 0) {
+    if ((int)threadIdx.x < k)
+      __hip_atomic_store(arrivals + threadIdx.x * kArriveStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0 && status) __hip_atomic_store(status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if ((int)blockIdx.x < nrouter) {
+    const int e = blockIdx.x * 4 + wave;
+    if (e >= E) return;
+    float v, unused;
+    const WBf16::Row row{wr + (int64_t)e * H};
+    wave_dots<false, WBf16>(x, row, row, H, lane, &v, &unused);
+    if (lane == 0) logits[e] = v + (bias ? bias[e] : 0.0f);
+    return;
+  }
+  const int i = (blockIdx.x - nrouter) * 4 + wave;
+  if (i >= Is) return;
+  float g, u;
+  wave_dots<true, W>(x, shared_w.gu(0, i, H, Is), shared_w.gu(1, i, H, Is), H, lane, &g, &u);
+  if (lane == 0) h_s[i] = silu(g) * u;
+}
+
+template <int EPL, class W>
+__global__ __launch_bounds__(512) void k_dec_experts(const uint16_t* __restrict__ x, const W expert_w,
+                                                     const W shared_w, const float* __restrict__ logits,
+                                                     int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                     float* __restrict__ h_r, const float* __restrict__ h_s,
+                                                     uint32_t* __restrict__ arrivals, int32_t* __restrict__ status,
+                                                     uint16_t* __restrict__ out, int H, int E, int I, int Is, int k,
+                                                     int probe) {
+  extern __shared__ __attribute__((aligned(16))) float s_h[];  // down workgroups: h of slots 0 .. k-1 ([k][I]), then the shared expert's [Is]
+  __shared__ int32_t s_ids[kMaxTopK];
+  __shared__ float s_w[kMaxTopK];
+  __shared__ uint64_t s_keys[64];
+  __shared__ int s_fail;
+  __shared__ float s_hv[kDW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rblocks = (I + kDW - 1) / kDW;  // gate/up workgroups per slot
+  if (wave == 0) {
+    uint64_t top;
+    float f[EPL];
+    load_scores<EPL>(logits, E, lane, f);
+    const uint64_t mine = wave_topk<EPL>(f, E, k, lane, &top, s_keys);
+    const int ej = (int)(0xFFFFFFFFu - (uint32_t)mine);
+    const float l0 = from_orderable((uint32_t)(top >> 32));
+    const float lj = from_orderable((uint32_t)(mine >> 32));
+    const float ex = lane < k ? expf(lj - l0) : 0.0f;
+    const float sum = wave_sum(ex);
+    if (lane < k) {
+      s_ids[lane] = ej;
+      s_w[lane] = ex / sum;
+      if (blockIdx.x == 0) {  // one workgroup publishes the selection
+        ids[lane] = ej;
+        wts[lane] = ex / sum;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int ngu = k * rblocks;  // gate/up workgroups: the first ngu of the grid
+  if ((int)blockIdx.x < ngu) {  // gated activations of slot j's expert, rows i0 .. i0 + kDW - 1
+    const int b = blockIdx.x;
+    const int j = b / rblocks, i0 = (b % rblocks) * kDW, i = i0 + wave;
+    if (i < I) {
+      const W ew = expert_w.block((int64_t)s_ids[j] * 3 * I * H);
+      float g, u;
+      wave_dots<true, W>(x, ew.gu(0, i, H, I), ew.gu(1, i, H, I), H, lane, &g, &u);
+      if (lane == 0) s_hv[wave] = silu(g) * u;
+    }
+    __syncthreads();
+    // one wave publishes the workgroup's kDW values: one store, then (once it is
+    // complete) one arrival
+    if (wave == 0) {
+      if (lane < kDW && i0 + lane < I)
+        __hip_atomic_store(h_r + (int64_t)j * I + i0 + lane, s_hv[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      if (lane == 0)
+        __hip_atomic_fetch_add(arrivals + j * kArriveStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+
+  // ---- down workgroup: output rows c0 .. c0 + kDRW - 1 of this wave
+  const int db = (int)blockIdx.x - ngu;
+  const int nslot = k + (Is > 0 ? 1 : 0);
+  const int c0 = (db * kDW + wave) * kDRW;
+  typename W::chunk_t wv[kDSB][kDRW];
+  // loads of slots jb .. jb + kDSB - 1 (slot k = the shared expert); slots past
+  // the last and lanes past a row's end re-read valid elements, never used
+  auto issue = [&](int jb) {
+#pragma unroll
+    for (int s = 0; s < kDSB; ++s) {
+      const int j = jb + s < nslot ? jb + s : 0;
+      const bool sh = j == k;
+      const int n = sh ? Is : I;
+      const W wd = sh ? shared_w : expert_w.block((int64_t)s_ids[j] * 3 * I * H);
+      const int q = lane * 8 < n ? lane * 8 : 0;
+#pragma unroll
+      for (int r = 0; r < kDRW; ++r) {
+        const int c = c0 + r < H ? c0 + r : H - 1;
+        wv[s][r] = wd.dn(c, H, n).load(q);
+      }
+    }
+  };
+  issue(0);
+
+  // wait until every gate/up workgroup has arrived (bounded)
+  if (wave == 0) {
+    const uint32_t target = probe ? 0xFFFFFFFFu : (uint32_t)rblocks;
+    const int limit = probe ? kDecProbeSpins : kDecSpinLimit;
+    int spins = 0;
+    bool ok = false;
+    for (;;) {
+      const uint32_t a = lane < k ? __hip_atomic_load(arrivals + lane * kArriveStride, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                  : target;
+      if (__all(a >= target)) {
+        ok = true;
+        break;
+      }
+      if (++spins >= limit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane == 0) s_fail = ok ? 0 : 1;
+  }
+  __syncthreads();
+  if (s_fail) {  // gave up: NaN rows, status 1
+    if (tid < kDW * kDRW) {
+      const int c = db * kDW * kDRW + tid;
+      if (c < H) out[c] = (uint16_t)0x7FC0u;
+    }
+    if (tid == 0 && status) __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  // h of every slot into LDS: the routed slots with agent-scope loads, the
+  // shared expert's from the previous launch
+  {
+    const uint64_t* hr64 = (const uint64_t*)h_r;
+    const int n64 = k * I / 2;
+    for (int q = tid; q < n64; q += kDW * 64) {
+      const uint64_t v = __hip_atomic_load(hr64 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_h[2 * q] = __uint_as_float((uint32_t)v);
+      s_h[2 * q + 1] = __uint_as_float((uint32_t)(v >> 32));
+    }
+    for (int q = tid; q < Is; q += kDW * 64) s_h[k * I + q] = h_s[q];
+  }
+  __syncthreads();
+
+  float acc[kDRW];
+#pragma unroll
+  for (int r = 0; r < kDRW; ++r) acc[r] = 0.0f;
+  for (int jb = 0; jb < nslot; jb += kDSB) {
+    if (jb > 0) issue(jb);
+#pragma unroll
+    for (int s = 0; s < kDSB; ++s) {
+      const int j = jb + s;
+      if (j >= nslot) break;  // uniform
+      const bool sh = j == k;
+      const int n = sh ? Is : I;
+      const bool ok = lane * 8 < n;
+      const float* hj = s_h + (int64_t)j * I + (ok ? lane * 8 : 0);
+      const f32x4_t h0 = *(const f32x4_t*)hj;
+      const f32x4_t h1 = *(const f32x4_t*)(hj + 4);
+      const float wj = sh ? 1.0f : s_w[j];
+#pragma unroll
+      for (int r = 0; r < kDRW; ++r) {
+        const float part = ok ? W::dot(wv[s][r], h0, h1) : 0.0f;
+        const float d = wave_sum(part);
+        {
+          // slot order, shared last; the product rounded before the sum (no fused
+          // multiply-add), as the three-launch and the small-batch paths compute it
+#pragma clang fp contract(off)
+          const float wd = wj * d;
+          acc[r] = acc[r] + wd;
+        }
+      }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < kDRW; ++r)
+      if (c0 + r < H) out[c0 + r] = (uint16_t)f32_to_bf16(acc[r]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
-                                const Plan& p, const Launch& lc) {
-  return launch(lc, k_dec_router, dim3((p.E + 3) / 4), dim3(256), x, wr, bias, logits, p.H, p.E);
+                                int32_t* status, const Plan& p, const Launch& lc) {
+  return launch(lc, k_dec_router, dim3((p.E + 3) / 4), dim3(256), x, wr, bias, logits, status, p.H, p.E);
 }
 
 namespace {
@@ -246,6 +474,75 @@ hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w
   const uint16_t* sw = p.shared ? shared_w : nullptr;
   if (p.tiled) return decode_down(WBf16T{expert_w}, WBf16T{sw}, ids, w, h_dec, out, p, lc);
   return decode_down(WBf16{expert_w}, WBf16{sw}, ids, w, h_dec, out, p, lc);
+}
+
+namespace {
+
+template <class W>
+hipError_t decode_route(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits, const W sw,
+                        float* h_dec, uint32_t* arrivals, int32_t* status, const Plan& p, const Launch& lc) {
+  const int nrouter = (p.E + 3) / 4;
+  const int nshared = p.shared ? (p.Is + 3) / 4 : 0;
+  float* h_s = h_dec + (int64_t)p.k * p.I;
+  return launch(lc, k_dec_route<W>, dim3(nrouter + nshared), dim3(256), x, wr, bias, logits, sw, h_s, arrivals,
+                status, p.H, p.E, p.Is, p.k, nrouter);
+}
+
+template <class W>
+hipError_t decode_experts(const uint16_t* x, const W ew, const W sw, const float* logits, int32_t* ids, float* w,
+                          float* h_dec, uint32_t* arrivals, int32_t* status, uint16_t* out, const Plan& p, int probe,
+                          const Launch& lc) {
+  const int ndown = (p.H + kDW * kDRW - 1) / (kDW * kDRW);
+  const int blocks = ndown + p.k * ((p.I + kDW - 1) / kDW);
+  const size_t shm = ((size_t)p.k * p.I + p.Is) * 4;
+  const float* h_s = h_dec + (int64_t)p.k * p.I;
+  const dim3 g(blocks), b(kDW * 64);
+#define MOE_DEC_EXPERTS(EPL) \
+  launch_shm(lc, k_dec_experts<EPL, W>, g, b, shm, x, ew, sw, logits, ids, w, h_dec, h_s, arrivals, status, out, \
+             p.H, p.E, p.I, p.Is, p.k, probe)
+  if (p.E <= 64) return MOE_DEC_EXPERTS(1);
+  if (p.E <= 128) return MOE_DEC_EXPERTS(2);
+  if (p.E <= 256) return MOE_DEC_EXPERTS(4);
+  if (p.E <= 512) return MOE_DEC_EXPERTS(8);
+  return MOE_DEC_EXPERTS(16);
+#undef MOE_DEC_EXPERTS
+}
+
+}  // namespace
+
+bool decode_two_launch_fits(const Plan& p) {
+  // one 8-element chunk per lane per down row; at most 256 down workgroups
+  return p.I <= 512 && p.Is <= 512 && p.H <= 4096 && ((int64_t)p.k * p.I + p.Is) * 4 <= 64 * 1024;
+}
+
+hipError_t launch_decode_route(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                               const uint16_t* shared_w, float* h_dec, uint32_t* arrivals, int32_t* status,
+                               const Plan& p, const Launch& lc) {
+  const uint16_t* sw = p.shared ? shared_w : nullptr;
+  if (p.tiled) return decode_route(x, wr, bias, logits, WBf16T{sw}, h_dec, arrivals, status, p, lc);
+  return decode_route(x, wr, bias, logits, WBf16{sw}, h_dec, arrivals, status, p, lc);
+}
+
+hipError_t launch_decode_route_q4(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                                  const Q4Weights& sh, float* h_dec, uint32_t* arrivals, int32_t* status,
+                                  const Plan& p, const Launch& lc) {
+  return decode_route(x, wr, bias, logits, WQ4{sh.codes, sh.groups}, h_dec, arrivals, status, p, lc);
+}
+
+hipError_t launch_decode_experts(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
+                                 const float* logits, int32_t* ids, float* w, float* h_dec, uint32_t* arrivals,
+                                 int32_t* status, uint16_t* out, const Plan& p, int probe, const Launch& lc) {
+  const uint16_t* sw = p.shared ? shared_w : nullptr;
+  if (p.tiled)
+    return decode_experts(x, WBf16T{expert_w}, WBf16T{sw}, logits, ids, w, h_dec, arrivals, status, out, p, probe, lc);
+  return decode_experts(x, WBf16{expert_w}, WBf16{sw}, logits, ids, w, h_dec, arrivals, status, out, p, probe, lc);
+}
+
+hipError_t launch_decode_experts_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const float* logits,
+                                    int32_t* ids, float* w, float* h_dec, uint32_t* arrivals, int32_t* status,
+                                    uint16_t* out, const Plan& p, int probe, const Launch& lc) {
+  return decode_experts(x, WQ4{ex.codes, ex.groups}, WQ4{sh.codes, sh.groups}, logits, ids, w, h_dec, arrivals,
+                        status, out, p, probe, lc);
 }
 
 hipError_t launch_decode_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh,

@@ -89,6 +89,7 @@ bool make_plan(Plan* p, int64_t M, int H, int E, int I, int Is, int k, bool gemv
     ok &= place(&off, &p->ids, A * 4);
     ok &= place(&off, &p->w, A * 4);
     ok &= place(&off, &p->h_r, (A * I + (uint64_t)M * Is) * 4);
+    if (M == 1) ok &= place(&off, &p->arrive, (uint64_t)k * kArriveStride * 4);
     if (M > 1) {
       ok &= place(&off, &p->un_count, 8);
       ok &= place(&off, &p->un_exp, (A < (uint64_t)E ? A : (uint64_t)E) * 4);
@@ -128,7 +129,8 @@ namespace {
 moe_status_t check_desc(const moe_desc_t* d, int top_k, bool* gemv) {
   if (!d) return MOE_ERR_INVALID_ARG;
   if (d->M < 0) return MOE_ERR_INVALID_ARG;
-  const uint32_t known = MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GEMM | MOE_FLAG_TILED_WEIGHTS;
+  const uint32_t known = MOE_FLAG_FORCE_GEMV | MOE_FLAG_FORCE_GEMM | MOE_FLAG_TILED_WEIGHTS | MOE_FLAG_WAIT_PROBE |
+                         MOE_FLAG_DECODE_TWO_LAUNCH;
   if (d->flags & ~known) return MOE_ERR_INVALID_ARG;
   if ((d->flags & MOE_FLAG_FORCE_GEMV) && (d->flags & MOE_FLAG_FORCE_GEMM)) return MOE_ERR_INVALID_ARG;
   if (d->H < 64 || d->H > 16384 || d->H % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
@@ -148,7 +150,8 @@ moe_status_t check_desc(const moe_desc_t* d, int top_k, bool* gemv) {
 
 moe_status_t check_routing(const moe_routing_t* r) {
   if (!r) return MOE_OK;
-  const void* ps[] = {r->topk_ids, r->topk_w, r->logits, r->counts, r->offsets, r->perm, r->tiles, r->num_tiles};
+  const void* ps[] = {r->topk_ids, r->topk_w, r->logits,    r->counts,
+                      r->offsets,  r->perm,   r->tiles,     r->num_tiles, r->wait_status};
   for (const void* p : ps)
     if (p && !aligned(p, 4)) return MOE_ERR_MISALIGNED;
   return MOE_OK;
@@ -166,6 +169,7 @@ void routing_regions(Regions* rg, const moe_routing_t* r, int64_t M, int E, int 
   rg->output(r->perm, A * 4);
   rg->output(r->tiles, (size_t)max_tiles * sizeof(Tile));
   rg->output(r->num_tiles, 4);
+  rg->output(r->wait_status, 4);
 }
 
 template <class T>
@@ -216,8 +220,8 @@ moe_status_t run_routing_grouped(const Plan& p, const moe_desc_t* d, const void*
   hipError_t e;
   uint64_t* cmask = ws_ptr<uint64_t>(ws, p.cmask);
   if ((e = tr.run(MOE_K_ROUTER_SCORES, [&](const Launch& lc) {
-         return launch_router_logits((const uint16_t*)x, (const uint16_t*)wr, d->router_bias, L, cmask, p.M,
-                                     p.H, p.E, lc);
+         return launch_router_logits((const uint16_t*)x, (const uint16_t*)wr, d->router_bias, L, cmask,
+                                     r ? r->wait_status : nullptr, p.M, p.H, p.E, lc);
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = tr.run(MOE_K_TOPK, [&](const Launch& lc) { return launch_topk(L, ids, w, cmask, p.M, p.E, p.k, lc); })) != hipSuccess)
@@ -366,6 +370,7 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   hipStream_t s = stream;
   Tracer tr{trace, s};
   const uint16_t* xb = (const uint16_t*)x;
+  int32_t* status = routing ? routing->wait_status : nullptr;
   hipError_t e;
   if (gemv && p.M > 1) {
     float* L = (routing && routing->logits) ? routing->logits : ws_ptr<float>(workspace, p.logits);
@@ -374,7 +379,7 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
     float* h = ws_ptr<float>(workspace, p.h_r);
     const SmallUnion un = small_union(workspace, p);
     if ((e = tr.run(MOE_K_SM_ROUTER, [&](const Launch& lc) {
-           return launch_small_router(xb, (const uint16_t*)router_w, d->router_bias, L, p, lc);
+           return launch_small_router(xb, (const uint16_t*)router_w, d->router_bias, L, status, p, lc);
          })) != hipSuccess)
       return hip_fail(e);
     if ((e = tr.run(MOE_K_SM_TOPK, [&](const Launch& lc) { return launch_small_topk(L, ids, w, un, p, lc); })) !=
@@ -397,8 +402,27 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
     int32_t* ids = (routing && routing->topk_ids) ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
     float* w = (routing && routing->topk_w) ? routing->topk_w : ws_ptr<float>(workspace, p.w);
     float* h = ws_ptr<float>(workspace, p.h_r);
+    if ((d->flags & MOE_FLAG_DECODE_TWO_LAUNCH) && decode_two_launch_fits(p)) {
+      uint32_t* arr = ws_ptr<uint32_t>(workspace, p.arrive);
+      const int probe = (d->flags & MOE_FLAG_WAIT_PROBE) ? 1 : 0;
+      if ((e = tr.run(MOE_K_DEC_ROUTE, [&](const Launch& lc) {
+             return wt.q4 ? launch_decode_route_q4(xb, (const uint16_t*)router_w, d->router_bias, L, wt.sq, h, arr,
+                                                   status, p, lc)
+                          : launch_decode_route(xb, (const uint16_t*)router_w, d->router_bias, L, wt.sw, h, arr,
+                                                status, p, lc);
+           })) != hipSuccess)
+        return hip_fail(e);
+      if ((e = tr.run(MOE_K_DEC_EXPERTS, [&](const Launch& lc) {
+             return wt.q4 ? launch_decode_experts_q4(xb, wt.eq, wt.sq, L, ids, w, h, arr, status, (uint16_t*)out, p,
+                                                     probe, lc)
+                          : launch_decode_experts(xb, wt.ew, wt.sw, L, ids, w, h, arr, status, (uint16_t*)out, p,
+                                                  probe, lc);
+           })) != hipSuccess)
+        return hip_fail(e);
+      return MOE_OK;
+    }
     if ((e = tr.run(MOE_K_DEC_ROUTER, [&](const Launch& lc) {
-           return launch_decode_router(xb, (const uint16_t*)router_w, d->router_bias, L, p, lc);
+           return launch_decode_router(xb, (const uint16_t*)router_w, d->router_bias, L, status, p, lc);
          })) != hipSuccess)
       return hip_fail(e);
     if ((e = tr.run(MOE_K_DEC_GATEUP, [&](const Launch& lc) {
@@ -520,16 +544,16 @@ moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w,
     float* w = routing->topk_w ? routing->topk_w : ws_ptr<float>(workspace, p.w);
     hipError_t e;
     if (p.M > 1) {
-      if ((e = launch_small_router((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias, L, p,
-                                   Launch{s, nullptr, nullptr})) != hipSuccess)
+      if ((e = launch_small_router((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias, L,
+                                   routing->wait_status, p, Launch{s, nullptr, nullptr})) != hipSuccess)
         return hip_fail(e);
       if ((e = launch_small_topk(L, ids, w, small_union(workspace, p), p, Launch{s, nullptr, nullptr})) !=
           hipSuccess)
         return hip_fail(e);
       return MOE_OK;
     }
-    if ((e = launch_decode_router((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias, L, q,
-                                  Launch{s, nullptr, nullptr})) != hipSuccess)
+    if ((e = launch_decode_router((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias, L,
+                                  routing->wait_status, q, Launch{s, nullptr, nullptr})) != hipSuccess)
       return hip_fail(e);
     if ((e = launch_decode_gateup((const uint16_t*)x, nullptr, nullptr, L, ids, w, nullptr, q,
                                   Launch{s, nullptr, nullptr})) != hipSuccess)

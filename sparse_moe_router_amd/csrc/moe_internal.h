@@ -17,6 +17,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxSmallM = 64;  // most rows the matrix-vector paths take
 constexpr int kSmallRows = 4;   // small-batch path: assignments per register batch / work unit
+constexpr int kArriveStride = 64;  // decode, two launches: one arrival counter per 256-byte line
 
 // ----------------------------------------------------------------- vector types
 
@@ -66,6 +67,7 @@ struct Plan {
   // byte offsets into the workspace (all 256-aligned)
   size_t logits, ids, w, cmask, cbase, counts, offsets, perm, inv, tiles, ntiles, h_r, h_s, y_r, y_s;
   size_t un_count, un_exp, un_off, un_pair, un_unit;  // small-batch path: union of the selected experts
+  size_t arrive;  // decode path, two launches: arrival counters of the gate/up workgroups, one per slot
   size_t total;
 };
 
@@ -105,8 +107,9 @@ struct Q4Weights {
 };
 
 // Router scores L[M][E] = x Wr^T (+ bias), fp32 (MFMA); clears the chunk masks.
+// *status (if given) = 0: this path has no in-kernel waits.
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, float* L,
-                                uint64_t* cmask, int64_t M, int H, int E, const Launch& lc);
+                                uint64_t* cmask, int32_t* status, int64_t M, int H, int E, const Launch& lc);
 // Top-k + weights per token, and the token's bits in the per-chunk expert masks.
 hipError_t launch_topk(const float* L, int32_t* ids, float* w, uint64_t* cmask, int64_t M, int E, int k,
                        const Launch& lc);
@@ -138,7 +141,7 @@ hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float*
 // Decode (M == 1) path.
 // Router scores.
 hipError_t launch_decode_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
-                                const Plan& p, const Launch& lc);
+                                int32_t* status, const Plan& p, const Launch& lc);
 // Shared and selected experts' gated activations (h_dec: fp32 [k][I] routed,
 // then [Is] shared); top-k ids and weights.
 hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
@@ -147,6 +150,29 @@ hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, con
 hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w, const int32_t* ids,
                               const float* w, const float* h_dec, uint16_t* out, const Plan& p,
                               const Launch& lc);
+
+// The decode layer in two launches (MOE_FLAG_DECODE_TWO_LAUNCH, when
+// decode_two_launch_fits(p): I, Is <= 512, H <= 4096, the h of all slots
+// within 64 KB of LDS): launch 1
+// writes the router scores and the shared expert's h and resets the
+// arrival counters (and *status, if given); launch 2 selects, computes the
+// routed h and the down projections + combine, the down workgroups waiting
+// in the launch for the routed h (bounded; on giving up, NaN rows and
+// *status = 1).  probe != 0 makes that wait one that never ends (test hook:
+// the give-up path).  Same results as the three-launch path.
+bool decode_two_launch_fits(const Plan& p);
+hipError_t launch_decode_route(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                               const uint16_t* shared_w, float* h_dec, uint32_t* arrivals, int32_t* status,
+                               const Plan& p, const Launch& lc);
+hipError_t launch_decode_route_q4(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
+                                  const Q4Weights& sh, float* h_dec, uint32_t* arrivals, int32_t* status,
+                                  const Plan& p, const Launch& lc);
+hipError_t launch_decode_experts(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
+                                 const float* logits, int32_t* ids, float* w, float* h_dec, uint32_t* arrivals,
+                                 int32_t* status, uint16_t* out, const Plan& p, int probe, const Launch& lc);
+hipError_t launch_decode_experts_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const float* logits,
+                                    int32_t* ids, float* w, float* h_dec, uint32_t* arrivals, int32_t* status,
+                                    uint16_t* out, const Plan& p, int probe, const Launch& lc);
 
 // The decode kernels above, reading 4-bit weights (same outputs and layout).
 hipError_t launch_decode_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh,
@@ -172,7 +198,7 @@ inline int64_t small_units(int64_t M, int k, int E) {
   return (A < E ? A : E) + (A + kSmallRows - 1) / kSmallRows + (M + kSmallRows - 1) / kSmallRows;
 }
 hipError_t launch_small_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
-                               const Plan& p, const Launch& lc);
+                               int32_t* status, const Plan& p, const Launch& lc);
 hipError_t launch_small_topk(const float* logits, int32_t* ids, float* w, const SmallUnion& un, const Plan& p,
                              const Launch& lc);
 hipError_t launch_small_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,

@@ -33,14 +33,15 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
                                                        const uint16_t* __restrict__ wr,
                                                        const float* __restrict__ bias,
                                                        float* __restrict__ L,
-                                                       uint64_t* __restrict__ cmask, int64_t M, int H,
-                                                       int E) {
+                                                       uint64_t* __restrict__ cmask,
+                                                       int32_t* __restrict__ status, int64_t M, int H, int E) {
   __shared__ u32x4_t sA[2][64 * 8];
   __shared__ u32x4_t sB[2][64 * 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
   const int e0 = blockIdx.y * 64;
   const int wm = wave >> 1, wn = wave & 1;
+  if (status && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *status = 0;  // no waits on this path
   // this tile's (chunk, expert) bitmask words start empty; top-k sets their bits
   if (cmask && tid < 64 && e0 + tid < E) cmask[(int64_t)blockIdx.x * E + e0 + tid] = 0ull;
 
@@ -310,9 +311,9 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, float* L,
-                                uint64_t* cmask, int64_t M, int H, int E, const Launch& lc) {
+                                uint64_t* cmask, int32_t* status, int64_t M, int H, int E, const Launch& lc) {
   dim3 grid((unsigned)((M + 63) / 64), (unsigned)((E + 63) / 64));
-  return launch(lc, k_router_logits, grid, dim3(256), x, wr, bias, L, cmask, M, H, E);
+  return launch(lc, k_router_logits, grid, dim3(256), x, wr, bias, L, cmask, status, M, H, E);
 }
 
 hipError_t launch_topk(const float* L, int32_t* ids, float* w, uint64_t* cmask, int64_t M, int E, int k,

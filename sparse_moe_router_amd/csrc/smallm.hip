@@ -96,8 +96,10 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane) {
 __global__ __launch_bounds__(256) void k_sm_router(const uint16_t* __restrict__ x,
                                                    const uint16_t* __restrict__ wr,
                                                    const float* __restrict__ bias,
-                                                   float* __restrict__ logits, int M, int H, int E) {
+                                                   float* __restrict__ logits, int32_t* __restrict__ status,
+                                                   int M, int H, int E) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;  // no waits on this path
   const int e = blockIdx.x * 4 + wave;
   if (e >= E) return;
   const WBf16::Row row{wr + (int64_t)e * H};
@@ -380,9 +382,9 @@ hipError_t small_down(const W ew, const W sw, const float* w, const SmallUnion& 
 }  // namespace
 
 hipError_t launch_small_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
-                               const Plan& p, const Launch& lc) {
+                               int32_t* status, const Plan& p, const Launch& lc) {
   return launch(lc, k_sm_router, dim3((p.E + 3) / 4, (unsigned)((p.M + NP - 1) / NP)), dim3(256), x, wr, bias,
-                logits, (int)p.M, p.H, p.E);
+                logits, status, (int)p.M, p.H, p.E);
 }
 
 hipError_t launch_small_topk(const float* logits, int32_t* ids, float* w, const SmallUnion& un, const Plan& p,

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe_layer.so")
 FLAG_FORCE_GEMV = 0x1
 FLAG_FORCE_GEMM = 0x2
 FLAG_TILED_WEIGHTS = 0x4
+FLAG_WAIT_PROBE = 0x8  # test hook: the two-launch decode path's in-launch wait takes its give-up path
+FLAG_DECODE_TWO_LAUNCH = 0x10  # decode path in two launches (opt-in; three launches are faster on MI355X)
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_MISALIGNED", 5: "MOE_ERR_HIP"}
@@ -31,7 +33,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 # moe_kernel_t
 KERNELS = {1: "router_scores", 2: "topk", 3: "route_scan", 4: "route_scatter", 5: "gemm_gateup",
            6: "gemm_down", 7: "combine", 8: "dec_router", 9: "dec_gateup", 10: "dec_down",
-           11: "sm_router", 12: "sm_topk", 13: "sm_gateup", 14: "sm_down"}
+           11: "sm_router", 12: "sm_topk", 13: "sm_gateup", 14: "sm_down", 15: "dec_route", 16: "dec_experts"}
 
 
 class MoeDesc(ctypes.Structure):
@@ -43,7 +45,7 @@ class MoeDesc(ctypes.Structure):
 class MoeRouting(ctypes.Structure):
     _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("logits", ctypes.c_void_p),
                 ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
-                ("tiles", ctypes.c_void_p), ("num_tiles", ctypes.c_void_p)]
+                ("tiles", ctypes.c_void_p), ("num_tiles", ctypes.c_void_p), ("wait_status", ctypes.c_void_p)]
 
 
 class MoeTrace(ctypes.Structure):
@@ -152,7 +154,7 @@ def _routing_struct(routing: Optional[dict]) -> Optional[MoeRouting]:
         return None
     spec = {"topk_ids": torch.int32, "topk_w": torch.float32, "logits": torch.float32,
             "counts": torch.int32, "offsets": torch.int32, "perm": torch.int32, "tiles": torch.int32,
-            "num_tiles": torch.int32}
+            "num_tiles": torch.int32, "wait_status": torch.int32}
     r = MoeRouting()
     for k, v in routing.items():
         if k not in spec:

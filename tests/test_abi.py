@@ -55,7 +55,7 @@ def test_workspace_size_valid_and_invalid():
     gemm = ws_size(_desc(M=1, H=2048, E=256, I=512, Is=512, flags=moe.FLAG_FORCE_GEMM), 8)
     assert 0 < gemv < gemm  # the decode path needs no permutation tables or y rows
     for bad in [_desc(H=100), _desc(I=96), _desc(E=0), _desc(E=2000), _desc(Is=32), _desc(M=-1),
-                _desc(flags=3), _desc(flags=0x10)]:
+                _desc(flags=3), _desc(flags=0x20)]:
         assert ws_size(bad, 2) == 0
     assert ws_size(_desc(), 0) == 0
     assert ws_size(_desc(), 17) == 0  # top_k > E

@@ -49,9 +49,11 @@ def _call(x, r, wts, flags, out, ws, stream=None):
 
 
 @pytest.mark.parametrize("kind", ["bf16", "tiled", "q4"])
-@pytest.mark.parametrize("M", [1, 8, 300])
+@pytest.mark.parametrize("M", [1, 8, 300, -1])  # -1: one row on the two-launch decode path
 def test_graph_replay_matches_eager(kind, M):
     r, wts, flags = _weights(kind)
+    if M == -1:
+        M, flags = 1, flags | TWO
     g0 = torch.Generator().manual_seed(M)
     xs = [upload(np.random.default_rng(M + i).standard_normal((M, H)).astype(np.float32)) for i in range(3)]
     x = xs[0].clone()
@@ -104,11 +106,12 @@ def test_two_streams_two_workspaces(M):
         assert torch.equal(outs_b[i].view(torch.int16), ref_b.view(torch.int16)), f"stream b call {i}"
 
 
-PATH_KERNELS = {1: [8, 9, 10], 8: [11, 12, 13, 14], 300: [1, 2, 3, 4, 5, 6, 7]}  # moe_kernel_t ids
+PATH_KERNELS = {1: [8, 9, 10], 8: [11, 12, 13, 14], 300: [1, 2, 3, 4, 5, 6, 7], -1: [15, 16]}  # moe_kernel_t ids
+TWO = moe.FLAG_DECODE_TWO_LAUNCH
 
 
 @pytest.mark.parametrize("kind", ["bf16", "q4"])
-@pytest.mark.parametrize("M", [1, 8, 300])
+@pytest.mark.parametrize("M", [1, 8, 300, -1])  # -1: one row on the two-launch decode path
 def test_traced_call_matches_and_records_kernels(kind, M):
     """With a trace the call gives the bits of the untraced call and records each kernel of its
     path once, in launch order, with a finite duration; with a trace shorter than the path the
@@ -117,11 +120,13 @@ def test_traced_call_matches_and_records_kernels(kind, M):
     import bench
     hip = bench.Hip()
     r, wts, flags = _weights(kind, seed=7)
+    want = PATH_KERNELS[M]
+    if M == -1:
+        M, flags = 1, flags | TWO
     x = upload(np.random.default_rng(30 + M).standard_normal((M, H)).astype(np.float32))
     ws = torch.empty(moe.workspace_size(M, H, E, I, IS, K, flags=flags), dtype=torch.uint8, device="cuda")
     ref = _call(x, r, wts, flags, torch.empty_like(x), ws).clone()
     torch.cuda.synchronize()
-    want = PATH_KERNELS[M]
     for cap in (16, 2):
         begin, end = hip.events(16), hip.events(16)
         kid = (ctypes.c_int32 * 16)(*([-1] * 16))
@@ -167,3 +172,49 @@ def test_two_streams_cached_workspaces():
         assert torch.equal(out.view(torch.int16), refs[i].view(torch.int16)), f"call {i}"
     keys = [kk for kk in moe._ws_cache if kk[2] in (sa.cuda_stream, sb.cuda_stream)]
     assert len(keys) == 2, keys
+
+
+@pytest.mark.parametrize("kind", ["bf16", "q4"])
+def test_decode_wait_status_and_give_up(kind):
+    """The two-launch decode path's second launch waits inside the kernel for the routed experts'
+    gated activations.  A normal call reports wait_status 0 (so do the paths without such a wait); with
+    the test hook MOE_FLAG_WAIT_PROBE the wait is for a condition that never occurs, bounded to a
+    few polls: it gives up, every output row is NaN and wait_status is 1, and the next normal call
+    on the same workspace is exact again."""
+    r, wts, flags = _weights(kind, seed=8)
+    x = upload(np.random.default_rng(77).standard_normal((1, H)).astype(np.float32))
+    ws = torch.empty(moe.workspace_size(1, H, E, I, IS, K, flags=flags), dtype=torch.uint8, device="cuda")
+    flags |= TWO
+
+    def run(extra, M_x=x, extra_off=0):
+        st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+        out = torch.empty_like(M_x)
+        rb = {"wait_status": st}
+        f = (flags | extra) & ~extra_off
+        if len(wts) == 4:
+            moe.forward_q4(M_x, r, *wts, K, out=out, flags=f, workspace=ws, routing=rb)
+        else:
+            moe.forward(M_x, r, wts[0], wts[1], K, out=out, flags=f, workspace=ws, routing=rb)
+        torch.cuda.synchronize()
+        return out, int(st.item())
+
+    ref, st0 = run(0)
+    assert st0 == 0 and torch.isfinite(ref.float()).all()
+    bad, st1 = run(moe.FLAG_WAIT_PROBE)
+    assert st1 == 1 and torch.isnan(bad.float()).all()
+    again, st2 = run(0)
+    assert st2 == 0 and torch.equal(again.view(torch.int16), ref.view(torch.int16))
+    # paths without an in-kernel wait write 0 (the three-launch decode path too)
+    three, st3 = run(0, extra_off=TWO)
+    assert st3 == 0 and torch.equal(three.view(torch.int16), ref.view(torch.int16))
+    for M in (8, 300):
+        xm = upload(np.random.default_rng(M).standard_normal((M, H)).astype(np.float32))
+        wsm = torch.empty(moe.workspace_size(M, H, E, I, IS, K, flags=flags), dtype=torch.uint8, device="cuda")
+        st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+        f = flags & ~TWO
+        if len(wts) == 4:
+            moe.forward_q4(xm, r, *wts, K, flags=f, workspace=wsm, routing={"wait_status": st})
+        else:
+            moe.forward(xm, r, wts[0], wts[1], K, flags=f, workspace=wsm, routing={"wait_status": st})
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, M

@@ -123,7 +123,12 @@ def test_decode_full_shape():
     for layer in range(w.layers):
         hl = HostLayer(w, layer)
         _, r, ex, sh = device_layer(w, layer, x_rows=1)
-        gs = [run_gpu(bits_to_dev(S.x_rows(w, row, 1, layer)), r, ex, sh, w.k) for row in DECODE_ROWS]
+        xs = [bits_to_dev(S.x_rows(w, row, 1, layer)) for row in DECODE_ROWS]
+        gs = [run_gpu(x1, r, ex, sh, w.k) for x1 in xs]
+        # the two-launch decode path gives the same bits
+        for x1, g1 in zip(xs, gs):
+            two = moe.forward(x1, r, ex, sh, w.k, flags=moe.FLAG_DECODE_TWO_LAUNCH)
+            assert np.array_equal(two.float().cpu().numpy(), g1["out"]), f"two launches, layer {layer}"
         del ex, r, sh
         g = {n: np.concatenate([one[n] for one in gs]) for n in gs[0]}
         xh = np.concatenate([hl.x(row, 1) for row in DECODE_ROWS])
@@ -243,3 +248,13 @@ def test_route_matches_forward_routing():
     torch.cuda.synchronize()
     for k, v in rb.items():
         assert np.array_equal(v.cpu().numpy(), g[k]), k
+
+
+@pytest.mark.parametrize("H,E,k,I,Is", [(4096, 64, 8, 512, 512), (4096, 64, 16, 512, 512), (4160, 64, 8, 512, 512),
+                                        (2048, 64, 32, 512, 512), (256, 16, 2, 576, 64), (192, 16, 2, 64, 0),
+                                        (256, 300, 8, 128, 256)])
+def test_decode_two_launch_limits(H, E, k, I, Is):
+    """Batch-1 decode with MOE_FLAG_DECODE_TWO_LAUNCH at the edges of the two-launch path (H = 4096:
+    256 down workgroups; top-16; no shared expert; E = 300) and just past them (H = 4160, h of 33
+    slots beyond 64 KB, I = 576), where the three launches run: every output against the oracle."""
+    _edge(1, H, E, k, I, Is, flags=moe.FLAG_DECODE_TWO_LAUNCH, seed=H + k + I)

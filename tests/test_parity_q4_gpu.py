@@ -112,7 +112,11 @@ def test_q4_decode_full_shape():
     for layer in range(w.layers):
         hl = HostLayerQ4(w, layer)
         _, r, ex, esb, sh, ssb = SD.layer_tensors_q4(w, layer, x_rows=1)
-        gs = [run_q4(bits_to_dev(S.x_rows(w, row, 1, layer)), r, ex, esb, sh, ssb, w.k) for row in rows]
+        xs = [bits_to_dev(S.x_rows(w, row, 1, layer)) for row in rows]
+        gs = [run_q4(x1, r, ex, esb, sh, ssb, w.k) for x1 in xs]
+        for x1, g1 in zip(xs, gs):  # the two-launch decode path gives the same bits
+            two = moe.forward_q4(x1, r, ex, esb, sh, ssb, w.k, flags=moe.FLAG_DECODE_TWO_LAUNCH)
+            assert np.array_equal(two.float().cpu().numpy(), g1["out"]), f"two launches, layer {layer}"
         del ex, esb
         g = {n: np.concatenate([one[n] for one in gs]) for n in gs[0]}
         hl.prefetch(g["topk_ids"].ravel())
