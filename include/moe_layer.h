@@ -192,8 +192,8 @@ typedef enum {
   MOE_K_ROUTE_SCAN = 3,        /* grouped path: prefix scan and block map */
   MOE_K_ROUTE_SCATTER = 4,     /* grouped path: scatter into expert groups */
   MOE_K_GEMM_GATEUP = 5,       /* grouped path: gate/up GEMM + gated activation */
-  MOE_K_GEMM_DOWN = 6,         /* grouped path: down GEMM */
-  MOE_K_COMBINE = 7,           /* grouped path: weighted combine + shared expert */
+  MOE_K_GEMM_DOWN = 6,         /* grouped path: down GEMM of the routed experts */
+  MOE_K_COMBINE = 7,           /* grouped path without a shared expert: weighted combine */
   MOE_K_DEC_ROUTER = 8,        /* decode: router scores */
   MOE_K_DEC_GATEUP = 9,        /* decode: shared expert gate/up, top-k, routed gate/up */
   MOE_K_DEC_DOWN = 10,         /* decode: down projections + combine */
@@ -202,7 +202,8 @@ typedef enum {
   MOE_K_SM_GATEUP = 13,        /* small batch: shared and union experts' gate/up + activation */
   MOE_K_SM_DOWN = 14,          /* small batch: down projections + combine */
   MOE_K_DEC_ROUTE = 15,        /* decode, two launches: router scores, shared expert gate/up */
-  MOE_K_DEC_EXPERTS = 16       /* decode, two launches: top-k, routed gate/up, all down projections, combine */
+  MOE_K_DEC_EXPERTS = 16,      /* decode, two launches: top-k, routed gate/up, all down projections, combine */
+  MOE_K_SHARED_DOWN_COMBINE = 17 /* grouped path with a shared expert: its down GEMM + the weighted combine */
 } moe_kernel_t;
 
 /* Instrumentation for moe_layer_forward_traced: caller-created hipEvent_t

@@ -355,7 +355,14 @@ def dequant_q4(packed, scale_bias) -> np.ndarray:
 
 
 def rel_err_per_token(y, ref) -> np.ndarray:
-    """max_c |y[t,c] - ref[t,c]| / max_c |ref[t,c]| for each token row t."""
+    """max_c |y[t,c] - ref[t,c]| / max_c |ref[t,c]| for each token row t.
+
+    The comparison every output check uses.  Reading: the bound on the
+    layer's outputs is a maximum relative error without a stated norm; it is
+    taken per token in the max norm (an elementwise relative error is
+    ill-posed at outputs near zero).  A row whose reference is all zero
+    divides by the smallest normal double, so equal zero rows give 0.
+    """
     y = _f64(y)
     ref = _f64(ref)
     num = np.abs(y - ref).max(axis=1)

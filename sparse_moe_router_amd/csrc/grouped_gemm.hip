@@ -56,6 +56,11 @@ struct GemmArgs {
   const uint32_t* sh_groups;
   uint16_t* out_r;
   uint16_t* out_s;
+  const uint16_t* y_r;  // MODE 2: the routed experts' output rows (group order) to combine
+  const float* w;       // MODE 2: routing weights [M][k]
+  const int32_t* inv;   // MODE 2: group position of each assignment [M*k]
+  uint16_t* out;        // MODE 2: the layer's output [M][H]
+  int skip_tail;        // MODE 1: tiles at the end of the block map left out (the shared expert's, done by MODE 2)
   int64_t M;
   int H, E, I, Is, k;
   int npan;
@@ -115,6 +120,103 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t c, uint32_t g) {
   return r;
 }
 
+// MODE 2 epilogue: the shared expert's down projection fused with the
+// weighted combine ("Optimizing on-device inference for Apple Silicon",
+// section "Reduce intermediate and state traffic": the output projection
+// goes with its routing score and the shared expert's result).  The tile is
+// <= 128 tokens (in order) x the panel's <= 256 columns.  Its shared-expert
+// outputs S, rounded to bf16, are staged in the idle LDS rings (rows 0-63 in
+// ring.a[0], 64-127 in ring.a[1], 512 bytes a row), the tile's inv / w
+// entries beside them, then all 512 threads build out[t] = sum_j w[t,j] *
+// y_r[inv[t,j]] (fp32, slot order) + S[t], rounded once to bf16, two
+// 8-column chunks (16-byte loads of each y row) per thread and step: the
+// arithmetic of the stand-alone combine.
+template <int NRH>
+__device__ __forceinline__ void combine_epilogue(const GemmArgs& p, const Tile& tl, int panel, const Ring& ring,
+                                                 const f32x16_t (&acc)[NRH][2], bool wave_cols, int cg, int rg,
+                                                 int half, int l32) {
+  const int tid = threadIdx.x, k = p.k;
+  uint16_t* s_lo = (uint16_t*)ring.a[0];
+  uint16_t* s_hi = (uint16_t*)ring.a[1];
+  int32_t* s_pos = (int32_t*)ring.w[0];  // [128][k]
+  float* s_w = (float*)ring.w[1];        // [128][k]
+  if (wave_cols) {
+#pragma unroll
+    for (int j = 0; j < NRH; ++j) {
+      const int rb = 2 * j + rg;
+      if (32 * rb >= tl.rows) break;  // uniform
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
+        uint16_t* srow = (row < 64 ? s_lo + row * 256 : s_hi + (row - 64) * 256);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) srow[64 * cg + 32 * cb + l32] = (uint16_t)f32_to_bf16(acc[j][cb][r]);
+      }
+    }
+  }
+  for (int e = tid; e < tl.rows * k; e += 512) {
+    const int64_t a = ((int64_t)tl.pos0 + e / k) * k + e % k;
+    s_pos[e] = p.inv[a];
+    s_w[e] = p.w[a];
+  }
+  __syncthreads();
+  const int c0 = panel * NWR;                                // first column of the panel
+  const int nq = (p.H - c0 < NWR ? p.H - c0 : NWR) / 8;    // 8-column chunks in the panel
+  const int nch = tl.rows * 32;
+  // two chunks per thread and step (rows row and row + 16): 2 x 8 y loads in flight
+  for (int c = tid; c < nch; c += 1024) {
+    int row[2], q[2];
+    bool ok[2];
+    float a8[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cu = c + 512 * u;
+      row[u] = cu >> 5;
+      q[u] = cu & 31;
+      ok[u] = cu < nch && q[u] < nq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a8[u][e] = 0.0f;
+    }
+    for (int jb = 0; jb < k; jb += 8) {
+      u32x4_t v[2][8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (ok[u] && jb + jj < k)
+            v[u][jj] = *(const u32x4_t*)(p.y_r + (int64_t)s_pos[row[u] * k + jb + jj] * p.H + c0 + 8 * q[u]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (!ok[u]) continue;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          if (jb + jj >= k) break;
+          const float wj = s_w[row[u] * k + jb + jj];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            a8[u][2 * qq] += wj * bf16_lo(v[u][jj][qq]);
+            a8[u][2 * qq + 1] += wj * bf16_hi(v[u][jj][qq]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!ok[u]) continue;
+      const uint16_t* srow = (row[u] < 64 ? s_lo + row[u] * 256 : s_hi + (row[u] - 64) * 256) + 8 * q[u];
+      const u32x4_t sv = *(const u32x4_t*)srow;
+      u32x4_t o;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        a8[u][2 * qq] += bf16_lo(sv[qq]);
+        a8[u][2 * qq + 1] += bf16_hi(sv[qq]);
+        o[qq] = pack_bf16x2(a8[u][2 * qq], a8[u][2 * qq + 1]);
+      }
+      *(u32x4_t*)(p.out + ((int64_t)tl.pos0 + row[u]) * p.H + c0 + 8 * q[u]) = o;
+    }
+  }
+}
+
 // One tile, eight waves (two per SIMD, so one wave's LDS and memory stalls
 // overlap the other's MFMAs).  Wave w = 4 rg + cg: column group cg, row group
 // rg.  MODE 0: h = silu(A Wg^T) * (A Wu^T) over a 128-column panel of I;
@@ -158,7 +260,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   auto srcq = [&](int blk) { return (lane & 7) ^ ((4 * (blk & 1) + (lr >> 1)) & 7); };
 
   int K, N, ncol0, ldw;
-  if (MODE == 0) {
+  if (MODE == 0) {  // gate/up; MODE 1 and 2: down
     K = p.H;
     N = Ig;
     ncol0 = panel * (NWR / 2) + 32 * cg;
@@ -370,6 +472,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   // every wave's reads done before the activation stage is reused for staging
   wait_vm_lgkm0<0>();
   barrier_only();
+  if (MODE == 2) {
+    combine_epilogue<NRH>(p, tl, panel, ring, acc, wave_cols, cg, rg, half, l32);
+    return;
+  }
   if (!wave_cols) return;
   u32x4_t* smem = ring.a[0];
 
@@ -423,7 +529,20 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmArgs p) {
   //      (its activation rows are re-read from that XCD's L2), the last tiles
   //      of the block map first (the shared expert's full 256-row tiles, the
   //      heaviest, start early and spread over all XCDs)
-  const int nt = *p.ntiles < p.max_tiles ? *p.ntiles : p.max_tiles;
+  if (MODE == 2) {  // the shared expert's tokens in tiles of 128, panel-minor
+    const int tile = blockIdx.x / p.npan, panel = blockIdx.x % p.npan;
+    const int64_t r0 = (int64_t)tile * 128;
+    if (r0 >= p.M) return;
+    const int rows = (int)(p.M - r0 < 128 ? p.M - r0 : 128);
+    const Tile tl{p.E, (int)r0, rows, (int)r0};
+    if (rows > 64)
+      gemm_tile<2, 4, Q4>(p, tl, panel, rg);
+    else
+      gemm_tile<2, 2, Q4>(p, tl, panel, rg);
+    return;
+  }
+  const int ntl = *p.ntiles - p.skip_tail;
+  const int nt = ntl < p.max_tiles ? ntl : p.max_tiles;
   const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
   const int j = local / p.npan, panel = local % p.npan;  // j-th tile of this XCD
   const int t = nt - 1 - (8 * j + (7 - xcd));            // from the end, dealt round-robin
@@ -517,8 +636,9 @@ hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const
 
 hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
                             const uint16_t* shared_w, const Tile* tiles, const int32_t* ntiles,
-                            uint16_t* y_r, uint16_t* y_s, const Plan& pl, const Launch& lc) {
+                            uint16_t* y_r, uint16_t* y_s, int skip_tail, const Plan& pl, const Launch& lc) {
   GemmArgs a{};
+  a.skip_tail = skip_tail;
   a.a_r = h_r;
   a.a_s = h_s;
   a.expert_w = expert_w;
@@ -572,9 +692,10 @@ hipError_t launch_gemm_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q
 }
 
 hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q4Weights& ex, const Q4Weights& sh,
-                               const Tile* tiles, const int32_t* ntiles, uint16_t* y_r, uint16_t* y_s, const Plan& pl,
-                               const Launch& lc) {
+                               const Tile* tiles, const int32_t* ntiles, uint16_t* y_r, uint16_t* y_s, int skip_tail,
+                               const Plan& pl, const Launch& lc) {
   GemmArgs a{};
+  a.skip_tail = skip_tail;
   a.a_r = h_r;
   a.a_s = h_s;
   a.ex_codes = ex.codes;
@@ -594,6 +715,48 @@ hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
   return launch(lc, k_grouped_gemm<1, true>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
+}
+
+namespace {
+
+GemmArgs shared_combine_args(const uint16_t* h_s, const uint16_t* y_r, const float* w, const int32_t* inv,
+                             uint16_t* out, const Plan& pl) {
+  GemmArgs a{};
+  a.a_s = h_s;
+  a.y_r = y_r;
+  a.w = w;
+  a.inv = inv;
+  a.out = out;
+  a.M = pl.M;
+  a.H = pl.H;
+  a.E = pl.E;
+  a.I = pl.I;
+  a.Is = pl.Is;
+  a.k = pl.k;
+  a.npan = (pl.H + NWR - 1) / NWR;
+  a.tiled = pl.tiled ? 1 : 0;
+  return a;
+}
+
+unsigned shared_combine_grid(const Plan& pl) { return (unsigned)(((pl.M + 127) / 128) * ((pl.H + NWR - 1) / NWR)); }
+
+}  // namespace
+
+hipError_t launch_shared_down_combine(const uint16_t* h_s, const uint16_t* shared_w, const uint16_t* y_r,
+                                      const float* w, const int32_t* inv, uint16_t* out, const Plan& pl,
+                                      const Launch& lc) {
+  GemmArgs a = shared_combine_args(h_s, y_r, w, inv, out, pl);
+  a.shared_w = shared_w;
+  return launch(lc, k_grouped_gemm<2, false>, dim3(shared_combine_grid(pl)), dim3(512), a);
+}
+
+hipError_t launch_shared_down_combine_q4(const uint16_t* h_s, const Q4Weights& sh, const uint16_t* y_r,
+                                         const float* w, const int32_t* inv, uint16_t* out, const Plan& pl,
+                                         const Launch& lc) {
+  GemmArgs a = shared_combine_args(h_s, y_r, w, inv, out, pl);
+  a.sh_codes = sh.codes;
+  a.sh_groups = sh.groups;
+  return launch(lc, k_grouped_gemm<2, true>, dim3(shared_combine_grid(pl)), dim3(512), a);
 }
 
 }  // namespace moe

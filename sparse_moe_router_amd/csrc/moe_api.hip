@@ -113,7 +113,6 @@ bool make_plan(Plan* p, int64_t M, int H, int E, int I, int Is, int k, bool gemv
     ok &= place(&off, &p->h_r, A * I * 2);
     ok &= place(&off, &p->h_s, (uint64_t)M * Is * 2);
     ok &= place(&off, &p->y_r, A * H * 2);
-    ok &= place(&off, &p->y_s, (uint64_t)M * H * 2);
   }
   p->total = align256(off);
   return ok;
@@ -443,21 +442,33 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   uint16_t* h_r = ws_ptr<uint16_t>(workspace, p.h_r);
   uint16_t* h_s = ws_ptr<uint16_t>(workspace, p.h_s);
   uint16_t* y_r = ws_ptr<uint16_t>(workspace, p.y_r);
-  uint16_t* y_s = ws_ptr<uint16_t>(workspace, p.y_s);
-  const Tile* tiles = ws_ptr<Tile>(workspace, p.tiles);
-  const int32_t* ntiles = ws_ptr<int32_t>(workspace, p.ntiles);
+  const int32_t* inv = ws_ptr<int32_t>(workspace, p.inv);
+  // with a shared expert, its down GEMM carries the weighted combine (its tiles
+  // are left out of the routed down GEMM); without one, a plain combine follows
+  const int skip = p.shared ? (int)((p.M + kTileM - 1) / kTileM) : 0;
+  // the block map where the scan wrote it: the caller's buffers when it asked for them
+  const Tile* tiles = (routing && routing->tiles) ? (const Tile*)routing->tiles : ws_ptr<Tile>(workspace, p.tiles);
+  const int32_t* ntiles = (routing && routing->num_tiles) ? routing->num_tiles : ws_ptr<int32_t>(workspace, p.ntiles);
   if ((e = tr.run(MOE_K_GEMM_GATEUP, [&](const Launch& lc) {
          return wt.q4 ? launch_gemm_gateup_q4(xb, wt.eq, wt.sq, perm, tiles, ntiles, h_r, h_s, p, lc)
                       : launch_gemm_gateup(xb, wt.ew, wt.sw, perm, tiles, ntiles, h_r, h_s, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = tr.run(MOE_K_GEMM_DOWN, [&](const Launch& lc) {
-         return wt.q4 ? launch_gemm_down_q4(h_r, h_s, wt.eq, wt.sq, tiles, ntiles, y_r, y_s, p, lc)
-                      : launch_gemm_down(h_r, h_s, wt.ew, wt.sw, tiles, ntiles, y_r, y_s, p, lc);
+         return wt.q4 ? launch_gemm_down_q4(h_r, h_s, wt.eq, wt.sq, tiles, ntiles, y_r, nullptr, skip, p, lc)
+                      : launch_gemm_down(h_r, h_s, wt.ew, wt.sw, tiles, ntiles, y_r, nullptr, skip, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
+  if (p.shared) {
+    if ((e = tr.run(MOE_K_SHARED_DOWN_COMBINE, [&](const Launch& lc) {
+           return wt.q4 ? launch_shared_down_combine_q4(h_s, wt.sq, y_r, w, inv, (uint16_t*)out, p, lc)
+                        : launch_shared_down_combine(h_s, wt.sw, y_r, w, inv, (uint16_t*)out, p, lc);
+         })) != hipSuccess)
+      return hip_fail(e);
+    return MOE_OK;
+  }
   if ((e = tr.run(MOE_K_COMBINE, [&](const Launch& lc) {
-         return launch_combine(y_r, y_s, w, ws_ptr<int32_t>(workspace, p.inv), (uint16_t*)out, p, lc);
+         return launch_combine(y_r, nullptr, w, inv, (uint16_t*)out, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
   return MOE_OK;

@@ -65,7 +65,7 @@ struct Plan {
   int64_t nchunk;
   int64_t max_tiles;
   // byte offsets into the workspace (all 256-aligned)
-  size_t logits, ids, w, cmask, cbase, counts, offsets, perm, inv, tiles, ntiles, h_r, h_s, y_r, y_s;
+  size_t logits, ids, w, cmask, cbase, counts, offsets, perm, inv, tiles, ntiles, h_r, h_s, y_r;
   size_t un_count, un_exp, un_off, un_pair, un_unit;  // small-batch path: union of the selected experts
   size_t arrive;  // decode path, two launches: arrival counters of the gate/up workgroups, one per slot
   size_t total;
@@ -123,17 +123,27 @@ hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const
 hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
                               const int32_t* perm, const Tile* tiles, const int32_t* ntiles,
                               uint16_t* h_r, uint16_t* h_s, const Plan& p, const Launch& lc);
-// Grouped down GEMM -> y (bf16).
+// Grouped down GEMM -> y (bf16), leaving out the last skip_tail tiles of
+// the block map (the shared expert's, when launch_shared_down_combine does them).
 hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
                             const uint16_t* shared_w, const Tile* tiles, const int32_t* ntiles,
-                            uint16_t* y_r, uint16_t* y_s, const Plan& p, const Launch& lc);
+                            uint16_t* y_r, uint16_t* y_s, int skip_tail, const Plan& p, const Launch& lc);
+// The shared expert's down GEMM over the tokens in tiles of 128, with the
+// weighted combine of the routed rows in its epilogue:
+// out[t] = sum_j w[t,j] y_r[inv[t*k+j]] + (Sd h_s[t]) (bf16 out).
+hipError_t launch_shared_down_combine(const uint16_t* h_s, const uint16_t* shared_w, const uint16_t* y_r,
+                                      const float* w, const int32_t* inv, uint16_t* out, const Plan& p,
+                                      const Launch& lc);
 // The two grouped GEMMs reading 4-bit weights (same outputs and layouts).
 hipError_t launch_gemm_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const int32_t* perm,
                                  const Tile* tiles, const int32_t* ntiles, uint16_t* h_r, uint16_t* h_s,
                                  const Plan& p, const Launch& lc);
 hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q4Weights& ex, const Q4Weights& sh,
-                               const Tile* tiles, const int32_t* ntiles, uint16_t* y_r, uint16_t* y_s, const Plan& p,
-                               const Launch& lc);
+                               const Tile* tiles, const int32_t* ntiles, uint16_t* y_r, uint16_t* y_s, int skip_tail,
+                               const Plan& p, const Launch& lc);
+hipError_t launch_shared_down_combine_q4(const uint16_t* h_s, const Q4Weights& sh, const uint16_t* y_r,
+                                         const float* w, const int32_t* inv, uint16_t* out, const Plan& p,
+                                         const Launch& lc);
 // out[t] = y_s[t] + sum_j w[t,j] y_r[inv[t*k+j]]  (bf16 out)
 hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float* w, const int32_t* inv,
                           uint16_t* out, const Plan& p, const Launch& lc);

@@ -38,15 +38,25 @@ def expected_tiles(counts, offsets, M, shared):
 
 
 def run_blockmap(x, r, ex, sh, k, bias=None, I=None, Is=None):
+    """One grouped-path call that exports the block map.  Its workspace is filled with 0x7F bytes
+    first: the grouped GEMMs must take the block map from the exported buffers the scan wrote (a
+    tile list read from this workspace would point far outside every buffer).  The output is
+    compared bit for bit with the same call exporting nothing."""
     M, H = x.shape
     E = r.shape[0]
-    cap = moe.block_map_capacity(M, H, E, I, Is, k, flags=moe.FLAG_FORCE_GEMM)
+    f = moe.FLAG_FORCE_GEMM
+    cap = moe.block_map_capacity(M, H, E, I, Is, k, flags=f)
     rb = routing_buffers(M, E, k)
     rb["tiles"] = torch.full((cap, 4), -1, dtype=torch.int32, device="cuda")
     rb["num_tiles"] = torch.full((1,), -1, dtype=torch.int32, device="cuda")
-    moe.forward(x, r, ex, sh, k, routing=rb, router_bias=bias, flags=moe.FLAG_FORCE_GEMM)
+    ws = torch.full((moe.workspace_size(M, H, E, I, Is, k, flags=f),), 0x7F, dtype=torch.uint8, device="cuda")
+    out = moe.forward(x, r, ex, sh, k, routing=rb, router_bias=bias, flags=f, workspace=ws)
+    ref = moe.forward(x, r, ex, sh, k, router_bias=bias, flags=f)
     torch.cuda.synchronize()
-    return {n: t.cpu().numpy() for n, t in rb.items()}, cap
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "exporting the block map changed the output"
+    res = {n: t.cpu().numpy() for n, t in rb.items()}
+    res["out"] = out.float().cpu().numpy()
+    return res, cap
 
 
 def check_blockmap(g, cap, M, k, shared):
@@ -97,9 +107,13 @@ def test_block_map_skewed_prefill():
 def test_block_map_hot_and_edge(M, E, k, shared):
     """A bias that sends every token to expert 5 first (or a single expert), one row, k = E, and
     groups just over a multiple of the tile height."""
-    x, r, ex, s, bias = rand_case(M, 128, E, k, 64, 64 if shared else 0, seed=M, hot=5 if E > 5 else None)
+    Is = 64 if shared else 0
+    x, r, ex, s, bias = rand_case(M, 128, E, k, 64, Is, seed=M, hot=5 if E > 5 else None)
     g, cap = run_blockmap(upload(x), upload(r), upload(ex), upload(s) if shared else None, k,
-                          bias=None if bias is None else torch.from_numpy(bias).cuda(), I=64, Is=64 if shared else 0)
+                          bias=None if bias is None else torch.from_numpy(bias).cuda(), I=64, Is=Is)
     check_blockmap(g, cap, M, k, shared)
     if E > 5:
         assert g["counts"][5] == M
+    orc = O.moe_forward(x, r, ex, s, k, 64, bias=bias, I_shared=Is)
+    rel = O.rel_err_per_token(g["out"], orc["out"])
+    assert rel.max() <= 1e-2, rel.max()

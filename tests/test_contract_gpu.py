@@ -106,7 +106,7 @@ def test_two_streams_two_workspaces(M):
         assert torch.equal(outs_b[i].view(torch.int16), ref_b.view(torch.int16)), f"stream b call {i}"
 
 
-PATH_KERNELS = {1: [8, 9, 10], 8: [11, 12, 13, 14], 300: [1, 2, 3, 4, 5, 6, 7], -1: [15, 16]}  # moe_kernel_t ids
+PATH_KERNELS = {1: [8, 9, 10], 8: [11, 12, 13, 14], 300: [1, 2, 3, 4, 5, 6, 17], -1: [15, 16]}  # moe_kernel_t ids
 TWO = moe.FLAG_DECODE_TWO_LAUNCH
 
 
