@@ -60,7 +60,9 @@ struct GemmArgs {
   const float* w;       // MODE 2: routing weights [M][k]
   const int32_t* inv;   // MODE 2: group position of each assignment [M*k]
   uint16_t* out;        // MODE 2: the layer's output [M][H]
-  int skip_tail;        // MODE 1: tiles at the end of the block map left out (the shared expert's, done by MODE 2)
+  int skip_tail;        // tiles at the end of the block map left out (the shared expert's, done elsewhere)
+  int sgu_units;        // MODE 1: leading workgroups that run the shared expert's gate/up tiles
+  int sgu_npan;         // MODE 1: gate/up panels of the shared expert
   int64_t M;
   int H, E, I, Is, k;
   int npan;
@@ -128,9 +130,9 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t c, uint32_t g) {
 // outputs S, rounded to bf16, are staged in the idle LDS rings (rows 0-63 in
 // ring.a[0], 64-127 in ring.a[1], 512 bytes a row), the tile's inv / w
 // entries beside them, then all 512 threads build out[t] = sum_j w[t,j] *
-// y_r[inv[t,j]] (fp32, slot order) + S[t], rounded once to bf16, two
-// 8-column chunks (16-byte loads of each y row) per thread and step: the
-// arithmetic of the stand-alone combine.
+// y_r[inv[t,j]] (fp32, slot order) + S[t], rounded once to bf16, 8 columns
+// (16-byte loads of each y row) per thread and step: the arithmetic of the
+// stand-alone combine.
 template <int NRH>
 __device__ __forceinline__ void combine_epilogue(const GemmArgs& p, const Tile& tl, int panel, const Ring& ring,
                                                  const f32x16_t (&acc)[NRH][2], bool wave_cols, int cg, int rg,
@@ -162,58 +164,38 @@ __device__ __forceinline__ void combine_epilogue(const GemmArgs& p, const Tile& 
   __syncthreads();
   const int c0 = panel * NWR;                                // first column of the panel
   const int nq = (p.H - c0 < NWR ? p.H - c0 : NWR) / 8;    // 8-column chunks in the panel
-  const int nch = tl.rows * 32;
-  // two chunks per thread and step (rows row and row + 16): 2 x 8 y loads in flight
-  for (int c = tid; c < nch; c += 1024) {
-    int row[2], q[2];
-    bool ok[2];
-    float a8[2][8];
+  for (int c = tid; c < tl.rows * 32; c += 512) {
+    const int row = c >> 5, q = c & 31;
+    if (q >= nq) continue;
+    const int64_t t = (int64_t)tl.pos0 + row;
+    const int col = c0 + 8 * q;
+    float a8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int jb = 0; jb < k; jb += 8) {  // eight rows' loads in flight at a time
+      u32x4_t v[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int cu = c + 512 * u;
-      row[u] = cu >> 5;
-      q[u] = cu & 31;
-      ok[u] = cu < nch && q[u] < nq;
+      for (int jj = 0; jj < 8; ++jj)
+        if (jb + jj < k) v[jj] = *(const u32x4_t*)(p.y_r + (int64_t)s_pos[row * k + jb + jj] * p.H + col);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a8[u][e] = 0.0f;
-    }
-    for (int jb = 0; jb < k; jb += 8) {
-      u32x4_t v[2][8];
+      for (int jj = 0; jj < 8; ++jj) {
+        if (jb + jj >= k) break;
+        const float wj = s_w[row * k + jb + jj];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          if (ok[u] && jb + jj < k)
-            v[u][jj] = *(const u32x4_t*)(p.y_r + (int64_t)s_pos[row[u] * k + jb + jj] * p.H + c0 + 8 * q[u]);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (!ok[u]) continue;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          if (jb + jj >= k) break;
-          const float wj = s_w[row[u] * k + jb + jj];
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            a8[u][2 * qq] += wj * bf16_lo(v[u][jj][qq]);
-            a8[u][2 * qq + 1] += wj * bf16_hi(v[u][jj][qq]);
-          }
+        for (int qq = 0; qq < 4; ++qq) {
+          a8[2 * qq] += wj * bf16_lo(v[jj][qq]);
+          a8[2 * qq + 1] += wj * bf16_hi(v[jj][qq]);
         }
       }
     }
+    const uint16_t* srow = (row < 64 ? s_lo + row * 256 : s_hi + (row - 64) * 256) + 8 * q;
+    const u32x4_t sv = *(const u32x4_t*)srow;
+    u32x4_t o;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (!ok[u]) continue;
-      const uint16_t* srow = (row[u] < 64 ? s_lo + row[u] * 256 : s_hi + (row[u] - 64) * 256) + 8 * q[u];
-      const u32x4_t sv = *(const u32x4_t*)srow;
-      u32x4_t o;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        a8[u][2 * qq] += bf16_lo(sv[qq]);
-        a8[u][2 * qq + 1] += bf16_hi(sv[qq]);
-        o[qq] = pack_bf16x2(a8[u][2 * qq], a8[u][2 * qq + 1]);
-      }
-      *(u32x4_t*)(p.out + ((int64_t)tl.pos0 + row[u]) * p.H + c0 + 8 * q[u]) = o;
+    for (int qq = 0; qq < 4; ++qq) {
+      a8[2 * qq] += bf16_lo(sv[qq]);
+      a8[2 * qq + 1] += bf16_hi(sv[qq]);
+      o[qq] = pack_bf16x2(a8[2 * qq], a8[2 * qq + 1]);
     }
+    *(u32x4_t*)(p.out + t * p.H + col) = o;
   }
 }
 
@@ -541,9 +523,29 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmArgs p) {
       gemm_tile<2, 2, Q4>(p, tl, panel, rg);
     return;
   }
+  int b = blockIdx.x;
+  if (MODE == 1 && p.sgu_units > 0) {
+    // leading workgroups: the shared expert's gate/up tiles of 256 tokens (they
+    // do not depend on the routing and their h is read only by the launch
+    // after this one), dispatched first, as the longest units of the launch
+    if (b < p.sgu_units) {
+      const int tile = b / p.sgu_npan, panel = b % p.sgu_npan;
+      const int64_t r0 = (int64_t)tile * BM;
+      if (r0 >= p.M || panel * (NWR / 2) >= p.Is) return;
+      const Tile tl{p.E, (int)r0, (int)(p.M - r0 < BM ? p.M - r0 : BM), (int)r0};
+      switch (((tl.rows + 63) >> 6) << 1) {
+        case 2: gemm_tile<0, 2, Q4>(p, tl, panel, rg); break;
+        case 4: gemm_tile<0, 4, Q4>(p, tl, panel, rg); break;
+        case 6: gemm_tile<0, 6, Q4>(p, tl, panel, rg); break;
+        default: gemm_tile<0, 8, Q4>(p, tl, panel, rg); break;
+      }
+      return;
+    }
+    b -= p.sgu_units;  // a multiple of 8: the XCD of b is still b % 8
+  }
   const int ntl = *p.ntiles - p.skip_tail;
   const int nt = ntl < p.max_tiles ? ntl : p.max_tiles;
-  const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
+  const int xcd = b & 7, local = b >> 3;
   const int j = local / p.npan, panel = local % p.npan;  // j-th tile of this XCD
   const int t = nt - 1 - (8 * j + (7 - xcd));            // from the end, dealt round-robin
   if (t < 0) return;
@@ -607,12 +609,26 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
 // 8 XCDs x (most tiles per XCD) x panels: every tile's panels have a workgroup
 unsigned xcd_grid(int64_t max_tiles, int npan) { return (unsigned)(8 * ((max_tiles + 7) / 8) * npan); }
 
+// The down launch's leading workgroups for the shared expert's gate/up tiles
+// (x_shared_gu non-null: the gate/up launch left them out): one per (256-token
+// tile, gate/up panel), rounded up to a multiple of 8 so that the down
+// workgroups keep their XCD order.
+void shared_gateup_units(GemmArgs* a, const uint16_t* x, uint16_t* h_s, const Plan& pl) {
+  if (!x || !h_s || !pl.shared) return;
+  a->a_x = x;
+  a->out_s = h_s;
+  a->sgu_npan = (pl.Is + NWR / 2 - 1) / (NWR / 2);
+  const int64_t units = ((pl.M + BM - 1) / BM) * a->sgu_npan;
+  a->sgu_units = (int)(8 * ((units + 7) / 8));
+}
+
 }  // namespace
 
 hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
                               const int32_t* perm, const Tile* tiles, const int32_t* ntiles,
-                              uint16_t* h_r, uint16_t* h_s, const Plan& pl, const Launch& lc) {
+                              uint16_t* h_r, uint16_t* h_s, int skip_tail, const Plan& pl, const Launch& lc) {
   GemmArgs a{};
+  a.skip_tail = skip_tail;
   a.a_x = x;
   a.expert_w = expert_w;
   a.shared_w = shared_w;
@@ -634,9 +650,10 @@ hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const
   return launch(lc, k_grouped_gemm<0, false>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 
-hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
+hipError_t launch_gemm_down(const uint16_t* h_r, uint16_t* h_s, const uint16_t* expert_w,
                             const uint16_t* shared_w, const Tile* tiles, const int32_t* ntiles,
-                            uint16_t* y_r, uint16_t* y_s, int skip_tail, const Plan& pl, const Launch& lc) {
+                            uint16_t* y_r, uint16_t* y_s, int skip_tail, const uint16_t* x_shared_gu,
+                            const Plan& pl, const Launch& lc) {
   GemmArgs a{};
   a.skip_tail = skip_tail;
   a.a_r = h_r;
@@ -656,7 +673,8 @@ hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
   a.tiled = pl.tiled ? 1 : 0;
-  return launch(lc, k_grouped_gemm<1, false>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
+  shared_gateup_units(&a, x_shared_gu, h_s, pl);  // last: it sets a_x and out_s
+  return launch(lc, k_grouped_gemm<1, false>, dim3(a.sgu_units + xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 
 hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float* w, const int32_t* inv,
@@ -667,8 +685,9 @@ hipError_t launch_combine(const uint16_t* y_r, const uint16_t* y_s, const float*
 
 hipError_t launch_gemm_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const int32_t* perm,
                                  const Tile* tiles, const int32_t* ntiles, uint16_t* h_r, uint16_t* h_s,
-                                 const Plan& pl, const Launch& lc) {
+                                 int skip_tail, const Plan& pl, const Launch& lc) {
   GemmArgs a{};
+  a.skip_tail = skip_tail;
   a.a_x = x;
   a.ex_codes = ex.codes;
   a.ex_groups = ex.groups;
@@ -691,9 +710,9 @@ hipError_t launch_gemm_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q
   return launch(lc, k_grouped_gemm<0, true>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 
-hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q4Weights& ex, const Q4Weights& sh,
+hipError_t launch_gemm_down_q4(const uint16_t* h_r, uint16_t* h_s, const Q4Weights& ex, const Q4Weights& sh,
                                const Tile* tiles, const int32_t* ntiles, uint16_t* y_r, uint16_t* y_s, int skip_tail,
-                               const Plan& pl, const Launch& lc) {
+                               const uint16_t* x_shared_gu, const Plan& pl, const Launch& lc) {
   GemmArgs a{};
   a.skip_tail = skip_tail;
   a.a_r = h_r;
@@ -714,7 +733,8 @@ hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q
   a.k = pl.k;
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
-  return launch(lc, k_grouped_gemm<1, true>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
+  shared_gateup_units(&a, x_shared_gu, h_s, pl);  // last: it sets a_x and out_s
+  return launch(lc, k_grouped_gemm<1, true>, dim3(a.sgu_units + xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 
 namespace {

@@ -443,20 +443,25 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   uint16_t* h_s = ws_ptr<uint16_t>(workspace, p.h_s);
   uint16_t* y_r = ws_ptr<uint16_t>(workspace, p.y_r);
   const int32_t* inv = ws_ptr<int32_t>(workspace, p.inv);
-  // with a shared expert, its down GEMM carries the weighted combine (its tiles
-  // are left out of the routed down GEMM); without one, a plain combine follows
+  // with a shared expert, its tiles (the last `skip` of the block map) are left
+  // out of both grouped launches: its gate/up tiles run at the start of the
+  // down launch, its down GEMM carries the weighted combine in a launch of
+  // its own; without one, a plain combine follows the down launch
   const int skip = p.shared ? (int)((p.M + kTileM - 1) / kTileM) : 0;
   // the block map where the scan wrote it: the caller's buffers when it asked for them
   const Tile* tiles = (routing && routing->tiles) ? (const Tile*)routing->tiles : ws_ptr<Tile>(workspace, p.tiles);
   const int32_t* ntiles = (routing && routing->num_tiles) ? routing->num_tiles : ws_ptr<int32_t>(workspace, p.ntiles);
+  // the shared expert's gate/up tiles run at the start of the down launch (the
+  // shared down + combine launch after it is the first to read their h)
+  const uint16_t* x_sgu = p.shared ? xb : nullptr;
   if ((e = tr.run(MOE_K_GEMM_GATEUP, [&](const Launch& lc) {
-         return wt.q4 ? launch_gemm_gateup_q4(xb, wt.eq, wt.sq, perm, tiles, ntiles, h_r, h_s, p, lc)
-                      : launch_gemm_gateup(xb, wt.ew, wt.sw, perm, tiles, ntiles, h_r, h_s, p, lc);
+         return wt.q4 ? launch_gemm_gateup_q4(xb, wt.eq, wt.sq, perm, tiles, ntiles, h_r, h_s, skip, p, lc)
+                      : launch_gemm_gateup(xb, wt.ew, wt.sw, perm, tiles, ntiles, h_r, h_s, skip, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = tr.run(MOE_K_GEMM_DOWN, [&](const Launch& lc) {
-         return wt.q4 ? launch_gemm_down_q4(h_r, h_s, wt.eq, wt.sq, tiles, ntiles, y_r, nullptr, skip, p, lc)
-                      : launch_gemm_down(h_r, h_s, wt.ew, wt.sw, tiles, ntiles, y_r, nullptr, skip, p, lc);
+         return wt.q4 ? launch_gemm_down_q4(h_r, h_s, wt.eq, wt.sq, tiles, ntiles, y_r, nullptr, skip, x_sgu, p, lc)
+                      : launch_gemm_down(h_r, h_s, wt.ew, wt.sw, tiles, ntiles, y_r, nullptr, skip, x_sgu, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
   if (p.shared) {

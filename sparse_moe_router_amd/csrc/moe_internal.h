@@ -119,15 +119,19 @@ hipError_t launch_route_scan(const uint64_t* cmask, int32_t* cbase, int32_t* cou
 // perm / inv from the chunk masks and bases.
 hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const int32_t* cbase,
                                 int32_t* perm, int32_t* inv, int64_t M, int E, int k, const Launch& lc);
-// Grouped gate/up GEMM + SwiGLU -> h (bf16).
+// Grouped gate/up GEMM + SwiGLU -> h (bf16), leaving out the last skip_tail
+// tiles of the block map (the shared expert's, when the down launch runs them).
 hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
                               const int32_t* perm, const Tile* tiles, const int32_t* ntiles,
-                              uint16_t* h_r, uint16_t* h_s, const Plan& p, const Launch& lc);
+                              uint16_t* h_r, uint16_t* h_s, int skip_tail, const Plan& p, const Launch& lc);
 // Grouped down GEMM -> y (bf16), leaving out the last skip_tail tiles of
-// the block map (the shared expert's, when launch_shared_down_combine does them).
-hipError_t launch_gemm_down(const uint16_t* h_r, const uint16_t* h_s, const uint16_t* expert_w,
+// the block map (the shared expert's, when launch_shared_down_combine does
+// them).  With x_shared_gu given, the launch first runs the shared expert's
+// gate/up tiles (x -> h_s), which the gate/up launch then leaves out.
+hipError_t launch_gemm_down(const uint16_t* h_r, uint16_t* h_s, const uint16_t* expert_w,
                             const uint16_t* shared_w, const Tile* tiles, const int32_t* ntiles,
-                            uint16_t* y_r, uint16_t* y_s, int skip_tail, const Plan& p, const Launch& lc);
+                            uint16_t* y_r, uint16_t* y_s, int skip_tail, const uint16_t* x_shared_gu,
+                            const Plan& p, const Launch& lc);
 // The shared expert's down GEMM over the tokens in tiles of 128, with the
 // weighted combine of the routed rows in its epilogue:
 // out[t] = sum_j w[t,j] y_r[inv[t*k+j]] + (Sd h_s[t]) (bf16 out).
@@ -137,10 +141,10 @@ hipError_t launch_shared_down_combine(const uint16_t* h_s, const uint16_t* share
 // The two grouped GEMMs reading 4-bit weights (same outputs and layouts).
 hipError_t launch_gemm_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const int32_t* perm,
                                  const Tile* tiles, const int32_t* ntiles, uint16_t* h_r, uint16_t* h_s,
-                                 const Plan& p, const Launch& lc);
-hipError_t launch_gemm_down_q4(const uint16_t* h_r, const uint16_t* h_s, const Q4Weights& ex, const Q4Weights& sh,
+                                 int skip_tail, const Plan& p, const Launch& lc);
+hipError_t launch_gemm_down_q4(const uint16_t* h_r, uint16_t* h_s, const Q4Weights& ex, const Q4Weights& sh,
                                const Tile* tiles, const int32_t* ntiles, uint16_t* y_r, uint16_t* y_s, int skip_tail,
-                               const Plan& p, const Launch& lc);
+                               const uint16_t* x_shared_gu, const Plan& p, const Launch& lc);
 hipError_t launch_shared_down_combine_q4(const uint16_t* h_s, const Q4Weights& sh, const uint16_t* y_r,
                                          const float* w, const int32_t* inv, uint16_t* out, const Plan& p,
                                          const Launch& lc);
