@@ -528,14 +528,14 @@ def bench_small(args, hip, moe, S, layers, xpool, Ms=(2, 4, 8, 16, 32, 64)):
 
 def gateup_roofline(kt, w, M, nonempty, q4, peaks=None):
     """Roofline position of the gate/up grouped GEMM (k_grouped_gemm<0>) for M rows: algorithmic
-    bytes (the gate/up weights of the experts that received rows and of the shared expert, x
-    read once; no intermediates) and FLOPs (2 * 2*I*H per assignment and per token for the
-    shared expert) per launch over its average event-timed duration; the bound is the resource
-    that work needs longer on at datasheet peaks."""
+    bytes (the gate/up weights of the routed experts that received rows, x read once; no
+    intermediates) and FLOPs (2 * 2*I*H per assignment) per launch over its average event-timed
+    duration; the bound is the resource that work needs longer on at datasheet peaks.  The
+    shared expert's gate/up tiles run in the down launch, so they count there, not here."""
     H, I, k = w.H, w.I, w.k
     wb = 0.5625 if q4 else 2  # weight bytes per element
-    gu_bytes = int((nonempty + 1) * 2 * I * H * wb) + M * H * 2
-    gu_flops = (M * k + M) * 2 * I * H * 2
+    gu_bytes = int(nonempty * 2 * I * H * wb) + M * H * 2
+    gu_flops = M * k * 2 * I * H * 2
     avg = sum(kt["gemm_gateup"]) / len(kt["gemm_gateup"])
     kname = "k_grouped_gemm<0, q4> (gate/up + SwiGLU)" if q4 else "k_grouped_gemm<0> (gate/up + SwiGLU)"
     traffic = traffic_for(f"k_grouped_gemm<0,q4>@{w.name}" if q4 else f"k_grouped_gemm<0>@{w.name}")

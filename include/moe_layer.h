@@ -290,7 +290,7 @@ moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void*
  *   - The scratch holds MOE_NOALLOC_SCRATCH_BYTES (64 MiB) on every
  *     device the library runs on, for the life of the process; a call whose
  *     moe_workspace_size() is larger returns MOE_ERR_WORKSPACE_TOO_SMALL and
- *     enqueues nothing (at H=2048, E=256, top-8, I=512: up to about 1,400
+ *     enqueues nothing (at H=2048, E=256, top-8, I=512: up to 1,553
  *     rows on the grouped path; the decode and small-batch paths always fit).
  *   - The scratch of the current device is used (hipGetDevice): make the
  *     stream's device current.  The first call on a device looks up that

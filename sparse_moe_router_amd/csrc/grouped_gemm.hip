@@ -512,7 +512,10 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmArgs p) {
   //      of the block map first (the shared expert's full 256-row tiles, the
   //      heaviest, start early and spread over all XCDs)
   if (MODE == 2) {  // the shared expert's tokens in tiles of 128, panel-minor
-    const int tile = blockIdx.x / p.npan, panel = blockIdx.x % p.npan;
+    // tile t on XCD t % 8 with all its panels: the tile's shared-expert h
+    // rows are fetched into that XCD's L2 once, not once per panel
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int tile = (local / p.npan) * 8 + xcd, panel = local % p.npan;
     const int64_t r0 = (int64_t)tile * 128;
     if (r0 >= p.M) return;
     const int rows = (int)(p.M - r0 < 128 ? p.M - r0 : 128);
@@ -758,7 +761,10 @@ GemmArgs shared_combine_args(const uint16_t* h_s, const uint16_t* y_r, const flo
   return a;
 }
 
-unsigned shared_combine_grid(const Plan& pl) { return (unsigned)(((pl.M + 127) / 128) * ((pl.H + NWR - 1) / NWR)); }
+// 8 XCDs x (most 128-token tiles per XCD) x panels
+unsigned shared_combine_grid(const Plan& pl) {
+  return (unsigned)(8 * (((pl.M + 127) / 128 + 7) / 8) * ((pl.H + NWR - 1) / NWR));
+}
 
 }  // namespace
 

@@ -41,15 +41,16 @@ def test_traffic_reported_only_for_unchanged_sources(tmp_path, monkeypatch):
 @pytest.mark.parametrize("q4,bound", [(False, "hbm"), (True, "mfma")])
 def test_gateup_roofline_bound_at_prefill(q4, bound):
     """At M = 4096 with every expert non-empty the bf16 gate/up GEMM needs longer on HBM than on
-    MFMA at datasheet peaks (1.13 GB vs 155 GFLOP), the 4-bit one longer on MFMA (0.36 GB)."""
+    MFMA at datasheet peaks (1.09 GB vs 137 GFLOP), the 4-bit one longer on MFMA (0.32 GB)."""
     w = S.PREFILL
     peaks = {"hbm_gbs": 6400.0, "mfma_tflops": 2000.0}
     r = bench.gateup_roofline({"gemm_gateup": [0.25, 0.25]}, w, w.M, w.E, q4, peaks)
     assert r["bound"] == bound and r["avg_us"] == 250.0
-    flops = (w.M * w.k + w.M) * 2 * w.I * w.H * 2
+    flops = w.M * w.k * 2 * w.I * w.H * 2
     wb = 0.5625 if q4 else 2
-    # algorithmic bytes only: gate/up weights of the non-empty experts + the shared expert, x once
-    nbytes = int((w.E + 1) * 2 * w.I * w.H * wb) + w.M * w.H * 2
+    # algorithmic bytes only: gate/up weights of the non-empty routed experts, x once (the shared
+    # expert's gate/up tiles run in the down launch)
+    nbytes = int(w.E * 2 * w.I * w.H * wb) + w.M * w.H * 2
     assert r["bytes_per_launch"] == nbytes and r["flops_per_launch"] == flops
     if bound == "hbm":
         assert r["frac"] == pytest.approx(nbytes / 250e-6 / 1e9 / bench.HBM_PEAK_GBS, abs=1e-4)
