@@ -90,6 +90,11 @@ struct Ring {
 __device__ __forceinline__ void dma16(const void* src, u32x4_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
+// The same with the non-temporal hint (streaming data read once: the weight
+// panel of an expert whose rows fit one tile).
+__device__ __forceinline__ void dma16_nt(const void* src, u32x4_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 2);
+}
 __device__ __forceinline__ void dma4(const void* src, uint32_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
 }
@@ -228,9 +233,9 @@ __device__ __forceinline__ void combine_epilogue(const GemmArgs& p, const Tile& 
 // Q4: a step's 64 K-values of a weight row are one group: the stage holds
 // the rows' 32 bytes of codes and their group words, expanded to bf16
 // operands in registers just before the MFMA.
-template <int MODE, int NRB, bool Q4>
+template <int MODE, int NRB, bool Q4, bool NT = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int panel, const Ring& ring) {
-  constexpr int NRH = NRB / 2;     // row blocks per row group
+  constexpr int NRH = (NRB + 1) / 2;  // row blocks of row group 0 (row group 1: NRB / 2)
   constexpr int U = DA * DW;       // unroll: every ring stage index static
   const bool is_shared = tl.g >= p.E;
   const int Ig = is_shared ? p.Is : p.I;
@@ -253,7 +258,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
     ncol0 = panel * NWR + WN * cg;
     ldw = Ig;
   }
-  const bool wave_cols = ncol0 < N;  // wave-uniform: does this wave own any output column?
+  // wave-uniform: does this wave own any output column (and, for one row
+  // block, any row)?
+  const bool wave_cols = ncol0 < N && (NRB > 1 || rg == 0);
   const int nsteps = K / BK;
 
   // ---- weight rows of column group cg: (col block cb, row l of 32) -> first element
@@ -337,7 +344,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
       if (rg == 0) dma4(gsrc + goff + (int64_t)s * 4, (uint32_t*)(st + 2 * NWR) + cg * 64);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(wsrc + woff[i] + (int64_t)s * wstep, st + (cg * 8 + rg * 4 + i) * 64);
+      for (int i = 0; i < 4; ++i) {
+        if (NT)
+          dma16_nt(wsrc + woff[i] + (int64_t)s * wstep, st + (cg * 8 + rg * 4 + i) * 64);
+        else
+          dma16(wsrc + woff[i] + (int64_t)s * wstep, st + (cg * 8 + rg * 4 + i) * 64);
+      }
     }
   };
 
@@ -356,14 +368,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   // wave there, instead of all transfers of a step queueing up front.  The
   // scheduling barriers keep that order (and the transfers after the barrier
   // of the step).
-  auto step = [&](const u32x4_t* sa, const u32x4_t* sw, u32x4_t* na, int a_next, u32x4_t* nw, int w_next) {
+  // RG: the wave's row group, a constant, so that row group 1 of an odd block
+  // count skips its last block (rows past the tile) without a branch
+  auto step = [&](auto rgc, const u32x4_t* sa, const u32x4_t* sw, u32x4_t* na, int a_next, u32x4_t* nw,
+                  int w_next) {
+    constexpr int RG = decltype(rgc)::value;
     u32x4_t af[2][NRH], bf[2][2];
     u32x4_t bq[2];
     uint32_t bg[2] = {0, 0};
     auto read_af = [&](u32x4_t (&f)[NRH], int kk) {
       const int q = (4 * half + kk) ^ swr;
 #pragma unroll
-      for (int j = 0; j < NRH; ++j) f[j] = sa[(32 * (2 * j + rg) + l32) * CPR + q];
+      for (int j = 0; j < NRH; ++j)
+        if (2 * j + RG < NRB) f[j] = sa[(32 * (2 * j + RG) + l32) * CPR + q];
     };
     auto read_bf = [&](u32x4_t (&f)[2], int kk) {
       const int q = (4 * half + kk) ^ swr;
@@ -392,6 +409,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
       for (int cb = 0; cb < 2; ++cb) bw[cb] = Q4 ? dequant8(bq[cb][kk], bg[cb]) : bf[kk & 1][cb];
 #pragma unroll
       for (int j = 0; j < NRH; ++j)
+        if (2 * j + RG < NRB)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
           acc[j][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[kk & 1][j]),
@@ -415,7 +433,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
 
   // The K loop, one copy per kind of wave (a branch inside the loop would
   // merge the compiler's wait bookkeeping of both kinds at every step).
-  auto kloop = [&](auto cols, auto nw) {
+  auto kloop = [&](auto cols, auto nw, auto rgc) {
     constexpr int NWC = decltype(nw)::value;
     for (int s0 = 0; s0 < nsteps; s0 += U) {
 #pragma unroll
@@ -433,7 +451,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
           wait_vm_lgkm0<NWC>();
         barrier_only();
         if (decltype(cols)::value) {
-          step(ring.a[u % DA], ring.w[u % DW], ring.a[(u + 1) % DA], clampst(s + 1), ring.w[(u + DW - 1) % DW],
+          step(rgc, ring.a[u % DA], ring.w[u % DW], ring.a[(u + 1) % DA], clampst(s + 1), ring.w[(u + DW - 1) % DW],
                clampst(s + DW - 1));
         } else {
           load_a(ring.a[(u + 1) % DA], clampst(s + 1));
@@ -447,9 +465,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   typedef std::integral_constant<int, Q4 ? 2 : 4> NW0;
   typedef std::integral_constant<int, Q4 ? 1 : 4> NW1;
   if (wave_cols) {
-    if (rg == 0) kloop(std::true_type{}, NW0{}); else kloop(std::true_type{}, NW1{});
+    if (rg == 0) kloop(std::true_type{}, NW0{}, std::integral_constant<int, 0>{});
+    else kloop(std::true_type{}, NW1{}, std::integral_constant<int, 1>{});
   } else {
-    if (rg == 0) kloop(std::false_type{}, NW0{}); else kloop(std::false_type{}, NW1{});
+    if (rg == 0) kloop(std::false_type{}, NW0{}, std::integral_constant<int, 0>{});
+    else kloop(std::false_type{}, NW1{}, std::integral_constant<int, 1>{});
   }
   // every wave's reads done before the activation stage is reused for staging
   wait_vm_lgkm0<0>();
@@ -498,6 +518,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// One routed tile, its inner loop specialised per count of 32-row blocks.
+template <int MODE, bool Q4, bool NT>
+__device__ __forceinline__ void routed_tile(const GemmArgs& p, const Tile& tl, int panel, const Ring& rg) {
+  switch ((tl.rows + 31) >> 5) {
+    case 1: gemm_tile<MODE, 1, Q4, NT>(p, tl, panel, rg); break;
+    case 2: gemm_tile<MODE, 2, Q4, NT>(p, tl, panel, rg); break;
+    case 3: gemm_tile<MODE, 3, Q4, NT>(p, tl, panel, rg); break;
+    case 4: gemm_tile<MODE, 4, Q4, NT>(p, tl, panel, rg); break;
+    case 5: gemm_tile<MODE, 5, Q4, NT>(p, tl, panel, rg); break;
+    case 6: gemm_tile<MODE, 6, Q4, NT>(p, tl, panel, rg); break;
+    case 7: gemm_tile<MODE, 7, Q4, NT>(p, tl, panel, rg); break;
+    default: gemm_tile<MODE, 8, Q4, NT>(p, tl, panel, rg); break;
   }
 }
 
@@ -557,14 +592,14 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmArgs p) {
     const int Ig = tl.g >= p.E ? p.Is : p.I;
     if (panel * (NWR / 2) >= Ig) return;
   }
-  // row blocks of 32, rounded up to even: the inner loop is specialised per count
-  const int nrb2 = ((tl.rows + 63) >> 6) << 1;
-  switch (nrb2) {
-    case 2: gemm_tile<MODE, 2, Q4>(p, tl, panel, rg); break;
-    case 4: gemm_tile<MODE, 4, Q4>(p, tl, panel, rg); break;
-    case 6: gemm_tile<MODE, 6, Q4>(p, tl, panel, rg); break;
-    default: gemm_tile<MODE, 8, Q4>(p, tl, panel, rg); break;
-  }
+  // bf16 weights of an expert whose rows fit one tile are read once in the
+  // launch: fetched with the non-temporal hint, they leave the caches to the
+  // activation rows (an expert split over several tiles is fetched by each of
+  // them and keeps the default policy, as does the shared expert)
+  if (!Q4 && tl.g < p.E && tl.r0 == 0 && tl.rows < BM)
+    routed_tile<MODE, Q4, true>(p, tl, panel, rg);
+  else
+    routed_tile<MODE, Q4, false>(p, tl, panel, rg);
 }
 
 // out[t] = sum_j w[t,j] * y_r[inv[t*k+j]] + y_s[t]: fp32 sums in slot order,

@@ -25,6 +25,13 @@
 //    bias b, w = s*q + b.  Codes: eight per 32-bit word, element 8i+j in bits
 //    4j..4j+3 (two per byte, low nibble first); groups: one 32-bit word each,
 //    s in the low half, b in the high half.
+//
+// The expert formats (WBf16T, WQ4 codes) load with the non-temporal hint: a
+// matrix-vector pass reads each expert weight once, and streamed with the
+// default policy those bytes push the activations, scores and h out of the
+// caches (the 40-layer decode graph: 18.6-19.0 -> 17.9-18.0 us per layer).
+// WBf16 keeps the default policy: it also serves the router rows, which the
+// row groups of the small-batch router re-read from cache.
 #pragma once
 
 #include "moe_internal.h"
@@ -63,7 +70,7 @@ struct WBf16T {
     int step;           // elements per K-step of its panel
     int swz;            // (R / 2) % 8
     __device__ __forceinline__ chunk_t load(int64_t k) const {
-      return *(const u32x4_t*)(p + (k >> 6) * step + 8 * (((int)(k >> 3) & 7) ^ swz));
+      return __builtin_nontemporal_load((const u32x4_t*)(p + (k >> 6) * step + 8 * (((int)(k >> 3) & 7) ^ swz)));
     }
   };
   __device__ __forceinline__ WBf16T block(int64_t e) const { return {p + e}; }
@@ -91,7 +98,9 @@ struct WQ4 {
   struct Row {
     const uint32_t* c;
     const uint32_t* g;
-    __device__ __forceinline__ chunk_t load(int64_t k) const { return {c[k >> 3], g[k >> 6]}; }
+    __device__ __forceinline__ chunk_t load(int64_t k) const {
+      return {__builtin_nontemporal_load(c + (k >> 3)), g[k >> 6]};
+    }
   };
   __device__ __forceinline__ WQ4 block(int64_t e) const { return {c + (e >> 3), g + (e >> 6)}; }
   __device__ __forceinline__ Row at_elem(int64_t e) const { return {c + (e >> 3), g + (e >> 6)}; }
