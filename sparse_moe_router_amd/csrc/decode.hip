@@ -465,7 +465,7 @@ hipError_t launch_decode_gateup(const uint16_t* x, const uint16_t* expert_w, con
                                 const Launch& lc) {
   const uint16_t* sw = p.shared ? shared_w : nullptr;
   if (p.tiled) return decode_gateup(x, WBf16T{expert_w}, WBf16T{sw}, logits, ids, w, h_dec, p, lc);
-  return decode_gateup(x, WBf16{expert_w}, WBf16{sw}, logits, ids, w, h_dec, p, lc);
+  return decode_gateup(x, WBf16S{expert_w}, WBf16S{sw}, logits, ids, w, h_dec, p, lc);
 }
 
 hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w, const int32_t* ids,
@@ -473,7 +473,7 @@ hipError_t launch_decode_down(const uint16_t* expert_w, const uint16_t* shared_w
                               const Launch& lc) {
   const uint16_t* sw = p.shared ? shared_w : nullptr;
   if (p.tiled) return decode_down(WBf16T{expert_w}, WBf16T{sw}, ids, w, h_dec, out, p, lc);
-  return decode_down(WBf16{expert_w}, WBf16{sw}, ids, w, h_dec, out, p, lc);
+  return decode_down(WBf16S{expert_w}, WBf16S{sw}, ids, w, h_dec, out, p, lc);
 }
 
 namespace {
@@ -520,7 +520,7 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* wr, const floa
                                const Plan& p, const Launch& lc) {
   const uint16_t* sw = p.shared ? shared_w : nullptr;
   if (p.tiled) return decode_route(x, wr, bias, logits, WBf16T{sw}, h_dec, arrivals, status, p, lc);
-  return decode_route(x, wr, bias, logits, WBf16{sw}, h_dec, arrivals, status, p, lc);
+  return decode_route(x, wr, bias, logits, WBf16S{sw}, h_dec, arrivals, status, p, lc);
 }
 
 hipError_t launch_decode_route_q4(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
@@ -535,7 +535,7 @@ hipError_t launch_decode_experts(const uint16_t* x, const uint16_t* expert_w, co
   const uint16_t* sw = p.shared ? shared_w : nullptr;
   if (p.tiled)
     return decode_experts(x, WBf16T{expert_w}, WBf16T{sw}, logits, ids, w, h_dec, arrivals, status, out, p, probe, lc);
-  return decode_experts(x, WBf16{expert_w}, WBf16{sw}, logits, ids, w, h_dec, arrivals, status, out, p, probe, lc);
+  return decode_experts(x, WBf16S{expert_w}, WBf16S{sw}, logits, ids, w, h_dec, arrivals, status, out, p, probe, lc);
 }
 
 hipError_t launch_decode_experts_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const float* logits,

@@ -179,7 +179,8 @@ __device__ __forceinline__ void combine_epilogue(const GemmArgs& p, const Tile& 
       u32x4_t v[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
-        if (jb + jj < k) v[jj] = *(const u32x4_t*)(p.y_r + (int64_t)s_pos[row * k + jb + jj] * p.H + col);
+        if (jb + jj < k)  // each y row is read once: non-temporal
+          v[jj] = __builtin_nontemporal_load((const u32x4_t*)(p.y_r + (int64_t)s_pos[row * k + jb + jj] * p.H + col));
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         if (jb + jj >= k) break;
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y_
   for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j = 0; j < k; ++j) {
-      const u32x4_t v = *(const u32x4_t*)(y_r + (int64_t)s_pos[j] * H + c);
+      const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)(y_r + (int64_t)s_pos[j] * H + c));
       const float wj = s_w[j];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

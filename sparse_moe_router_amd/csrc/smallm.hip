@@ -407,14 +407,14 @@ hipError_t launch_small_gateup(const uint16_t* x, const uint16_t* expert_w, cons
                                const SmallUnion& un, float* h, const Plan& p, const Launch& lc) {
   const uint16_t* sw = p.shared ? shared_w : nullptr;
   if (p.tiled) return small_gateup(x, WBf16T{expert_w}, WBf16T{sw}, un, h, p, lc);
-  return small_gateup(x, WBf16{expert_w}, WBf16{sw}, un, h, p, lc);
+  return small_gateup(x, WBf16S{expert_w}, WBf16S{sw}, un, h, p, lc);
 }
 
 hipError_t launch_small_down(const uint16_t* expert_w, const uint16_t* shared_w, const float* w,
                              const SmallUnion& un, const float* h, uint16_t* out, const Plan& p, const Launch& lc) {
   const uint16_t* sw = p.shared ? shared_w : nullptr;
   if (p.tiled) return small_down(WBf16T{expert_w}, WBf16T{sw}, w, un, h, out, p, lc);
-  return small_down(WBf16{expert_w}, WBf16{sw}, w, un, h, out, p, lc);
+  return small_down(WBf16S{expert_w}, WBf16S{sw}, w, un, h, out, p, lc);
 }
 
 hipError_t launch_small_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const SmallUnion& un,

@@ -5,7 +5,7 @@
 // is row i of gate (m = 0) or up (m = 1), dn(c) row c of down; a row's
 // load(k) returns its 8-element chunk k .. k+7 (k % 8 == 0).
 //
-//  - WBf16: one bf16 per element, rows stored one after another.
+//  - WBf16 / WBf16S: one bf16 per element, rows stored one after another.
 //  - WBf16T: the same bf16 weights in the tiled layout the grouped GEMM
 //    streams (each K-step of a weight tile one contiguous block): in the
 //    gate/up part, panel p holds gate and up rows [128p, 128p + n) (n =
@@ -26,26 +26,28 @@
 //    4j..4j+3 (two per byte, low nibble first); groups: one 32-bit word each,
 //    s in the low half, b in the high half.
 //
-// The expert formats (WBf16T, WQ4 codes) load with the non-temporal hint: a
-// matrix-vector pass reads each expert weight once, and streamed with the
-// default policy those bytes push the activations, scores and h out of the
-// caches (the 40-layer decode graph: 18.6-19.0 -> 17.9-18.0 us per layer).
-// WBf16 keeps the default policy: it also serves the router rows, which the
-// row groups of the small-batch router re-read from cache.
+// The expert formats (WBf16S, WBf16T, WQ4 codes) load with the non-temporal
+// hint: a matrix-vector pass reads each expert weight once, and streamed with
+// the default policy those bytes push the activations, scores and h out of
+// the caches (the 40-layer decode graph: 18.6-19.0 -> 17.9-18.0 us per
+// layer).  WBf16 keeps the default policy for the router rows.
 #pragma once
 
 #include "moe_internal.h"
 
 namespace moe {
 
-struct WBf16 {
+template <bool NT>
+struct WBf16Rows {
   const uint16_t* p;
   typedef u32x4_t chunk_t;  // 8 elements
   struct Row {
     const uint16_t* p;
-    __device__ __forceinline__ chunk_t load(int64_t k) const { return *(const u32x4_t*)(p + k); }
+    __device__ __forceinline__ chunk_t load(int64_t k) const {
+      return NT ? __builtin_nontemporal_load((const u32x4_t*)(p + k)) : *(const u32x4_t*)(p + k);
+    }
   };
-  __device__ __forceinline__ WBf16 block(int64_t e) const { return {p + e}; }
+  __device__ __forceinline__ WBf16Rows block(int64_t e) const { return {p + e}; }
   __device__ __forceinline__ Row gu(int m, int i, int H, int I) const { return {p + ((int64_t)m * I + i) * H}; }
   __device__ __forceinline__ Row dn(int c, int H, int I) const { return {p + (int64_t)2 * I * H + (int64_t)c * I}; }
   // sum_i w_i x_i over the 8 elements, x as 8 bf16
@@ -61,6 +63,14 @@ struct WBf16 {
            bf16_lo(w[2]) * x1[0] + bf16_hi(w[2]) * x1[1] + bf16_lo(w[3]) * x1[2] + bf16_hi(w[3]) * x1[3];
   }
 };
+
+// Row-major bf16 rows with the default cache policy (router rows: the
+// small-batch router re-reads them, and across decode steps the routers of
+// all layers, 1 MB each, stay in the last-level cache; measured slower with
+// the hint) and with the non-temporal hint (expert rows: read once per
+// layer).
+typedef WBf16Rows<false> WBf16;
+typedef WBf16Rows<true> WBf16S;
 
 struct WBf16T {
   const uint16_t* p;
