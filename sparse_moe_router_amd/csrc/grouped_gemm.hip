@@ -23,8 +23,8 @@
 // accumulator registers).  With tiles of 256 rows an expert's weights are
 // read once whenever it has at most 256 rows (all experts at near-uniform
 // routing).  The number of 32-row blocks is a template parameter chosen per
-// tile (rounded up to even), so the inner loop has no branches and row
-// blocks past the group's rows cost nothing.
+// tile, so the inner loop has no branches and row blocks past the group's
+// rows cost nothing.
 //
 // Launch order is XCD-aware: workgroup b runs on XCD b % 8; the tiles are
 // dealt to the XCDs round-robin (heaviest first) and the panels of a tile
@@ -212,6 +212,8 @@ __device__ __forceinline__ void combine_epilogue(const GemmArgs& p, const Tile& 
 // of the same columns (col block 1), so SwiGLU is lane-local.  MODE 1:
 // y = A Wd^T over a 256-column panel of H; column group cg owns columns
 // [n0+64cg, +64).  Row group rg owns the 32-row blocks rb = rg, rg+2, ...
+// below NRB (an odd NRB leaves row group 1 one block fewer; with NRB = 1 its
+// waves only move their share of the transfers).
 //
 // K runs in steps of BK through two LDS rings filled by direct global->LDS
 // transfers (no register staging): the weight tile (NWR rows x BK) in DW
