@@ -172,14 +172,20 @@ class LayerCall:
             raise RuntimeError(f"moe_layer_forward failed with status {st}")
 
 
-def layout_flag(args, moe, q4):
-    """MOE_FLAG_TILED_WEIGHTS when the bf16 expert weights were tiled (4-bit weights stay as they are)."""
-    return moe.FLAG_TILED_WEIGHTS if args.layout == "tiled" and not q4 else 0
-
-
-def layout_name(args, q4):
+def layout_flag(args, moe, q4, q4_tiled=False):
+    """MOE_FLAG_TILED_WEIGHTS when the expert weights were tiled: bf16 weights with --layout tiled
+    (moe_tile_weights), 4-bit weights only in the legs that ask for it (moe_tile_weights_q4: faster
+    grouped GEMMs, slower matrix-vector paths, so the 4-bit decode and small-batch legs keep the
+    row-major packing)."""
     if q4:
-        return "4-bit codes + scale/bias words, row-major"
+        return moe.FLAG_TILED_WEIGHTS if q4_tiled else 0
+    return moe.FLAG_TILED_WEIGHTS if args.layout == "tiled" else 0
+
+
+def layout_name(args, q4, q4_tiled=False):
+    if q4:
+        return ("4-bit codes + scale/bias words, tiled (moe_tile_weights_q4, once before timing)"
+                if q4_tiled else "4-bit codes + scale/bias words, row-major")
     return "tiled (moe_tile_weights, once before timing)" if args.layout == "tiled" else "row-major"
 
 
@@ -526,7 +532,7 @@ def bench_small(args, hip, moe, S, layers, xpool, Ms=(2, 4, 8, 16, 32, 64)):
 
 # ------------------------------------------------------------------ prefill
 
-def gateup_roofline(kt, w, M, nonempty, q4, peaks=None):
+def gateup_roofline(kt, w, M, nonempty, q4, peaks=None, q4_tiled=False):
     """Roofline position of the gate/up grouped GEMM (k_grouped_gemm<0>) for M rows: algorithmic
     bytes (the gate/up weights of the routed experts that received rows, x read once; no
     intermediates) and FLOPs (2 * 2*I*H per assignment) per launch over its average event-timed
@@ -537,8 +543,10 @@ def gateup_roofline(kt, w, M, nonempty, q4, peaks=None):
     gu_bytes = int(nonempty * 2 * I * H * wb) + M * H * 2
     gu_flops = M * k * 2 * I * H * 2
     avg = sum(kt["gemm_gateup"]) / len(kt["gemm_gateup"])
-    kname = "k_grouped_gemm<0, q4> (gate/up + SwiGLU)" if q4 else "k_grouped_gemm<0> (gate/up + SwiGLU)"
-    traffic = traffic_for(f"k_grouped_gemm<0,q4>@{w.name}" if q4 else f"k_grouped_gemm<0>@{w.name}")
+    tag = ("<0,q4t>" if q4_tiled else "<0,q4>") if q4 else "<0>"
+    kname = {"<0>": "k_grouped_gemm<0>", "<0,q4>": "k_grouped_gemm<0, q4>",
+             "<0,q4t>": "k_grouped_gemm<0, q4> on tiled 4-bit weights"}[tag] + " (gate/up + SwiGLU)"
+    traffic = traffic_for(f"k_grouped_gemm{tag}@{w.name}")
     return roofline_obj(kname, avg, gu_bytes, gu_flops, peaks or {}, traffic=traffic)
 
 
@@ -580,11 +588,13 @@ class CpuPrefill:
                     seconds=round(sum(self.t), 3))
 
 
-def bench_prefill(args, hip, moe, SD, S, w, peaks, q4=False, cpu=None):
+def bench_prefill(args, hip, moe, SD, S, w, peaks, q4=False, cpu=None, q4_tiled=False):
     import torch
     if q4:
         x, r, ec, esb, sc, ssb = SD.layer_tensors_q4(w)
         ex, sh = (ec, esb), (sc, ssb)
+        if q4_tiled:
+            ex, sh = moe.tile_weights_q4(*ex, w.H, w.I), moe.tile_weights_q4(*sh, w.H, w.I_shared)
     else:
         x, r, ex, sh = SD.layer_tensors(w)
         if args.layout == "tiled":
@@ -596,7 +606,7 @@ def bench_prefill(args, hip, moe, SD, S, w, peaks, q4=False, cpu=None):
     ws = torch.empty(moe.workspace_size(w.M, w.H, w.E, w.I, w.I_shared, w.k), dtype=torch.uint8, device="cuda")
     counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
     call = LayerCall(moe, x, r, ex, sh, w.k, out, ws, bias=bias, routing={"counts": counts},
-                     flags=layout_flag(args, moe, q4))
+                     flags=layout_flag(args, moe, q4, q4_tiled))
     for _ in range(args.warmup):
         call()
     per_round = max(20, args.steps // ROUNDS)
@@ -610,12 +620,12 @@ def bench_prefill(args, hip, moe, SD, S, w, peaks, q4=False, cpu=None):
     layer_bytes = int((nonempty + 1) * w.expert_elems() * wb) + E * H * 2 + 2 * M * H * 2
     flops = M * (2 * H * E + (k + 1) * 3 * 2 * H * I)
     lay_f = layer_fracs(layer_bytes, flops, ms, peaks)
-    roof = gateup_roofline(kt, w, M, nonempty, q4, peaks)
+    roof = gateup_roofline(kt, w, M, nonempty, q4, peaks, q4_tiled)
     roof["layer"] = {"hbm_frac": lay_f["hbm_frac"], "mfma_frac": lay_f["mfma_frac"], "bound": lay_f["bound"]}
     res = dict(
         value=M / (ms * 1e-3), unit="tok/s", ms_per_step=ms, steps=per_round * ROUNDS, ms_rounds=spread(per),
         config=dict(workload=f"{w.name}: {w.describe()}, {'4-bit group-affine' if q4 else 'bf16'} experts",
-                    weights_layout=layout_name(args, q4),
+                    weights_layout=layout_name(args, q4, q4_tiled),
                     nonempty_experts=nonempty,
                     max_group=int(c.max()), empty_groups=int((c == 0).sum())),
         layer_bytes=layer_bytes, layer_flops=flops, layer=lay_f,
@@ -721,7 +731,7 @@ def main():
     skew = bench_prefill(args, hip, moe, SD, S, S.SKEW, peaks)
     long = None if args.no_long else bench_long(args, hip, moe, SD, S, S.LONG, peaks)
     torch.cuda.empty_cache()
-    dec_q4 = pre_q4 = small_q4 = None
+    dec_q4 = pre_q4 = pre_q4t = small_q4 = None
     if not args.no_q4:
         dq, keep = bench_decode(args, hip, moe, SD, S, peaks, q4=True)
         small_q4 = None if args.no_small else bench_small(args, hip, moe, S, *keep, Ms=(2, 8, 16))
@@ -733,6 +743,8 @@ def main():
                   "config": {"workload": f"decode batch-1, {args.layers} layers, 4-bit group-affine experts "
                                          f"(g=64, bf16 scale+bias), bf16 router/x/out"}}
         pre_q4 = bench_prefill(args, hip, moe, SD, S, S.PREFILL, peaks, q4=True)
+        torch.cuda.empty_cache()
+        pre_q4t = bench_prefill(args, hip, moe, SD, S, S.PREFILL, peaks, q4=True, q4_tiled=True)
     w = S.DECODE
     line = {
         "metric": METRIC, "value": round(dec["value"], 2), "unit": "tok/s", "n_gpus": 1,
@@ -755,6 +767,7 @@ def main():
         "prefill_long": long,
         "decode_q4": dec_q4,
         "prefill_q4": pre_q4,
+        "prefill_q4_tiled": pre_q4t,
         "small_batch": None if args.no_small else {
             "config": {"workload": f"M token rows x {args.layers} decode layers (same weights), "
                                    f"matrix-vector path over the union of selected experts vs grouped path"},

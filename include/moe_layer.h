@@ -99,9 +99,9 @@ typedef enum {
 #define MOE_FLAG_FORCE_GEMV 0x1u /* matrix-vector paths; requires M <= 64 */
 #define MOE_FLAG_FORCE_GEMM 0x2u /* grouped (matrix-matrix) path, also at M == 1 */
 /* expert_w and shared_w are in the tiled layout written by moe_tile_weights
- * (bf16 weights only: moe_layer_forward_q4 rejects it with
- * MOE_ERR_INVALID_ARG).  Every path reads it; results are bit-identical to
- * the row-major layout's. */
+ * (bf16), or the 4-bit experts and shared expert in the one written by
+ * moe_tile_weights_q4 (moe_layer_forward_q4).  Every path reads it; results
+ * are bit-identical to the row-major layout's. */
 #define MOE_FLAG_TILED_WEIGHTS 0x4u
 /* Decode path (M == 1) in two launches instead of three, when I and
  * I_shared <= 512, H <= 4096 and (top_k * I + I_shared) * 4 <= 64 KiB (else
@@ -280,6 +280,24 @@ moe_status_t moe_layer_forward_q4(const moe_desc_t* d, const void* x, const void
  * are device pointers, 16-byte aligned, not overlapping; H and I follow the
  * layer's shape rules.  Asynchronous on `stream` like the layer calls. */
 moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void* src, void* dst, hipStream_t stream);
+
+/* The same tiled order for 4-bit experts (moe_q4_t): rewrites nblocks blocks'
+ * codes (3*H*I/2 bytes each) and group words (3*H*I/64 words each) from
+ * codes / groups into codes_dst / groups_dst.  Element e of a tiled block
+ * (the order above, without the chunk swizzle) is element f of the row-major
+ * block; its code goes to code word e/8 (nibble e%8) and each group word to
+ * position e/64, so a 4-bit K-step of a weight tile is one contiguous block
+ * of codes (32 bytes per tile row) and one of group words (one per tile row).
+ * With MOE_FLAG_TILED_WEIGHTS moe_layer_forward_q4 reads experts and shared
+ * expert in this layout on every path, bit-identical to the row-major one.
+ * It speeds up the grouped path (whole cache lines per K-step instead of a
+ * quarter line of each row) and slows down the matrix-vector paths (a row's
+ * codes come in 32-byte pieces, one per K-step), so it suits prefill-heavy
+ * use; decode is faster on the row-major packing.  All four pointers are
+ * device pointers, 16-byte aligned; the outputs overlap neither input nor
+ * each other.  Asynchronous on `stream`. */
+moe_status_t moe_tile_weights_q4(int64_t nblocks, int32_t H, int32_t I, const void* codes, const void* groups,
+                                 void* codes_dst, void* groups_dst, hipStream_t stream);
 
 /* moe_layer_forward for callers that cannot allocate or pass device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid

@@ -526,6 +526,7 @@ hipError_t launch_decode_route(const uint16_t* x, const uint16_t* wr, const floa
 hipError_t launch_decode_route_q4(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
                                   const Q4Weights& sh, float* h_dec, uint32_t* arrivals, int32_t* status,
                                   const Plan& p, const Launch& lc) {
+  if (p.tiled) return decode_route(x, wr, bias, logits, WQ4T{sh.codes, sh.groups}, h_dec, arrivals, status, p, lc);
   return decode_route(x, wr, bias, logits, WQ4{sh.codes, sh.groups}, h_dec, arrivals, status, p, lc);
 }
 
@@ -541,6 +542,9 @@ hipError_t launch_decode_experts(const uint16_t* x, const uint16_t* expert_w, co
 hipError_t launch_decode_experts_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const float* logits,
                                     int32_t* ids, float* w, float* h_dec, uint32_t* arrivals, int32_t* status,
                                     uint16_t* out, const Plan& p, int probe, const Launch& lc) {
+  if (p.tiled)
+    return decode_experts(x, WQ4T{ex.codes, ex.groups}, WQ4T{sh.codes, sh.groups}, logits, ids, w, h_dec, arrivals,
+                          status, out, p, probe, lc);
   return decode_experts(x, WQ4{ex.codes, ex.groups}, WQ4{sh.codes, sh.groups}, logits, ids, w, h_dec, arrivals,
                         status, out, p, probe, lc);
 }
@@ -548,11 +552,13 @@ hipError_t launch_decode_experts_q4(const uint16_t* x, const Q4Weights& ex, cons
 hipError_t launch_decode_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh,
                                    const float* logits, int32_t* ids, float* w, float* h_dec, const Plan& p,
                                    const Launch& lc) {
+  if (p.tiled) return decode_gateup(x, WQ4T{ex.codes, ex.groups}, WQ4T{sh.codes, sh.groups}, logits, ids, w, h_dec, p, lc);
   return decode_gateup(x, WQ4{ex.codes, ex.groups}, WQ4{sh.codes, sh.groups}, logits, ids, w, h_dec, p, lc);
 }
 
 hipError_t launch_decode_down_q4(const Q4Weights& ex, const Q4Weights& sh, const int32_t* ids, const float* w,
                                  const float* h_dec, uint16_t* out, const Plan& p, const Launch& lc) {
+  if (p.tiled) return decode_down(WQ4T{ex.codes, ex.groups}, WQ4T{sh.codes, sh.groups}, ids, w, h_dec, out, p, lc);
   return decode_down(WQ4{ex.codes, ex.groups}, WQ4{sh.codes, sh.groups}, ids, w, h_dec, out, p, lc);
 }
 

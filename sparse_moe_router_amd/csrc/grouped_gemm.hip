@@ -67,7 +67,7 @@ struct GemmArgs {
   int H, E, I, Is, k;
   int npan;
   int max_tiles;
-  int tiled;  // bf16 weights in the tiled layout: a panel's K-step is one block (the stage image)
+  int tiled;  // weights in the tiled layout: a panel's K-step is one block (bf16: the stage image)
 };
 
 constexpr int BK = 64;        // K per pipeline step
@@ -286,15 +286,34 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   uint32_t woff[4];            // byte offsets within the expert block
   uint32_t goff = 0;
   int wstep = 128;             // bytes from one weight step to the next
+  int gstep = 4;               // 4-bit: group-word bytes from one step to the next
   if (Q4) {
     const int64_t eb = is_shared ? 0 : (int64_t)tl.g * 3 * p.I * p.H;  // expert block, elements
     wsrc = (const char*)(is_shared ? p.sh_codes : p.ex_codes) + eb / 2;
     gsrc = (const char*)(is_shared ? p.sh_groups : p.ex_groups) + eb / 16;
-    // codes: rows 64cg + 32rg + lane/2, 16 bytes (half lane&1) each
-    woff[0] = (uint32_t)(wrow_elem(rg, lane >> 1) / 2 + 16 * (lane & 1));
+    // codes: stage rows 64cg + 32rg + lane/2, 16 bytes (half lane&1) each;
+    // group words: stage rows 64cg + lane (moved by row group 0)
+    if (p.tiled) {
+      // tiled: step s of this panel is one block of trows x 32 bytes of codes
+      // and one of trows group words, in stage row order (rows past a
+      // partial panel re-read the first row: never stored)
+      const int n = MODE == 0 ? (Ig - panel * (NWR / 2) < NWR / 2 ? Ig - panel * (NWR / 2) : NWR / 2)
+                              : (p.H - panel * NWR < NWR ? p.H - panel * NWR : NWR);
+      const int trows = MODE == 0 ? 2 * n : n;
+      const int64_t pbase = MODE == 0 ? (int64_t)NWR * panel * p.H : (int64_t)2 * Ig * p.H + (int64_t)NWR * panel * Ig;
+      wsrc += pbase / 2;
+      gsrc += pbase / 16;
+      wstep = trows * 32;
+      gstep = trows * 4;
+      const int R = 64 * cg + 32 * rg + (lane >> 1), gR = 64 * cg + lane;
+      woff[0] = (uint32_t)((R < trows ? R : 0) * 32 + 16 * (lane & 1));
+      goff = (uint32_t)((gR < trows ? gR : 0) * 4);
+    } else {
+      wstep = 32;
+      woff[0] = (uint32_t)(wrow_elem(rg, lane >> 1) / 2 + 16 * (lane & 1));
+      goff = (uint32_t)(wrow_elem(lane >> 5, lane & 31) / 64 * 4);
+    }
     woff[1] = woff[2] = woff[3] = 0;
-    // group words: rows 64cg + lane (moved by row group 0)
-    goff = (uint32_t)(wrow_elem(lane >> 5, lane & 31) / 64 * 4);
   } else {
     const uint16_t* W = is_shared ? p.shared_w : p.expert_w + (int64_t)tl.g * 3 * p.I * p.H;
     wsrc = (const char*)W;
@@ -343,8 +362,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   };
   auto load_w = [&](u32x4_t* st, int s) {
     if (Q4) {
-      dma16(wsrc + woff[0] + (int64_t)s * 32, st + (cg * 2 + rg) * 64);
-      if (rg == 0) dma4(gsrc + goff + (int64_t)s * 4, (uint32_t*)(st + 2 * NWR) + cg * 64);
+      if (NT)
+        dma16_nt(wsrc + woff[0] + (int64_t)s * wstep, st + (cg * 2 + rg) * 64);
+      else
+        dma16(wsrc + woff[0] + (int64_t)s * wstep, st + (cg * 2 + rg) * 64);
+      if (rg == 0) dma4(gsrc + goff + (int64_t)s * gstep, (uint32_t*)(st + 2 * NWR) + cg * 64);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -595,11 +617,13 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmArgs p) {
     const int Ig = tl.g >= p.E ? p.Is : p.I;
     if (panel * (NWR / 2) >= Ig) return;
   }
-  // bf16 weights of an expert whose rows fit one tile are read once in the
+  // the weights of an expert whose rows fit one tile are read once in the
   // launch: fetched with the non-temporal hint, they leave the caches to the
   // activation rows (an expert split over several tiles is fetched by each of
-  // them and keeps the default policy, as does the shared expert)
-  if (!Q4 && tl.g < p.E && tl.r0 == 0 && tl.rows < BM)
+  // them and keeps the default policy, as does the shared expert).  Not for
+  // row-major 4-bit codes: a step takes a quarter of each row's cache line,
+  // and the next three steps need the rest.
+  if ((!Q4 || p.tiled) && tl.g < p.E && tl.r0 == 0 && tl.rows < BM)
     routed_tile<MODE, Q4, true>(p, tl, panel, rg);
   else
     routed_tile<MODE, Q4, false>(p, tl, panel, rg);
@@ -748,6 +772,7 @@ hipError_t launch_gemm_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q
   const int maxI = pl.I > pl.Is ? pl.I : pl.Is;
   a.npan = (maxI + NWR / 2 - 1) / (NWR / 2);
   a.max_tiles = (int)pl.max_tiles;
+  a.tiled = pl.tiled ? 1 : 0;
   return launch(lc, k_grouped_gemm<0, true>, dim3(xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }
 
@@ -774,6 +799,7 @@ hipError_t launch_gemm_down_q4(const uint16_t* h_r, uint16_t* h_s, const Q4Weigh
   a.k = pl.k;
   a.npan = (pl.H + NWR - 1) / NWR;
   a.max_tiles = (int)pl.max_tiles;
+  a.tiled = pl.tiled ? 1 : 0;
   shared_gateup_units(&a, x_shared_gu, h_s, pl);  // last: it sets a_x and out_s
   return launch(lc, k_grouped_gemm<1, true>, dim3(a.sgu_units + xcd_grid(pl.max_tiles, a.npan)), dim3(512), a);
 }

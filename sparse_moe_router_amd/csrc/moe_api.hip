@@ -310,7 +310,6 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   if (st != MOE_OK) return st;
   if (!x || !router_w || !out) return MOE_ERR_INVALID_ARG;
   if (wt.q4) {
-    if (d->flags & MOE_FLAG_TILED_WEIGHTS) return MOE_ERR_INVALID_ARG;  // bf16 weights only
     if (!wt.eq.codes || !wt.eq.groups) return MOE_ERR_INVALID_ARG;
     const bool has_sh = wt.sq.codes || wt.sq.groups;
     if ((d->I_shared > 0) != has_sh || (has_sh && (!wt.sq.codes || !wt.sq.groups))) return MOE_ERR_INVALID_ARG;
@@ -578,6 +577,26 @@ moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w,
   }
   Tracer none{nullptr, s};
   return run_routing_grouped(p, d, x, router_w, workspace, routing, s, none);
+}
+
+moe_status_t moe_tile_weights_q4(int64_t nblocks, int32_t H, int32_t I, const void* codes, const void* groups,
+                                 void* codes_dst, void* groups_dst, hipStream_t stream) {
+  if (nblocks < 0 || !codes || !groups || !codes_dst || !groups_dst) return MOE_ERR_INVALID_ARG;
+  if (H < 64 || H > 16384 || H % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (I < 64 || I > 16384 || I % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned(codes, 16) || !aligned(groups, 16) || !aligned(codes_dst, 16) || !aligned(groups_dst, 16))
+    return MOE_ERR_MISALIGNED;
+  const size_t cbytes = (size_t)nblocks * 3 * I * H / 2, gbytes = (size_t)nblocks * 3 * I * H / 16;
+  Regions r;  // outputs disjoint from the inputs and from each other
+  r.input(codes, cbytes);
+  r.input(groups, gbytes);
+  r.output(codes_dst, cbytes);
+  r.output(groups_dst, gbytes);
+  if (!r.disjoint()) return MOE_ERR_INVALID_ARG;
+  if (nblocks == 0) return MOE_OK;
+  const hipError_t e = launch_tile_weights_q4((const uint32_t*)codes, (const uint32_t*)groups, (uint32_t*)codes_dst,
+                                              (uint32_t*)groups_dst, nblocks, H, I, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
 moe_status_t moe_tile_weights(int64_t nblocks, int32_t H, int32_t I, const void* src, void* dst, hipStream_t stream) {

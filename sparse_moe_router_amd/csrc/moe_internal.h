@@ -227,5 +227,7 @@ hipError_t launch_small_down_q4(const Q4Weights& ex, const Q4Weights& sh, const 
 // nblocks bf16 expert blocks (hidden H, intermediate I) from the row-major
 // packing to the tiled layout read with MOE_FLAG_TILED_WEIGHTS.
 hipError_t launch_tile_weights(const uint16_t* src, uint16_t* dst, int64_t nblocks, int H, int I, hipStream_t s);
+hipError_t launch_tile_weights_q4(const uint32_t* codes, const uint32_t* groups, uint32_t* codes_dst,
+                                  uint32_t* groups_dst, int64_t nblocks, int H, int I, hipStream_t s);
 
 }  // namespace moe

@@ -419,11 +419,13 @@ hipError_t launch_small_down(const uint16_t* expert_w, const uint16_t* shared_w,
 
 hipError_t launch_small_gateup_q4(const uint16_t* x, const Q4Weights& ex, const Q4Weights& sh, const SmallUnion& un,
                                   float* h, const Plan& p, const Launch& lc) {
+  if (p.tiled) return small_gateup(x, WQ4T{ex.codes, ex.groups}, WQ4T{sh.codes, sh.groups}, un, h, p, lc);
   return small_gateup(x, WQ4{ex.codes, ex.groups}, WQ4{sh.codes, sh.groups}, un, h, p, lc);
 }
 
 hipError_t launch_small_down_q4(const Q4Weights& ex, const Q4Weights& sh, const float* w, const SmallUnion& un,
                                 const float* h, uint16_t* out, const Plan& p, const Launch& lc) {
+  if (p.tiled) return small_down(WQ4T{ex.codes, ex.groups}, WQ4T{sh.codes, sh.groups}, w, un, h, out, p, lc);
   return small_down(WQ4{ex.codes, ex.groups}, WQ4{sh.codes, sh.groups}, w, un, h, out, p, lc);
 }
 

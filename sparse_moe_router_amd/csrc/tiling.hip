@@ -21,6 +21,13 @@
 //   a panel is K/64 steps one after another (K = H for gate/up, I for
 //   down), a step being its tile rows in order, 64 elements each, with the
 //   8-element chunk q of tile row R at chunk position q ^ ((R / 2) % 8).
+//
+// The 4-bit format has the same tiled order without the swizzle: its code
+// words (8 codes each) follow the element order above, and its group words
+// (one per 64 elements) too, so a K-step of a 4-bit weight tile is one
+// contiguous block of codes and one of group words.  In the row-major
+// 4-bit packing one step is 32 bytes of each of 256 rows (a quarter of a
+// 128-byte line) and 4 bytes of group words of each, 256 lines apiece.
 #include "moe_internal.h"
 
 namespace moe {
@@ -60,7 +67,63 @@ __global__ __launch_bounds__(256) void k_tile_bf16(const u32x4_t* __restrict__ s
   }
 }
 
+// Element e of a tiled block (the order above, without the swizzle) -> its
+// element in the row-major block.
+__device__ __forceinline__ int64_t tiled_to_rowmajor(int64_t e, int H, int I) {
+  const int64_t gu = (int64_t)2 * I * H;
+  if (e < gu) {
+    const int64_t pn = e / ((int64_t)256 * H);
+    const int64_t rem = e - pn * 256 * H;
+    const int n = I - 128 * pn < 128 ? (int)(I - 128 * pn) : 128;
+    const int64_t per = (int64_t)128 * n;
+    const int64_t s = rem / per;
+    const int w = (int)(rem - s * per);
+    const int R = w >> 6;
+    const int m = (R >> 5) & 1;
+    const int64_t row = 128 * pn + 32 * (R >> 6) + (R & 31);
+    return ((int64_t)m * I + row) * H + 64 * s + (w & 63);
+  }
+  const int64_t e2 = e - gu;
+  const int64_t pn = e2 / ((int64_t)256 * I);
+  const int64_t rem = e2 - pn * 256 * I;
+  const int n = H - 256 * pn < 256 ? (int)(H - 256 * pn) : 256;
+  const int64_t per = (int64_t)64 * n;
+  const int64_t s = rem / per;
+  const int w = (int)(rem - s * per);
+  return gu + (256 * pn + (w >> 6)) * (int64_t)I + 64 * s + (w & 63);
+}
+
+// 4-bit: one thread per destination code word (8 elements), then per group
+// word (64 elements).
+__global__ __launch_bounds__(256) void k_tile_q4(const uint32_t* __restrict__ csrc, const uint32_t* __restrict__ gsrc,
+                                                 uint32_t* __restrict__ cdst, uint32_t* __restrict__ gdst,
+                                                 int64_t nblocks, int64_t block_words, int H, int I) {
+  const int64_t block_groups = block_words / 8;
+  const int64_t total = nblocks * (block_words + block_groups);
+  for (int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x; d < total; d += (int64_t)gridDim.x * 256) {
+    if (d < nblocks * block_words) {
+      const int64_t b = d / block_words, w = d - b * block_words;
+      cdst[d] = csrc[b * block_words + (tiled_to_rowmajor(8 * w, H, I) >> 3)];
+    } else {
+      const int64_t d2 = d - nblocks * block_words;
+      const int64_t b = d2 / block_groups, w = d2 - b * block_groups;
+      gdst[d2] = gsrc[b * block_groups + (tiled_to_rowmajor(64 * w, H, I) >> 6)];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tile_weights_q4(const uint32_t* codes, const uint32_t* groups, uint32_t* codes_dst,
+                                  uint32_t* groups_dst, int64_t nblocks, int H, int I, hipStream_t s) {
+  const int64_t block_words = (int64_t)3 * I * H / 8;
+  const int64_t total = nblocks * (block_words + block_words / 8);
+  const int64_t want = (total + 255) / 256;
+  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(k_tile_q4, dim3(grid), dim3(256), 0, s, codes, groups, codes_dst, groups_dst, nblocks,
+                     block_words, H, I);
+  return hipGetLastError();
+}
 
 hipError_t launch_tile_weights(const uint16_t* src, uint16_t* dst, int64_t nblocks, int H, int I, hipStream_t s) {
   const int64_t block_chunks = (int64_t)3 * I * H / 8;

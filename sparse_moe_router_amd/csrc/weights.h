@@ -25,6 +25,8 @@
 //    bias b, w = s*q + b.  Codes: eight per 32-bit word, element 8i+j in bits
 //    4j..4j+3 (two per byte, low nibble first); groups: one 32-bit word each,
 //    s in the low half, b in the high half.
+//  - WQ4T: the WQ4 codes and group words in the grouped GEMM's tiled order
+//    (below).
 //
 // The expert formats (WBf16S, WBf16T, WQ4 codes) load with the non-temporal
 // hint: a matrix-vector pass reads each expert weight once, and streamed with
@@ -137,6 +139,43 @@ struct WQ4 {
                      code(w.c, 4) * x1[0] + code(w.c, 5) * x1[1] + code(w.c, 6) * x1[2] + code(w.c, 7) * x1[3];
     const float sx = (x0[0] + x0[1]) + (x0[2] + x0[3]) + ((x1[0] + x1[1]) + (x1[2] + x1[3]));
     return bf16_lo(w.g) * qx + bf16_hi(w.g) * sx;
+  }
+};
+
+// The 4-bit format in the tiled order of the grouped GEMM (moe_tile_weights_q4):
+// the same panels and 64-element K-steps as WBf16T (no swizzle), a tile row's
+// step being its 8 code words, and the group words in the same order, one
+// per tile row and step.  A row's code word for elements k .. k+7 sits at
+// panel + step * (tile rows * 8) + R * 8 + (k / 8) % 8, its group word at
+// panel / 64 + step * (tile rows) + R.
+struct WQ4T {
+  const uint32_t* c;
+  const uint32_t* g;
+  typedef WQ4::chunk_t chunk_t;
+  struct Row {
+    const uint32_t* c;  // code words of tile row R at step 0
+    const uint32_t* g;  // group word of tile row R at step 0
+    int cst, gst;       // words per step: tile rows * 8, tile rows
+    __device__ __forceinline__ chunk_t load(int64_t k) const {
+      const int64_t s = k >> 6;
+      return {__builtin_nontemporal_load(c + s * cst + ((k >> 3) & 7)), g[s * gst]};
+    }
+  };
+  __device__ __forceinline__ WQ4T block(int64_t e) const { return {c + (e >> 3), g + (e >> 6)}; }
+  __device__ __forceinline__ Row at(int64_t base, int R, int trows) const {
+    return {c + (base >> 3) + 8 * R, g + (base >> 6) + R, 8 * trows, trows};
+  }
+  __device__ __forceinline__ Row gu(int m, int i, int H, int I) const {
+    const int pn = i >> 7, j = i & 127, n = I - 128 * pn < 128 ? I - 128 * pn : 128;
+    return at((int64_t)256 * pn * H, 64 * (j >> 5) + 32 * m + (j & 31), 2 * n);
+  }
+  __device__ __forceinline__ Row dn(int c, int H, int I) const {
+    const int pn = c >> 8, n = H - 256 * pn < 256 ? H - 256 * pn : 256;
+    return at((int64_t)2 * I * H + (int64_t)256 * pn * I, c & 255, n);
+  }
+  __device__ __forceinline__ static float dot(const chunk_t& w, const u32x4_t& x) { return WQ4::dot(w, x); }
+  __device__ __forceinline__ static float dot(const chunk_t& w, const f32x4_t& x0, const f32x4_t& x1) {
+    return WQ4::dot(w, x0, x1);
   }
 };
 

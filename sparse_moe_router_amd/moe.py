@@ -26,7 +26,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_MISALIGNED", 5: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_block_map_capacity", "moe_layer_forward", "moe_route", "moe_layer_forward_traced",
-           "moe_layer_forward_q4", "moe_tile_weights", "moe_layer_forward_noalloc", "moe_status_string",
+           "moe_layer_forward_q4", "moe_tile_weights", "moe_tile_weights_q4", "moe_layer_forward_noalloc",
+           "moe_status_string",
            "moe_last_hip_error")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route.restype = ctypes.c_int
         L.moe_tile_weights.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
         L.moe_tile_weights.restype = ctypes.c_int
+        L.moe_tile_weights_q4.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp]
+        L.moe_tile_weights_q4.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_hip_error.argtypes = []
@@ -288,6 +291,21 @@ def tile_weights(w: torch.Tensor, H: int, I: int, out: Optional[torch.Tensor] = 
                                 _stream(stream))
     _check(st, "moe_tile_weights")
     return out
+
+
+def tile_weights_q4(codes: torch.Tensor, scale_bias: torch.Tensor, H: int, I: int, stream=None):
+    """moe_tile_weights_q4: 4-bit expert blocks (codes uint8, 3*I*H/2 bytes per block; scale_bias int32,
+    3*I*H/64 words per block) rewritten into the tiled order read with FLAG_TILED_WEIGHTS by
+    forward_q4; returns (codes, scale_bias) tensors of the inputs' shapes."""
+    n = codes.numel() * 2 // (3 * I * H)
+    if n * 3 * I * H != codes.numel() * 2 or n * 3 * I * H != scale_bias.numel() * 64:
+        raise ValueError("codes and scale_bias must hold the same whole expert blocks")
+    c_out, g_out = torch.empty_like(codes), torch.empty_like(scale_bias)
+    st = lib().moe_tile_weights_q4(n, int(H), int(I), _ptr(codes, torch.uint8, "codes"),
+                                   _ptr(scale_bias, torch.int32, "scale_bias"), _ptr(c_out, torch.uint8, "codes_out"),
+                                   _ptr(g_out, torch.int32, "scale_bias_out"), _stream(stream))
+    _check(st, "moe_tile_weights_q4")
+    return c_out, g_out
 
 
 def route(x: torch.Tensor, router_w: torch.Tensor, top_k: int, routing: dict,

@@ -160,8 +160,9 @@ def test_forward_q4_rejects_bad_arguments():
 
 def test_tiled_flag_and_tile_weights_arguments():
     L = moe.lib()
-    # the tiled layout holds bf16 weights: the 4-bit entry point rejects the flag
-    assert fwd_q4(_desc(flags=moe.FLAG_TILED_WEIGHTS)) == INVALID
+    # the 4-bit entry point takes the flag too (weights from moe_tile_weights_q4); its other checks still apply
+    assert fwd_q4(_desc(flags=moe.FLAG_TILED_WEIGHTS), k=17) == SHAPE
+    assert fwd_q4(_desc(flags=moe.FLAG_TILED_WEIGHTS), wsb=ws_size(_desc(), 2) - 1) == WS
     assert ws_size(_desc(flags=moe.FLAG_TILED_WEIGHTS), 2) == ws_size(_desc(), 2)
     assert ws_size(_desc(flags=moe.FLAG_TILED_WEIGHTS | moe.FLAG_FORCE_GEMM), 2) > 0
     dst = FAKE + (1 << 28)
@@ -176,6 +177,24 @@ def test_tiled_flag_and_tile_weights_arguments():
     assert tw(2, 256, 128, FAKE, dst + 4, None) == MISALIGNED
     assert tw(2, 256, 128, FAKE, FAKE + 1024, None) == INVALID  # dst overlaps src
     assert tw(0, 256, 128, FAKE, dst, None) == OK  # no blocks: nothing enqueued
+    # 4-bit: codes (3*I*H/2 bytes per block) and group words (3*I*H/16 bytes per block), four pointers
+    tq = L.moe_tile_weights_q4
+    cb, gb = 3 * 128 * 256 // 2 * 2, 3 * 128 * 256 // 16 * 2  # two blocks at H=256, I=128
+    c, g, cd, gd = FAKE, FAKE + (1 << 24), FAKE + (2 << 24), FAKE + (3 << 24)
+    assert tq(-1, 256, 128, c, g, cd, gd, None) == INVALID
+    for i in range(4):
+        args = [c, g, cd, gd]
+        args[i] = None
+        assert tq(2, 256, 128, *args, None) == INVALID
+    assert tq(2, 100, 128, c, g, cd, gd, None) == SHAPE
+    assert tq(2, 256, 96, c, g, cd, gd, None) == SHAPE
+    assert tq(2, 256, 128, c + 8, g, cd, gd, None) == MISALIGNED
+    assert tq(2, 256, 128, c, g, cd, gd + 4, None) == MISALIGNED
+    assert tq(2, 256, 128, c, g, c + cb - 256, gd, None) == INVALID  # codes out overlaps codes in
+    assert tq(2, 256, 128, c, g, cd, g + gb - 256, None) == INVALID  # groups out overlaps groups in
+    assert tq(2, 256, 128, c, g, cd, cd + cb - 256, None) == INVALID  # the two outputs overlap
+    assert tq(2, 256, 128, c, g, g, gd, None) == INVALID  # codes out is the groups input
+    assert tq(0, 256, 128, c, g, cd, gd, None) == OK
 
 
 def _routing(**kw):
