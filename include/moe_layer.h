@@ -145,9 +145,13 @@ typedef struct {
                         GEMM works on): per tile (group g, first row r0 in the
                         group, rows, group position of row r0); routed groups
                         g < E in expert order, then the shared expert (g == E,
-                        its rows are the tokens in order); a group of c rows
-                        is cut into ceil(c / 256) tiles, all of 256 rows but
-                        the last, which holds the rest */
+                        its rows are the tokens in order); a routed group of
+                        c > 0 rows is cut into one tile when c <= 288, else
+                        into ceil((c - 32) / 256) tiles, all of 256 rows but
+                        the last, which holds the rest (1 .. 288 rows: up to
+                        32 rows past a multiple of 256 ride with the tile
+                        before); the shared group is cut into ceil(M / 256)
+                        tiles of 256 rows but the last */
   int32_t* num_tiles; /* [1] tiles in the block map (grouped path only) */
   int32_t* wait_status; /* [1] 0 when every wait inside the call's kernels ended
                            normally; 1 when one gave up, in which case out holds

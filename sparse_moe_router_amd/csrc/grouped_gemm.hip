@@ -12,17 +12,19 @@
 //    up tiles share the A rows and SwiGLU runs on the accumulators), the
 //    output projection goes with its routing score and the shared expert.
 //
-// Tile: up to 256 rows of one expert group (eight 32-row blocks) x 256
-// weight rows, one 8-wave workgroup per CU (two waves per SIMD: the LDS
+// Tile: up to 256 rows of one expert group (eight 32-row blocks), or 288
+// for a group's last tile (a ninth block holding the group's last 1..32
+// rows past a multiple of 256), x 256 weight rows, one 8-wave workgroup per CU (two waves per SIMD: the LDS
 // serves one wave's operand reads about half as fast as two waves', and one
 // wave's stalls hide behind the other's MFMAs).  Weights and the gathered
 // activation rows (rows of a routed group through the scatter permutation,
 // never copied) travel straight from global memory into LDS rings by
 // global->LDS transfers, 8 rows x 128 bytes per instruction, each weight byte
 // once per tile; a wave computes up to 128 rows x 64 columns (128 fp32
-// accumulator registers).  With tiles of 256 rows an expert's weights are
-// read once whenever it has at most 256 rows (all experts at near-uniform
-// routing).  The number of 32-row blocks is a template parameter chosen per
+// accumulator registers).  With tiles of 256 rows (288 for a group's last)
+// an expert's weights are read once whenever it has at most 288 rows (all
+// experts at near-uniform routing, most of them on 8192-token chunks).  The
+// number of 32-row blocks is a template parameter chosen per
 // tile, so the inner loop has no branches and row blocks past the group's
 // rows cost nothing.
 //
@@ -237,9 +239,28 @@ __device__ __forceinline__ void combine_epilogue(const GemmArgs& p, const Tile& 
 // the rows' 32 bytes of codes and their group words, expanded to bf16
 // operands in registers just before the MFMA.
 template <int MODE, int NRB, bool Q4, bool NT = false>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int panel, const Ring& ring) {
-  constexpr int NRH = (NRB + 1) / 2;  // row blocks of row group 0 (row group 1: NRB / 2)
-  constexpr int U = DA * DW;       // unroll: every ring stage index static
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int panel, const Ring& ring0) {
+  // NRB = 9: a 288-row tile (a group's last 1..32 rows past 256 kept with
+  // its 256).  Blocks 0..7 run as for NRB = 8; block 8 is split by column
+  // block between the row groups (row group rg takes column block rg), its
+  // activation rows in a stage of their own in the third weight stage, which
+  // the tile gives up (weights one step ahead instead of two).
+  constexpr bool X9 = NRB == 9;
+  constexpr int NRBm = X9 ? 8 : NRB;   // blocks of the main stages
+  constexpr int NRH = (NRBm + 1) / 2;  // row blocks of row group 0 (row group 1: NRBm / 2)
+  constexpr int DWT = X9 ? 2 : DW;
+  constexpr int U = DA * DWT;          // unroll: every ring stage index static
+  struct RingT {
+    u32x4_t* a[DA];
+    u32x4_t* w[DW];
+    u32x4_t* x[DA];
+  } ring;
+  ring.a[0] = ring0.a[0];
+  ring.a[1] = ring0.a[1];
+#pragma unroll
+  for (int d = 0; d < DW; ++d) ring.w[d] = ring0.w[d];
+  ring.x[0] = ring0.w[DW - 1];
+  ring.x[1] = ring0.w[DW - 1] + 32 * CPR;  // 32 rows x 128 bytes further
   const bool is_shared = tl.g >= p.E;
   const int Ig = is_shared ? p.Is : p.I;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -356,9 +377,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
     asrc[i] = (const char*)(rowp + 8 * srcq(wave * NRH + i));
   }
 
-  auto load_a = [&](u32x4_t* st, int s) {
+  const char* xsrc = nullptr;  // NRB = 9: rows 256 + 8 wave + lane/8 (waves 0..3)
+  if (X9) {
+    const int row = 256 + 8 * (wave & 3) + lr;
+    const int r = row < tl.rows ? row : 0;
+    const uint16_t* rowp;
+    if (MODE == 0) {
+      const int64_t tok = is_shared ? (int64_t)tl.pos0 + r : (int64_t)(p.perm[tl.pos0 + r] / p.k);
+      rowp = p.a_x + tok * p.H;
+    } else {
+      rowp = (is_shared ? p.a_s : p.a_r) + ((int64_t)tl.pos0 + r) * Ig;
+    }
+    xsrc = (const char*)(rowp + 8 * srcq(wave & 3));
+  }
+  auto load_a = [&](u32x4_t* st, u32x4_t* xst, int s) {
 #pragma unroll
     for (int i = 0; i < NRH; ++i) dma16(asrc[i] + (int64_t)s * 128, st + (wave * NRH + i) * 64);
+    if (X9 && wave < 4) dma16(xsrc + (int64_t)s * 128, xst + wave * 64);
   };
   auto load_w = [&](u32x4_t* st, int s) {
     if (Q4) {
@@ -383,6 +418,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   for (int j = 0; j < NRH; ++j)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) acc[j][cb] = (f32x16_t){};
+  f32x16_t accx = {};  // NRB = 9: block 8 x column block rg
 
   // operand reads: activation row 32 (2j + rg) + l32, weight row 64 cg + 32 cb
   // + l32, chunk 4 half + kk, swizzled by the row (both rows are = l32 mod 16)
@@ -396,16 +432,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   // RG: the wave's row group, a constant, so that row group 1 of an odd block
   // count skips its last block (rows past the tile) without a branch
   auto step = [&](auto rgc, const u32x4_t* sa, const u32x4_t* sw, u32x4_t* na, int a_next, u32x4_t* nw,
-                  int w_next) {
+                  int w_next, const u32x4_t* sx, u32x4_t* nx) {
     constexpr int RG = decltype(rgc)::value;
     u32x4_t af[2][NRH], bf[2][2];
     u32x4_t bq[2];
     uint32_t bg[2] = {0, 0};
+    u32x4_t ax[KK];  // NRB = 9: block 8's operands of the whole step, read before this step's transfers
+    if (X9) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) ax[kk] = sx[l32 * CPR + ((4 * half + kk) ^ swr)];
+    }
     auto read_af = [&](u32x4_t (&f)[NRH], int kk) {
       const int q = (4 * half + kk) ^ swr;
 #pragma unroll
       for (int j = 0; j < NRH; ++j)
-        if (2 * j + RG < NRB) f[j] = sa[(32 * (2 * j + RG) + l32) * CPR + q];
+        if (2 * j + RG < NRBm) f[j] = sa[(32 * (2 * j + RG) + l32) * CPR + q];
     };
     auto read_bf = [&](u32x4_t (&f)[2], int kk) {
       const int q = (4 * half + kk) ^ swr;
@@ -434,14 +475,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
       for (int cb = 0; cb < 2; ++cb) bw[cb] = Q4 ? dequant8(bq[cb][kk], bg[cb]) : bf[kk & 1][cb];
 #pragma unroll
       for (int j = 0; j < NRH; ++j)
-        if (2 * j + RG < NRB)
+        if (2 * j + RG < NRBm)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
           acc[j][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[kk & 1][j]),
                                                                __builtin_bit_cast(bf16x8_t, bw[cb]),
                                                                acc[j][cb], 0, 0, 0);
+      if (X9)
+        accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ax[kk]),
+                                                       __builtin_bit_cast(bf16x8_t, bw[RG]), accx, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (kk == 0) load_a(na, a_next);
+      if (kk == 0) load_a(na, nx, a_next);
       if (kk == 1) load_w(nw, w_next);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -453,8 +497,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   // into a stage nobody reads.
   auto clampst = [&](int st) { return st < nsteps ? st : nsteps - 1; };
 #pragma unroll
-  for (int d = 0; d < DW - 1; ++d) load_w(ring.w[d], clampst(d));
-  load_a(ring.a[0], 0);
+  for (int d = 0; d < DWT - 1; ++d) load_w(ring.w[d], clampst(d));
+  load_a(ring.a[0], ring.x[0], 0);
 
   // The K loop, one copy per kind of wave (a branch inside the loop would
   // merge the compiler's wait bookkeeping of both kinds at every step).
@@ -470,17 +514,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
         // s = 0 the activation transfers were the last ones.  Own operand
         // reads of step s-1 are done too (lgkmcnt 0), so the stages of step
         // s-1 may be refilled once every wave has passed the barrier.
-        if (s == 0)
+        // (two weight stages: the weights of step s were the last transfers)
+        if (s == 0 || DWT == 2)
           wait_vm_lgkm0<0>();
         else
           wait_vm_lgkm0<NWC>();
         barrier_only();
         if (decltype(cols)::value) {
-          step(rgc, ring.a[u % DA], ring.w[u % DW], ring.a[(u + 1) % DA], clampst(s + 1), ring.w[(u + DW - 1) % DW],
-               clampst(s + DW - 1));
+          step(rgc, ring.a[u % DA], ring.w[u % DWT], ring.a[(u + 1) % DA], clampst(s + 1),
+               ring.w[(u + DWT - 1) % DWT], clampst(s + DWT - 1), ring.x[u % DA], ring.x[(u + 1) % DA]);
         } else {
-          load_a(ring.a[(u + 1) % DA], clampst(s + 1));
-          load_w(ring.w[(u + DW - 1) % DW], clampst(s + DW - 1));
+          load_a(ring.a[(u + 1) % DA], ring.x[(u + 1) % DA], clampst(s + 1));
+          load_w(ring.w[(u + DWT - 1) % DWT], clampst(s + DWT - 1));
         }
       }
     }
@@ -500,8 +545,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   wait_vm_lgkm0<0>();
   barrier_only();
   if (MODE == 2) {
-    combine_epilogue<NRH>(p, tl, panel, ring, acc, wave_cols, cg, rg, half, l32);
+    combine_epilogue<NRH>(p, tl, panel, ring0, acc, wave_cols, cg, rg, half, l32);
     return;
+  }
+  // NRB = 9, gate/up: block 8's up values (row group 1) go to the gate
+  // waves (row group 0) of the column group through LDS; every wave passes
+  // the barrier (none has left yet)
+  float* xch = (float*)ring.w[0] + (cg * 64 + lane) * 16;
+  if (X9 && MODE == 0) {
+    if (wave_cols && rg == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[r] = accx[r];
+    }
+    wait_vm_lgkm0<0>();
+    barrier_only();
   }
   if (!wave_cols) return;
   u32x4_t* smem = ring.a[0];
@@ -544,6 +601,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
+  if (X9) {
+    // block 8 (rows 256..287): gate/up -> row group 0 writes h for its 32
+    // columns; down -> each wave writes its column block's 32 columns
+    if (MODE == 0 && rg == 1) return;
+    constexpr int XC = 32;  // columns of block 8 per wave
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+      const float v = MODE == 0 ? silu(accx[r]) * xch[r] : accx[r];
+      stage[row * XC + l32] = (uint16_t)f32_to_bf16(v);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int xcol0 = MODE == 0 ? ncol0 : ncol0 + 32 * rg;
+#pragma unroll
+    for (int c = lane; c < 32 * (XC / 8); c += 64) {
+      const int row = c / (XC / 8), q = c % (XC / 8);
+      const int grow = 256 + row;
+      const int col = xcol0 + 8 * q;
+      if (grow < tl.rows && col < N)
+        *(u32x4_t*)(obase + ((int64_t)tl.pos0 + grow) * ldo + col) = *(const u32x4_t*)(stage + row * XC + 8 * q);
+    }
+  }
 }
 
 // One routed tile, its inner loop specialised per count of 32-row blocks.
@@ -557,7 +638,8 @@ __device__ __forceinline__ void routed_tile(const GemmArgs& p, const Tile& tl, i
     case 5: gemm_tile<MODE, 5, Q4, NT>(p, tl, panel, rg); break;
     case 6: gemm_tile<MODE, 6, Q4, NT>(p, tl, panel, rg); break;
     case 7: gemm_tile<MODE, 7, Q4, NT>(p, tl, panel, rg); break;
-    default: gemm_tile<MODE, 8, Q4, NT>(p, tl, panel, rg); break;
+    case 8: gemm_tile<MODE, 8, Q4, NT>(p, tl, panel, rg); break;
+    default: gemm_tile<MODE, 9, Q4, NT>(p, tl, panel, rg); break;
   }
 }
 
@@ -623,7 +705,7 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmArgs p) {
   // them and keeps the default policy, as does the shared expert).  Not for
   // row-major 4-bit codes: a step takes a quarter of each row's cache line,
   // and the next three steps need the rest.
-  if ((!Q4 || p.tiled) && tl.g < p.E && tl.r0 == 0 && tl.rows < BM)
+  if ((!Q4 || p.tiled) && tl.g < p.E && tl.r0 == 0 && tl.rows != BM)
     routed_tile<MODE, Q4, true>(p, tl, panel, rg);
   else
     routed_tile<MODE, Q4, false>(p, tl, panel, rg);

@@ -224,7 +224,10 @@ __global__ __launch_bounds__(1024) void k_route_scan(const uint64_t* __restrict_
   int routed_total;
   const int off = block_exclusive_scan(tid < E ? total : 0, s_wave, &routed_total);
   // tile counts per group, scan
-  const int nt = tid < E ? (total + kTileM - 1) / kTileM : 0;
+  // tiles of kTileM rows; a group's last 1..32 rows past a multiple of
+  // kTileM stay with the tile before (the last tile takes up to kTileM + 32
+  // rows), so that group's weights are streamed once fewer
+  const int nt = tid < E && total > 0 ? (total <= kTileM + 32 ? 1 : (total - 32 + kTileM - 1) / kTileM) : 0;
   int routed_tiles;
   const int tstart = block_exclusive_scan(nt, s_wave, &routed_tiles);
   if (tid < E) {
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(const uint64_t* __restrict_
       Tile tl;
       tl.g = tid;
       tl.r0 = r0;
-      tl.rows = total - r0 < kTileM ? total - r0 : kTileM;
+      tl.rows = i == nt - 1 ? total - r0 : kTileM;
       tl.pos0 = off + r0;
       tiles[tstart + i] = tl;
     }

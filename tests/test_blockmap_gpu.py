@@ -3,10 +3,12 @@
 "Optimizing on-device inference for Apple Silicon", section "Keep expert
 routing on the GPU": after the histogram, prefix scan and scatter, a block
 map lists the fixed-size blocks of rows the grouped matrix multiplication
-works on.  Here a group of c rows is cut into ceil(c / 256) tiles (all of
-256 rows but the last), routed groups in expert order, then the shared
-expert's tokens in order; the tile count is the sum of ceil(c_g / 256) plus
-ceil(M / 256), and every row of every group lies in exactly one tile."""
+works on.  Here a routed group of c rows is one tile when c <= 288, else
+ceil((c - 32) / 256) tiles, all of 256 rows but the last, which takes the
+rest (up to 288 rows: a group's last 1..32 rows past a multiple of 256 ride
+with the tile before, so its weights are streamed once fewer); routed groups
+come in expert order, then the shared expert's tokens in order in tiles of
+256 rows but the last; every row of every group lies in exactly one tile."""
 import numpy as np
 import pytest
 import torch
@@ -16,6 +18,7 @@ from gpu_util import HostLayer, device_layer, moe, rand_case, routing_buffers, u
 
 pytestmark = pytest.mark.gpu
 TILE = 256
+LAST = TILE + 32  # the largest last tile of a routed group
 
 
 @pytest.fixture(autouse=True, scope="module")
@@ -29,8 +32,13 @@ def expected_tiles(counts, offsets, M, shared):
     E = len(counts)
     want = []
     for g in range(E):
-        for r0 in range(0, int(counts[g]), TILE):
-            want.append((g, r0, min(TILE, int(counts[g]) - r0), int(offsets[g]) + r0))
+        c = int(counts[g])
+        r0 = 0
+        while c - r0 > LAST:  # full tiles while more than a last tile's worth is left
+            want.append((g, r0, TILE, int(offsets[g]) + r0))
+            r0 += TILE
+        if c > r0:
+            want.append((g, r0, c - r0, int(offsets[g]) + r0))
     if shared:
         for r0 in range(0, M, TILE):
             want.append((E, r0, min(TILE, M - r0), r0))
@@ -65,14 +73,15 @@ def check_blockmap(g, cap, M, k, shared):
     assert counts.sum() == M * k and offsets[E] == M * k
     n = int(g["num_tiles"][0])
     want = expected_tiles(counts, offsets, M, shared)
-    assert n == len(want) == int(np.sum((counts + TILE - 1) // TILE)) + (-(-M // TILE) if shared else 0)
+    nt = np.where(counts <= LAST, (counts > 0).astype(np.int64), -(-(counts.astype(np.int64) - 32) // TILE))
+    assert n == len(want) == int(nt.sum()) + (-(-M // TILE) if shared else 0)
     assert n <= cap
     got = g["tiles"][:n].astype(np.int64)
     assert np.array_equal(got, want), "block map differs"
     # every row of every group in exactly one tile
     cover = np.zeros(M * k + (M if shared else 0), dtype=np.int64)
     for gg, r0, rows, pos0 in got:
-        assert 0 < rows <= TILE
+        assert 0 < rows <= (LAST if gg < E else TILE)
         base = 0 if gg < E else M * k
         cover[base + pos0: base + pos0 + rows] += 1
     assert (cover == 1).all()
@@ -103,10 +112,13 @@ def test_block_map_skewed_prefill():
 
 
 @pytest.mark.parametrize("M,E,k,shared", [(520, 32, 4, True), (600, 1, 1, False), (1, 16, 2, True),
-                                          (257, 8, 8, True), (4100, 4, 2, False)])
+                                          (257, 8, 8, True), (4100, 4, 2, False), (288, 4, 4, True),
+                                          (289, 2, 2, False), (544, 1, 1, True), (545, 1, 1, False),
+                                          (800, 1, 1, True)])
 def test_block_map_hot_and_edge(M, E, k, shared):
-    """A bias that sends every token to expert 5 first (or a single expert), one row, k = E, and
-    groups just over a multiple of the tile height."""
+    """A bias that sends every token to expert 5 first (or a single expert), one row, k = E, groups
+    just over a multiple of the tile height and at the edges of the last tile's 288 rows (288 and
+    289, 544 = 256 + 288 and 545, 800 = 2 * 256 + 288)."""
     Is = 64 if shared else 0
     x, r, ex, s, bias = rand_case(M, 128, E, k, 64, Is, seed=M, hot=5 if E > 5 else None)
     g, cap = run_blockmap(upload(x), upload(r), upload(ex), upload(s) if shared else None, k,
