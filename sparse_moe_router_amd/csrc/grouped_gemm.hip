@@ -29,8 +29,11 @@
 // rows cost nothing.
 //
 // Launch order is XCD-aware: workgroup b runs on XCD b % 8; the tiles are
-// dealt to the XCDs round-robin (heaviest first) and the panels of a tile
-// stay on one XCD, so its activation rows are re-read from that XCD's L2.
+// dealt to the XCDs round-robin and the panels of a tile stay on one XCD,
+// so its activation rows are re-read from that XCD's L2.  The gate/up launch
+// takes the tiles in the order the routing scan lists them for it (most
+// 32-row blocks first: the longest units start first and the short ones
+// fill the end), the down launch the block map from its end.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -649,10 +652,8 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmArgs p) {
   const Ring rg{{sA0, sA1}, {sW0, sW1, sW2}};
 
   // ---- tile of this workgroup, XCD-aware: workgroup b runs on XCD b % 8;
-  //      XCD x takes the tiles t = x (mod 8), all panels of a tile in a row
-  //      (its activation rows are re-read from that XCD's L2), the last tiles
-  //      of the block map first (the shared expert's full 256-row tiles, the
-  //      heaviest, start early and spread over all XCDs)
+  //      XCD x takes the tiles t = x (mod 8) of its list, all panels of a
+  //      tile in a row (its activation rows are re-read from that XCD's L2)
   if (MODE == 2) {  // the shared expert's tokens in tiles of 128, panel-minor
     // tile t on XCD t % 8 with all its panels: the tile's shared-expert h
     // rows are fetched into that XCD's L2 once, not once per panel
@@ -692,8 +693,12 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmArgs p) {
   const int nt = ntl < p.max_tiles ? ntl : p.max_tiles;
   const int xcd = b & 7, local = b >> 3;
   const int j = local / p.npan, panel = local % p.npan;  // j-th tile of this XCD
-  const int t = nt - 1 - (8 * j + (7 - xcd));            // from the end, dealt round-robin
-  if (t < 0) return;
+  // gate/up: the launch-order list from its start; down: the block map from
+  // its end (its short tiles, which mostly stream weights, then run among
+  // the long ones, which mostly compute: the down tiles' weight panels are a
+  // quarter of the gate/up ones', so there the mix pays more than the order)
+  const int t = MODE == 0 ? 8 * j + xcd : nt - 1 - (8 * j + (7 - xcd));
+  if (t < 0 || t >= nt) return;
   const Tile tl = p.tiles[t];
   if (MODE == 0) {
     const int Ig = tl.g >= p.E ? p.Is : p.I;

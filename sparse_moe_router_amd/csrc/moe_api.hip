@@ -110,6 +110,7 @@ bool make_plan(Plan* p, int64_t M, int H, int E, int I, int Is, int k, bool gemv
     ok &= place(&off, &p->inv, A * 4);
     ok &= place(&off, &p->tiles, (uint64_t)p->max_tiles * sizeof(Tile));
     ok &= place(&off, &p->ntiles, 4);
+    ok &= place(&off, &p->tiles_lpt, (uint64_t)p->max_tiles * sizeof(Tile));
     ok &= place(&off, &p->h_r, A * I * 2);
     ok &= place(&off, &p->h_s, (uint64_t)M * Is * 2);
     ok &= place(&off, &p->y_r, A * H * 2);
@@ -226,8 +227,8 @@ moe_status_t run_routing_grouped(const Plan& p, const moe_desc_t* d, const void*
   if ((e = tr.run(MOE_K_TOPK, [&](const Launch& lc) { return launch_topk(L, ids, w, cmask, p.M, p.E, p.k, lc); })) != hipSuccess)
     return hip_fail(e);
   if ((e = tr.run(MOE_K_ROUTE_SCAN, [&](const Launch& lc) {
-         return launch_route_scan(cmask, ws_ptr<int32_t>(ws, p.cbase), counts, offsets, tiles, ntiles, p.M, p.E,
-                                  p.k, p.shared, lc);
+         return launch_route_scan(cmask, ws_ptr<int32_t>(ws, p.cbase), counts, offsets, tiles, ntiles,
+                                  ws_ptr<Tile>(ws, p.tiles_lpt), p.M, p.E, p.k, p.shared, lc);
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = tr.run(MOE_K_ROUTE_SCATTER, [&](const Launch& lc) {
@@ -447,15 +448,17 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   // down launch, its down GEMM carries the weighted combine in a launch of
   // its own; without one, a plain combine follows the down launch
   const int skip = p.shared ? (int)((p.M + kTileM - 1) / kTileM) : 0;
-  // the block map where the scan wrote it: the caller's buffers when it asked for them
+  // the block map and its count where the scan wrote them (the caller's
+  // buffers when it asked for them), the gate/up launch's order of the tiles
   const Tile* tiles = (routing && routing->tiles) ? (const Tile*)routing->tiles : ws_ptr<Tile>(workspace, p.tiles);
   const int32_t* ntiles = (routing && routing->num_tiles) ? routing->num_tiles : ws_ptr<int32_t>(workspace, p.ntiles);
+  const Tile* tiles_lpt = ws_ptr<Tile>(workspace, p.tiles_lpt);
   // the shared expert's gate/up tiles run at the start of the down launch (the
   // shared down + combine launch after it is the first to read their h)
   const uint16_t* x_sgu = p.shared ? xb : nullptr;
   if ((e = tr.run(MOE_K_GEMM_GATEUP, [&](const Launch& lc) {
-         return wt.q4 ? launch_gemm_gateup_q4(xb, wt.eq, wt.sq, perm, tiles, ntiles, h_r, h_s, skip, p, lc)
-                      : launch_gemm_gateup(xb, wt.ew, wt.sw, perm, tiles, ntiles, h_r, h_s, skip, p, lc);
+         return wt.q4 ? launch_gemm_gateup_q4(xb, wt.eq, wt.sq, perm, tiles_lpt, ntiles, h_r, h_s, skip, p, lc)
+                      : launch_gemm_gateup(xb, wt.ew, wt.sw, perm, tiles_lpt, ntiles, h_r, h_s, skip, p, lc);
        })) != hipSuccess)
     return hip_fail(e);
   if ((e = tr.run(MOE_K_GEMM_DOWN, [&](const Launch& lc) {

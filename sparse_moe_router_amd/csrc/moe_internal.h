@@ -66,6 +66,7 @@ struct Plan {
   int64_t max_tiles;
   // byte offsets into the workspace (all 256-aligned)
   size_t logits, ids, w, cmask, cbase, counts, offsets, perm, inv, tiles, ntiles, h_r, h_s, y_r;
+  size_t tiles_lpt;  // grouped path: the block map's tiles in launch order
   size_t un_count, un_exp, un_off, un_pair, un_unit;  // small-batch path: union of the selected experts
   size_t arrive;  // decode path, two launches: arrival counters of the gate/up workgroups, one per slot
   size_t total;
@@ -113,19 +114,23 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const flo
 // Top-k + weights per token, and the token's bits in the per-chunk expert masks.
 hipError_t launch_topk(const float* L, int32_t* ids, float* w, uint64_t* cmask, int64_t M, int E, int k,
                        const Launch& lc);
-// counts, offsets, per-chunk bases, block map.
+// counts, offsets, per-chunk bases, block map; the same tiles in the gate/up
+// launch's order (tiles_lpt: the routed tiles by count of 32-row blocks,
+// most first, then the shared expert's in order).
 hipError_t launch_route_scan(const uint64_t* cmask, int32_t* cbase, int32_t* counts, int32_t* offsets,
-                             Tile* tiles, int32_t* ntiles, int64_t M, int E, int k, bool shared, const Launch& lc);
+                             Tile* tiles, int32_t* ntiles, Tile* tiles_lpt, int64_t M, int E, int k, bool shared,
+                             const Launch& lc);
 // perm / inv from the chunk masks and bases.
 hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const int32_t* cbase,
                                 int32_t* perm, int32_t* inv, int64_t M, int E, int k, const Launch& lc);
-// Grouped gate/up GEMM + SwiGLU -> h (bf16), leaving out the last skip_tail
-// tiles of the block map (the shared expert's, when the down launch runs them).
+// Grouped gate/up GEMM + SwiGLU -> h (bf16) over the tiles in its launch
+// order (tiles_lpt of launch_route_scan), leaving out the last skip_tail (the
+// shared expert's, when the down launch runs them).
 hipError_t launch_gemm_gateup(const uint16_t* x, const uint16_t* expert_w, const uint16_t* shared_w,
                               const int32_t* perm, const Tile* tiles, const int32_t* ntiles,
                               uint16_t* h_r, uint16_t* h_s, int skip_tail, const Plan& p, const Launch& lc);
-// Grouped down GEMM -> y (bf16), leaving out the last skip_tail tiles of
-// the block map (the shared expert's, when launch_shared_down_combine does
+// Grouped down GEMM -> y (bf16) over the block map, leaving out its last
+// skip_tail tiles (the shared expert's, when launch_shared_down_combine does
 // them).  With x_shared_gu given, the launch first runs the shared expert's
 // gate/up tiles (x -> h_s), which the gate/up launch then leaves out.
 hipError_t launch_gemm_down(const uint16_t* h_r, uint16_t* h_s, const uint16_t* expert_w,

@@ -183,16 +183,21 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
 
 // Single workgroup.  Reads the per-(chunk, expert) masks, writes counts,
 // offsets, the block map, and cbase = the group position of the chunk's
-// first assignment to each expert.
+// first assignment to each expert.  Also the same tiles in the order the
+// gate/up launch takes them (tiles_lpt): the routed tiles by count of 32-row
+// blocks, most first, so that the longest units start first and the short
+// ones fill the end of the launch, then the shared expert's in order.
 __global__ __launch_bounds__(1024) void k_route_scan(const uint64_t* __restrict__ cmask,
                                                      int32_t* __restrict__ cbase,
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets,
                                                      Tile* __restrict__ tiles,
-                                                     int32_t* __restrict__ ntiles, int64_t M, int E,
+                                                     int32_t* __restrict__ ntiles,
+                                                     Tile* __restrict__ tiles_lpt, int64_t M, int E,
                                                      int k, int shared) {
   __shared__ int s_part[1024];
   __shared__ int s_wave[40];
+  __shared__ int s_cls[10];  // routed tiles per count of 32-row blocks (1..9), then each class's next slot
   const int tid = threadIdx.x;
   const int64_t nchunk = (M + kChunk - 1) / kChunk;
   const int P = 1024 / E;  // threads per expert (E <= 1024)
@@ -255,6 +260,41 @@ __global__ __launch_bounds__(1024) void k_route_scan(const uint64_t* __restrict_
     tiles[routed_tiles + i] = tl;
   }
   if (tid == 0) *ntiles = routed_tiles + nts;
+  // launch order: class c = 32-row blocks of a tile (full tiles 8, a group's
+  // last tile 1..9), classes from 9 down; the order inside a class is that
+  // of the LDS atomics (it decides which workgroup runs a tile, not what is
+  // computed); the shared expert's tiles after them as in the block map
+  if (tid < 10) s_cls[tid] = 0;
+  __syncthreads();
+  const int last_rows = nt > 0 ? total - (nt - 1) * kTileM : 0;
+  if (tid < E && nt > 0) {
+    if (nt > 1) atomicAdd(&s_cls[8], nt - 1);
+    atomicAdd(&s_cls[(last_rows + 31) >> 5], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int c = 9; c >= 1; --c) {
+      const int v = s_cls[c];
+      s_cls[c] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  if (tid < E && nt > 0) {
+    const int f = nt > 1 ? atomicAdd(&s_cls[8], nt - 1) : 0;
+    for (int i = 0; i < nt - 1; ++i) tiles_lpt[f + i] = Tile{tid, i * kTileM, kTileM, off + i * kTileM};
+    const int r0 = (nt - 1) * kTileM;
+    tiles_lpt[atomicAdd(&s_cls[(last_rows + 31) >> 5], 1)] = Tile{tid, r0, last_rows, off + r0};
+  }
+  for (int i = tid; i < nts; i += 1024) {
+    Tile tl;
+    tl.g = E;
+    tl.r0 = i * kTileM;
+    tl.rows = (int)(M - tl.r0 < kTileM ? M - tl.r0 : kTileM);
+    tl.pos0 = tl.r0;
+    tiles_lpt[routed_tiles + i] = tl;
+  }
   // pass 2: chunk bases.  s_part[part*E + e] -> start of the part within expert e
   __syncthreads();
   if (tid < E) {
@@ -330,9 +370,10 @@ hipError_t launch_topk(const float* L, int32_t* ids, float* w, uint64_t* cmask, 
 }
 
 hipError_t launch_route_scan(const uint64_t* cmask, int32_t* cbase, int32_t* counts, int32_t* offsets,
-                             Tile* tiles, int32_t* ntiles, int64_t M, int E, int k, bool shared, const Launch& lc) {
-  return launch(lc, k_route_scan, dim3(1), dim3(1024), cmask, cbase, counts, offsets, tiles, ntiles, M, E, k,
-                shared ? 1 : 0);
+                             Tile* tiles, int32_t* ntiles, Tile* tiles_lpt, int64_t M, int E, int k, bool shared,
+                             const Launch& lc) {
+  return launch(lc, k_route_scan, dim3(1), dim3(1024), cmask, cbase, counts, offsets, tiles, ntiles, tiles_lpt, M,
+                E, k, shared ? 1 : 0);
 }
 
 hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const int32_t* cbase,
