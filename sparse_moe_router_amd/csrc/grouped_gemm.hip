@@ -253,6 +253,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   constexpr int NRH = (NRBm + 1) / 2;  // row blocks of row group 0 (row group 1: NRBm / 2)
   constexpr int DWT = X9 ? 2 : DW;
   constexpr int U = DA * DWT;          // unroll: every ring stage index static
+  // the K-step pipeline runs across steps (two sub-steps' operands live at
+  // the step boundary) where the registers allow it without spilling
+  constexpr bool XPIPE = NRB <= 8;
   struct RingT {
     u32x4_t* a[DA];
     u32x4_t* w[DW];
@@ -426,109 +429,137 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const Tile& tl, int
   // operand reads: activation row 32 (2j + rg) + l32, weight row 64 cg + 32 cb
   // + l32, chunk 4 half + kk, swizzled by the row (both rows are = l32 mod 16)
   const int swr = (l32 >> 1) & 7;
-  // One K-step from stages (sa, sw).  The step's transfers (activation step
-  // a_next into na, weight step w_next into nw) are issued between the MFMA
-  // sub-steps: a wave that stalls issuing them leaves its SIMD to the other
-  // wave there, instead of all transfers of a step queueing up front.  The
-  // scheduling barriers keep that order (and the transfers after the barrier
-  // of the step).
-  // RG: the wave's row group, a constant, so that row group 1 of an odd block
-  // count skips its last block (rows past the tile) without a branch
-  auto step = [&](auto rgc, const u32x4_t* sa, const u32x4_t* sw, u32x4_t* na, int a_next, u32x4_t* nw,
-                  int w_next, const u32x4_t* sx, u32x4_t* nx) {
+  auto clampst = [&](int st) { return st < nsteps ? st : nsteps - 1; };
+
+  // The K loop, one copy per kind of wave (a branch inside the loop would
+  // merge the compiler's wait bookkeeping of both kinds at every step).
+  //
+  // Each step runs KK MFMA sub-steps; sub-step kk + 1's operands are read
+  // from LDS while sub-step kk's MFMAs run.  The pipeline also runs across
+  // steps: the barrier that opens step s + 1 and the reads of its first
+  // sub-step's operands come before step s's last sub-step of MFMAs (whose
+  // operands are already in registers), so the MFMA pipe keeps working
+  // through every step's barrier and first LDS round trip.  Per accumulator
+  // the MFMA order is that of the plain loop.  The step's transfers
+  // (activation step s + 1 into the stage of step s - 1, weight step
+  // s + DWT - 1 likewise) are issued between the MFMA sub-steps: a wave that
+  // stalls issuing them leaves its SIMD to the other wave there, instead of
+  // all transfers of a step queueing up front; the scheduling barriers keep
+  // that order.  RG: the wave's row group, a constant, so that row group 1 of
+  // an odd block count skips its last block (rows past the tile) without a
+  // branch.
+  auto kloop = [&](auto cols, auto nw, auto rgc) {
+    constexpr bool XP = XPIPE;
+    constexpr bool COLS = decltype(cols)::value;
+    constexpr int NWC = decltype(nw)::value;
     constexpr int RG = decltype(rgc)::value;
-    u32x4_t af[2][NRH], bf[2][2];
-    u32x4_t bq[2];
-    uint32_t bg[2] = {0, 0};
-    u32x4_t ax[KK];  // NRB = 9: block 8's operands of the whole step, read before this step's transfers
-    if (X9) {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) ax[kk] = sx[l32 * CPR + ((4 * half + kk) ^ swr)];
-    }
-    auto read_af = [&](u32x4_t (&f)[NRH], int kk) {
+    u32x4_t af[2][NRH], bf[2][2], ax[2];  // operands of sub-steps of parity 0 / 1
+    u32x4_t bq[2];                        // 4-bit: the step's codes of the wave's two weight rows
+    uint32_t bg[2] = {0, 0};              // 4-bit: their group words
+    auto read_af = [&](const u32x4_t* sa, u32x4_t (&f)[NRH], int kk) {
       const int q = (4 * half + kk) ^ swr;
 #pragma unroll
       for (int j = 0; j < NRH; ++j)
         if (2 * j + RG < NRBm) f[j] = sa[(32 * (2 * j + RG) + l32) * CPR + q];
     };
-    auto read_bf = [&](u32x4_t (&f)[2], int kk) {
+    auto read_bf = [&](const u32x4_t* sw, u32x4_t (&f)[2], int kk) {
       const int q = (4 * half + kk) ^ swr;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) f[cb] = sw[(64 * cg + 32 * cb + l32) * CPR + q];
     };
-    if (Q4) {
+    auto read_ax = [&](const u32x4_t* sx, u32x4_t& f, int kk) { f = sx[l32 * CPR + ((4 * half + kk) ^ swr)]; };
+    // the first sub-step's operands of the step held in stages (sa, sw, sx)
+    auto pre = [&](const u32x4_t* sa, const u32x4_t* sw, const u32x4_t* sx) {
+      if (!COLS) return;
+      if (Q4) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int R = 64 * cg + 32 * cb + l32;
-        bq[cb] = sw[2 * R + half];
-        bg[cb] = ((const uint32_t*)(sw + 2 * NWR))[R];
+        for (int cb = 0; cb < 2; ++cb) {
+          const int R = 64 * cg + 32 * cb + l32;
+          bq[cb] = sw[2 * R + half];
+          bg[cb] = ((const uint32_t*)(sw + 2 * NWR))[R];
+        }
+      } else {
+        read_bf(sw, bf[0], 0);
       }
-    } else {
-      read_bf(bf[0], 0);
-    }
-    read_af(af[0], 0);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) {
-        read_af(af[(kk + 1) & 1], kk + 1);
-        if (!Q4) read_bf(bf[(kk + 1) & 1], kk + 1);
-      }
-      u32x4_t bw[2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) bw[cb] = Q4 ? dequant8(bq[cb][kk], bg[cb]) : bf[kk & 1][cb];
-#pragma unroll
-      for (int j = 0; j < NRH; ++j)
-        if (2 * j + RG < NRBm)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          acc[j][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[kk & 1][j]),
-                                                               __builtin_bit_cast(bf16x8_t, bw[cb]),
-                                                               acc[j][cb], 0, 0, 0);
-      if (X9)
-        accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ax[kk]),
-                                                       __builtin_bit_cast(bf16x8_t, bw[RG]), accx, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk == 0) load_a(na, nx, a_next);
-      if (kk == 1) load_w(nw, w_next);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
+      read_af(sa, af[0], 0);
+      if (X9) read_ax(sx, ax[0], 0);
+    };
 
-  // prologue: weight steps 0 .. DW-2, then activation step 0.  Transfers
-  // are never conditional (a branch would merge the compiler's wait
-  // bookkeeping into a full wait): steps past the end re-read the last step
-  // into a stage nobody reads.
-  auto clampst = [&](int st) { return st < nsteps ? st : nsteps - 1; };
+    // prologue: weight steps 0 .. DWT-2, then activation step 0; every
+    // wave's transfers of step 0 done; step 0's first operands.  Transfers
+    // are never conditional (a branch would merge the compiler's wait
+    // bookkeeping into a full wait): steps past the end re-read the last step
+    // into a stage nobody reads.
 #pragma unroll
-  for (int d = 0; d < DWT - 1; ++d) load_w(ring.w[d], clampst(d));
-  load_a(ring.a[0], ring.x[0], 0);
+    for (int d = 0; d < DWT - 1; ++d) load_w(ring.w[d], clampst(d));
+    load_a(ring.a[0], ring.x[0], 0);
+    wait_vm_lgkm0<0>();
+    barrier_only();
+    pre(ring.a[0], ring.w[0], ring.x[0]);
 
-  // The K loop, one copy per kind of wave (a branch inside the loop would
-  // merge the compiler's wait bookkeeping of both kinds at every step).
-  auto kloop = [&](auto cols, auto nw, auto rgc) {
-    constexpr int NWC = decltype(nw)::value;
     for (int s0 = 0; s0 < nsteps; s0 += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int s = s0 + u;
         if (s >= nsteps) break;  // uniform
-        // own transfers of step s done: after activation step s (issued
-        // during step s-1) only a weight step was issued (NWC transfers); at
-        // s = 0 the activation transfers were the last ones.  Own operand
-        // reads of step s-1 are done too (lgkmcnt 0), so the stages of step
-        // s-1 may be refilled once every wave has passed the barrier.
-        // (two weight stages: the weights of step s were the last transfers)
-        if (s == 0 || DWT == 2)
-          wait_vm_lgkm0<0>();
-        else
-          wait_vm_lgkm0<NWC>();
-        barrier_only();
-        if (decltype(cols)::value) {
-          step(rgc, ring.a[u % DA], ring.w[u % DWT], ring.a[(u + 1) % DA], clampst(s + 1),
-               ring.w[(u + DWT - 1) % DWT], clampst(s + DWT - 1), ring.x[u % DA], ring.x[(u + 1) % DA]);
-        } else {
-          load_a(ring.a[(u + 1) % DA], ring.x[(u + 1) % DA], clampst(s + 1));
-          load_w(ring.w[(u + DWT - 1) % DWT], clampst(s + DWT - 1));
+        const u32x4_t* sa = ring.a[u % DA];
+        const u32x4_t* sw = ring.w[u % DWT];
+        const u32x4_t* sx = ring.x[u % DA];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          u32x4_t bw[2];
+          if (COLS) {
+            if (kk + 1 < KK) {
+              read_af(sa, af[(kk + 1) & 1], kk + 1);
+              if (!Q4) read_bf(sw, bf[(kk + 1) & 1], kk + 1);
+              if (X9) read_ax(sx, ax[(kk + 1) & 1], kk + 1);
+            }
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) bw[cb] = Q4 ? dequant8(bq[cb][kk], bg[cb]) : bf[kk & 1][cb];
+          }
+          if (kk == KK - 1 && XP) {
+            // open step s + 1: own transfers of step s + 1 done (after them
+            // only this step's weight transfers were issued, NWC of them; with
+            // two weight stages those are step s + 1's own), own operand
+            // reads of step s done (lgkmcnt 0), then the barrier: every
+            // wave's transfers of step s + 1 have landed and no wave reads the
+            // stages of step s any more (step s + 1 refills them).  Past the
+            // last step this reads stale stages into registers nobody uses.
+            __builtin_amdgcn_sched_barrier(0);
+            if (DWT == 2)
+              wait_vm_lgkm0<0>();
+            else
+              wait_vm_lgkm0<NWC>();
+            barrier_only();
+            pre(ring.a[(u + 1) % DA], ring.w[(u + 1) % DWT], ring.x[(u + 1) % DA]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (COLS) {
+#pragma unroll
+            for (int j = 0; j < NRH; ++j)
+              if (2 * j + RG < NRBm)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                  acc[j][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[kk & 1][j]),
+                                                                       __builtin_bit_cast(bf16x8_t, bw[cb]),
+                                                                       acc[j][cb], 0, 0, 0);
+            if (X9)
+              accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ax[kk & 1]),
+                                                             __builtin_bit_cast(bf16x8_t, bw[RG]), accx, 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (kk == 0) load_a(ring.a[(u + 1) % DA], ring.x[(u + 1) % DA], clampst(s + 1));
+          if (kk == 1) load_w(ring.w[(u + DWT - 1) % DWT], clampst(s + DWT - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          if (kk == KK - 1 && !XP) {  // the same, after the step's last MFMAs
+            if (DWT == 2)
+              wait_vm_lgkm0<0>();
+            else
+              wait_vm_lgkm0<NWC>();
+            barrier_only();
+            pre(ring.a[(u + 1) % DA], ring.w[(u + 1) % DWT], ring.x[(u + 1) % DA]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     }
