@@ -207,7 +207,8 @@ typedef enum {
   MOE_K_SM_DOWN = 14,          /* small batch: down projections + combine */
   MOE_K_DEC_ROUTE = 15,        /* decode, two launches: router scores, shared expert gate/up */
   MOE_K_DEC_EXPERTS = 16,      /* decode, two launches: top-k, routed gate/up, all down projections, combine */
-  MOE_K_SHARED_DOWN_COMBINE = 17 /* grouped path with a shared expert: its down GEMM + the weighted combine */
+  MOE_K_SHARED_DOWN_COMBINE = 17, /* grouped path with a shared expert: its down GEMM + the weighted combine */
+  MOE_K_ROUTE_SCAN_SCATTER = 18   /* grouped path, calls of up to 8192 tokens: scan, block map and scatter */
 } moe_kernel_t;
 
 /* Instrumentation for moe_layer_forward_traced: caller-created hipEvent_t

@@ -206,7 +206,8 @@ struct Tracer {
   }
 };
 
-// Routing on the grouped path: scores, top-k, chunk masks, scan + block map, scatter.
+// Routing on the grouped path: scores, top-k, chunk masks, scan + block map, scatter
+// (the last two in one launch for calls of up to 8192 tokens).
 moe_status_t run_routing_grouped(const Plan& p, const moe_desc_t* d, const void* x, const void* wr,
                                  void* ws, const moe_routing_t* r, hipStream_t s, Tracer& tr) {
   float* L = (r && r->logits) ? r->logits : ws_ptr<float>(ws, p.logits);
@@ -226,6 +227,14 @@ moe_status_t run_routing_grouped(const Plan& p, const moe_desc_t* d, const void*
     return hip_fail(e);
   if ((e = tr.run(MOE_K_TOPK, [&](const Launch& lc) { return launch_topk(L, ids, w, cmask, p.M, p.E, p.k, lc); })) != hipSuccess)
     return hip_fail(e);
+  if (route_scan_fused(p.M)) {
+    if ((e = tr.run(MOE_K_ROUTE_SCAN_SCATTER, [&](const Launch& lc) {
+           return launch_route_scan_scatter(ids, cmask, counts, offsets, tiles, ntiles, ws_ptr<Tile>(ws, p.tiles_lpt),
+                                            perm, ws_ptr<int32_t>(ws, p.inv), p.M, p.E, p.k, p.shared, lc);
+         })) != hipSuccess)
+      return hip_fail(e);
+    return MOE_OK;
+  }
   if ((e = tr.run(MOE_K_ROUTE_SCAN, [&](const Launch& lc) {
          return launch_route_scan(cmask, ws_ptr<int32_t>(ws, p.cbase), counts, offsets, tiles, ntiles,
                                   ws_ptr<Tile>(ws, p.tiles_lpt), p.M, p.E, p.k, p.shared, lc);

@@ -123,6 +123,13 @@ hipError_t launch_route_scan(const uint64_t* cmask, int32_t* cbase, int32_t* cou
 // perm / inv from the chunk masks and bases.
 hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const int32_t* cbase,
                                 int32_t* perm, int32_t* inv, int64_t M, int E, int k, const Launch& lc);
+// Scan, block map and scatter in one launch (one workgroup per 64-token
+// chunk), for calls of at most 8192 tokens (route_scan_fused); the
+// chunk-base table is not written.
+bool route_scan_fused(int64_t M);
+hipError_t launch_route_scan_scatter(const int32_t* ids, const uint64_t* cmask, int32_t* counts, int32_t* offsets,
+                                     Tile* tiles, int32_t* ntiles, Tile* tiles_lpt, int32_t* perm, int32_t* inv,
+                                     int64_t M, int E, int k, bool shared, const Launch& lc);
 // Grouped gate/up GEMM + SwiGLU -> h (bf16) over the tiles in its launch
 // order (tiles_lpt of launch_route_scan), leaving out the last skip_tail (the
 // shared expert's, when the down launch runs them).

@@ -181,7 +181,87 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   return r;
 }
 
-// Single workgroup.  Reads the per-(chunk, expert) masks, writes counts,
+// Counts, offsets, the block map and its launch-order copy (tiles_lpt),
+// from each expert's assignment count `total` (thread e < E; 0 elsewhere),
+// its exclusive offset `off` and the routed total.  Every thread of the
+// 1024-thread block calls it (it synchronises).
+//
+// Tiles of kTileM rows; a group's last 1..32 rows past a multiple of kTileM
+// stay with the tile before (the last tile takes up to kTileM + 32 rows), so
+// that group's weights are streamed once fewer.  The shared expert's tiles
+// (all M tokens in order) follow the routed ones.  Launch order: class c =
+// 32-row blocks of a tile (full tiles 8, a group's last tile 1..9), classes
+// from 9 down, so that the longest units start first and the short ones fill
+// the end of the launch; the order inside a class is that of the LDS atomics
+// (it decides which workgroup runs a tile, not what is computed); the shared
+// expert's tiles after them as in the block map.
+__device__ void write_block_map(int total, int off, int routed_total, int32_t* __restrict__ counts,
+                                int32_t* __restrict__ offsets, Tile* __restrict__ tiles,
+                                int32_t* __restrict__ ntiles, Tile* __restrict__ tiles_lpt, int* s_wave,
+                                int* s_cls, int64_t M, int E, int shared) {
+  const int tid = threadIdx.x;
+  const int nt = tid < E && total > 0 ? (total <= kTileM + 32 ? 1 : (total - 32 + kTileM - 1) / kTileM) : 0;
+  int routed_tiles;
+  const int tstart = block_exclusive_scan(nt, s_wave, &routed_tiles);
+  if (tid < E) {
+    counts[tid] = total;
+    offsets[tid] = off;
+    for (int i = 0; i < nt; ++i) {
+      const int r0 = i * kTileM;
+      Tile tl;
+      tl.g = tid;
+      tl.r0 = r0;
+      tl.rows = i == nt - 1 ? total - r0 : kTileM;
+      tl.pos0 = off + r0;
+      tiles[tstart + i] = tl;
+    }
+  }
+  if (tid == 0) offsets[E] = routed_total;
+  const int nts = shared ? (int)((M + kTileM - 1) / kTileM) : 0;
+  for (int i = tid; i < nts; i += 1024) {
+    Tile tl;
+    tl.g = E;
+    tl.r0 = i * kTileM;
+    tl.rows = (int)(M - tl.r0 < kTileM ? M - tl.r0 : kTileM);
+    tl.pos0 = tl.r0;
+    tiles[routed_tiles + i] = tl;
+  }
+  if (tid == 0) *ntiles = routed_tiles + nts;
+  if (tid < 10) s_cls[tid] = 0;
+  __syncthreads();
+  const int last_rows = nt > 0 ? total - (nt - 1) * kTileM : 0;
+  if (tid < E && nt > 0) {
+    if (nt > 1) atomicAdd(&s_cls[8], nt - 1);
+    atomicAdd(&s_cls[(last_rows + 31) >> 5], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int c = 9; c >= 1; --c) {
+      const int v = s_cls[c];
+      s_cls[c] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  if (tid < E && nt > 0) {
+    const int f = nt > 1 ? atomicAdd(&s_cls[8], nt - 1) : 0;
+    for (int i = 0; i < nt - 1; ++i) tiles_lpt[f + i] = Tile{tid, i * kTileM, kTileM, off + i * kTileM};
+    const int r0 = (nt - 1) * kTileM;
+    tiles_lpt[atomicAdd(&s_cls[(last_rows + 31) >> 5], 1)] = Tile{tid, r0, last_rows, off + r0};
+  }
+  for (int i = tid; i < nts; i += 1024) {
+    Tile tl;
+    tl.g = E;
+    tl.r0 = i * kTileM;
+    tl.rows = (int)(M - tl.r0 < kTileM ? M - tl.r0 : kTileM);
+    tl.pos0 = tl.r0;
+    tiles_lpt[routed_tiles + i] = tl;
+  }
+}
+
+// Single workgroup (calls of more than kFusedScanChunks chunks; smaller ones
+// take k_route_scan_scatter).  Reads the per-(chunk, expert) masks, writes counts,
 // offsets, the block map, and cbase = the group position of the chunk's
 // first assignment to each expert.  Also the same tiles in the order the
 // gate/up launch takes them (tiles_lpt): the routed tiles by count of 32-row
@@ -228,73 +308,8 @@ __global__ __launch_bounds__(1024) void k_route_scan(const uint64_t* __restrict_
     for (int p = 0; p < P; ++p) total += s_part[p * E + tid];
   int routed_total;
   const int off = block_exclusive_scan(tid < E ? total : 0, s_wave, &routed_total);
-  // tile counts per group, scan
-  // tiles of kTileM rows; a group's last 1..32 rows past a multiple of
-  // kTileM stay with the tile before (the last tile takes up to kTileM + 32
-  // rows), so that group's weights are streamed once fewer
-  const int nt = tid < E && total > 0 ? (total <= kTileM + 32 ? 1 : (total - 32 + kTileM - 1) / kTileM) : 0;
-  int routed_tiles;
-  const int tstart = block_exclusive_scan(nt, s_wave, &routed_tiles);
-  if (tid < E) {
-    counts[tid] = total;
-    offsets[tid] = off;
-    for (int i = 0; i < nt; ++i) {
-      const int r0 = i * kTileM;
-      Tile tl;
-      tl.g = tid;
-      tl.r0 = r0;
-      tl.rows = i == nt - 1 ? total - r0 : kTileM;
-      tl.pos0 = off + r0;
-      tiles[tstart + i] = tl;
-    }
-  }
-  if (tid == 0) offsets[E] = routed_total;
-  // shared group after the routed tiles
-  const int nts = shared ? (int)((M + kTileM - 1) / kTileM) : 0;
-  for (int i = tid; i < nts; i += 1024) {
-    Tile tl;
-    tl.g = E;
-    tl.r0 = i * kTileM;
-    tl.rows = (int)(M - tl.r0 < kTileM ? M - tl.r0 : kTileM);
-    tl.pos0 = tl.r0;
-    tiles[routed_tiles + i] = tl;
-  }
-  if (tid == 0) *ntiles = routed_tiles + nts;
-  // launch order: class c = 32-row blocks of a tile (full tiles 8, a group's
-  // last tile 1..9), classes from 9 down; the order inside a class is that
-  // of the LDS atomics (it decides which workgroup runs a tile, not what is
-  // computed); the shared expert's tiles after them as in the block map
-  if (tid < 10) s_cls[tid] = 0;
-  __syncthreads();
-  const int last_rows = nt > 0 ? total - (nt - 1) * kTileM : 0;
-  if (tid < E && nt > 0) {
-    if (nt > 1) atomicAdd(&s_cls[8], nt - 1);
-    atomicAdd(&s_cls[(last_rows + 31) >> 5], 1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int c = 9; c >= 1; --c) {
-      const int v = s_cls[c];
-      s_cls[c] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  if (tid < E && nt > 0) {
-    const int f = nt > 1 ? atomicAdd(&s_cls[8], nt - 1) : 0;
-    for (int i = 0; i < nt - 1; ++i) tiles_lpt[f + i] = Tile{tid, i * kTileM, kTileM, off + i * kTileM};
-    const int r0 = (nt - 1) * kTileM;
-    tiles_lpt[atomicAdd(&s_cls[(last_rows + 31) >> 5], 1)] = Tile{tid, r0, last_rows, off + r0};
-  }
-  for (int i = tid; i < nts; i += 1024) {
-    Tile tl;
-    tl.g = E;
-    tl.r0 = i * kTileM;
-    tl.rows = (int)(M - tl.r0 < kTileM ? M - tl.r0 : kTileM);
-    tl.pos0 = tl.r0;
-    tiles_lpt[routed_tiles + i] = tl;
-  }
+  write_block_map(tid < E ? total : 0, off, routed_total, counts, offsets, tiles, ntiles, tiles_lpt, s_wave, s_cls, M,
+                  E, shared);
   // pass 2: chunk bases.  s_part[part*E + e] -> start of the part within expert e
   __syncthreads();
   if (tid < E) {
@@ -351,6 +366,101 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
   }
 }
 
+// ------------------------------------------------------------------ scan + scatter in one launch
+
+// One 1024-thread workgroup per 64-token chunk c, for calls of at most
+// kFusedScanChunks chunks.  Every workgroup counts the assignments of every
+// (chunk, expert) mask: the group offsets need all of them and chunk c's
+// base in expert e's group is offset(e) plus the assignments to e of the
+// chunks before c.  Then it scatters chunk c's assignments (the arithmetic
+// of k_route_scatter); workgroup 0 also writes counts, offsets and the block
+// map.  This replaces the single-workgroup scan and the scatter launch: the
+// masks (128 KB at 4096 tokens) are read by every workgroup from the L2
+// instead of twice by one workgroup.
+constexpr int kFusedScanChunks = 128;
+constexpr int kFusedScanBatch = 16;  // mask loads in flight per thread
+__global__ __launch_bounds__(1024) void k_route_scan_scatter(const int32_t* __restrict__ ids,
+                                                             const uint64_t* __restrict__ cmask,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             Tile* __restrict__ tiles,
+                                                             int32_t* __restrict__ ntiles,
+                                                             Tile* __restrict__ tiles_lpt,
+                                                             int32_t* __restrict__ perm,
+                                                             int32_t* __restrict__ inv, int64_t M, int E, int k,
+                                                             int shared) {
+  __shared__ int s_tot[1024];       // per (part, expert): assignments in the part's chunks
+  __shared__ int s_pre[1024];       // per (part, expert): the same, chunks before c only
+  __shared__ uint64_t s_cm[kMaxE];  // chunk c's mask per expert
+  __shared__ int s_base[kMaxE];     // chunk c's first position in each expert's group
+  __shared__ int s_wave[40];
+  __shared__ int s_cls[10];
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x;
+  const int nchunk = (int)((M + kChunk - 1) / kChunk);
+  const int P = 1024 / E;  // threads per expert (E <= 1024)
+  const int e = tid % E, part = tid / E;
+  const bool active = part < P;
+  const int cpp = (nchunk + P - 1) / P;
+  const int c0 = active ? part * cpp : 0;
+  const int c1 = active ? (c0 + cpp < nchunk ? c0 + cpp : nchunk) : 0;
+
+  // this thread's assignments of chunk c (at most two: 64 tokens x k <= 2048),
+  // their experts loaded before the masks
+  int my_a[2], my_e[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = tid + 1024 * r;
+    const int tl = idx & (kChunk - 1), j = idx >> 6;
+    const int64_t t = (int64_t)c * kChunk + tl;
+    const bool ok = j < k && t < M;
+    my_a[r] = ok ? (int)(t * k + j) : -1;
+    my_e[r] = ok ? ids[t * k + j] : 0;
+  }
+
+  int tot = 0, pre = 0;
+  for (int cc = c0; cc < c1; cc += kFusedScanBatch) {
+    uint64_t v[kFusedScanBatch];
+#pragma unroll
+    for (int j = 0; j < kFusedScanBatch; ++j) {
+      const int ch = cc + j < c1 ? cc + j : c1 - 1;  // clamped: never past the part
+      v[j] = cmask[(int64_t)ch * E + e];
+    }
+#pragma unroll
+    for (int j = 0; j < kFusedScanBatch; ++j) {
+      if (cc + j >= c1) break;
+      const int pc = __popcll(v[j]);
+      tot += pc;
+      if (cc + j < c) pre += pc;
+      if (cc + j == c) s_cm[e] = v[j];
+    }
+  }
+  s_tot[tid] = active ? tot : 0;
+  s_pre[tid] = active ? pre : 0;
+  __syncthreads();
+  int total = 0, before = 0;
+  if (tid < E)
+    for (int p = 0; p < P; ++p) {
+      total += s_tot[p * E + tid];
+      before += s_pre[p * E + tid];
+    }
+  int routed_total;
+  const int off = block_exclusive_scan(tid < E ? total : 0, s_wave, &routed_total);
+  if (tid < E) s_base[tid] = off + before;
+  if (blockIdx.x == 0)  // uniform in the workgroup
+    write_block_map(tid < E ? total : 0, off, routed_total, counts, offsets, tiles, ntiles, tiles_lpt, s_wave, s_cls,
+                    M, E, shared);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (my_a[r] < 0) continue;
+    const int tl = (tid + 1024 * r) & (kChunk - 1);
+    const int p = s_base[my_e[r]] + __popcll(s_cm[my_e[r]] & ((1ull << tl) - 1ull));
+    perm[p] = my_a[r];
+    inv[my_a[r]] = p;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, float* L,
@@ -374,6 +484,16 @@ hipError_t launch_route_scan(const uint64_t* cmask, int32_t* cbase, int32_t* cou
                              const Launch& lc) {
   return launch(lc, k_route_scan, dim3(1), dim3(1024), cmask, cbase, counts, offsets, tiles, ntiles, tiles_lpt, M,
                 E, k, shared ? 1 : 0);
+}
+
+bool route_scan_fused(int64_t M) { return (M + kChunk - 1) / kChunk <= kFusedScanChunks; }
+
+hipError_t launch_route_scan_scatter(const int32_t* ids, const uint64_t* cmask, int32_t* counts, int32_t* offsets,
+                                     Tile* tiles, int32_t* ntiles, Tile* tiles_lpt, int32_t* perm, int32_t* inv,
+                                     int64_t M, int E, int k, bool shared, const Launch& lc) {
+  dim3 grid((unsigned)((M + kChunk - 1) / kChunk));
+  return launch(lc, k_route_scan_scatter, grid, dim3(1024), ids, cmask, counts, offsets, tiles, ntiles, tiles_lpt, perm,
+                inv, M, E, k, shared ? 1 : 0);
 }
 
 hipError_t launch_route_scatter(const int32_t* ids, const uint64_t* cmask, const int32_t* cbase,

@@ -35,7 +35,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 KERNELS = {1: "router_scores", 2: "topk", 3: "route_scan", 4: "route_scatter", 5: "gemm_gateup",
            6: "gemm_down", 7: "combine", 8: "dec_router", 9: "dec_gateup", 10: "dec_down",
            11: "sm_router", 12: "sm_topk", 13: "sm_gateup", 14: "sm_down", 15: "dec_route", 16: "dec_experts",
-           17: "shared_down_combine"}
+           17: "shared_down_combine", 18: "route_scan_scatter"}
 
 
 class MoeDesc(ctypes.Structure):

@@ -129,3 +129,24 @@ def test_block_map_hot_and_edge(M, E, k, shared):
     orc = O.moe_forward(x, r, ex, s, k, 64, bias=bias, I_shared=Is)
     rel = O.rel_err_per_token(g["out"], orc["out"])
     assert rel.max() <= 1e-2, rel.max()
+
+
+@pytest.mark.parametrize("M,E,k,shared", [(8192, 16, 2, True), (8193, 16, 2, False), (8256, 8, 3, True),
+                                          (4097, 256, 8, False)])
+def test_routing_tables_both_scan_forms(M, E, k, shared):
+    """Calls of up to 8192 tokens scan, build the block map and scatter in one launch (one
+    workgroup per 64-token chunk), longer ones in two (one workgroup scans, then a scatter):
+    on each side of that boundary, with a ragged last chunk, the counts, offsets, permutation
+    and block map equal the oracle's routing tables (ids bit-exact, near-ties aside)."""
+    Is = 64 if shared else 0
+    x, r, ex, s, _ = rand_case(M, 128, E, k, 64, Is, seed=M + E)
+    g, cap = run_blockmap(upload(x), upload(r), upload(ex), upload(s) if shared else None, k, I=64, Is=Is)
+    check_blockmap(g, cap, M, k, shared)
+    L32 = O.selection_logits(O.router_logits(x, r))
+    ids = O.topk_ids(L32, k)
+    flagged = O.near_tie_flags(L32, k)
+    assert np.array_equal(g["topk_ids"][~flagged], ids[~flagged])
+    if not flagged.any():
+        counts, offsets, perm, _ = O.route_tables(ids, E)
+        assert np.array_equal(g["counts"], counts) and np.array_equal(g["offsets"], offsets)
+        assert np.array_equal(g["perm"], perm)
