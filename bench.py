@@ -227,22 +227,34 @@ def round_sizes(total: int, rounds: int = ROUNDS):
     return [total // r + (1 if i < total % r else 0) for i in range(r)]
 
 
-def timed_rounds(step, total, between=None, rounds=ROUNDS):
+REWARM = 3  # untimed calls before a round that follows the CPU oracle's arm
+
+
+def timed_rounds(step, total, between=None, rounds=ROUNDS, sync=None, event=None):
     """Times exactly `total` calls of step(i) in rounds, each bracketed by a device synchronisation
     and timed with events on the current stream; between(r) runs after round r, untimed (the CPU
-    oracle's arm of the same leg).  Returns the per-round milliseconds per call."""
+    oracle's arm of the same leg), and is followed by REWARM untimed calls of step(0) before the
+    next round: after a second or more of host work the device has dropped its clocks and the
+    host's BLAS threads are still spinning, which would otherwise be charged to the first steps of
+    the round.  Returns the per-round milliseconds per call."""
     import torch
+    sync = sync or torch.cuda.synchronize
+    event = event or (lambda: torch.cuda.Event(enable_timing=True))
     per = []
     i = 0
-    for r, n in enumerate(round_sizes(total, rounds)):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
+    sizes = round_sizes(total, rounds)
+    for r, n in enumerate(sizes):
+        if r > 0 and between is not None:
+            for _ in range(REWARM):
+                step(0)
+        e0, e1 = event(), event()
+        sync()
         e0.record()
         for _ in range(n):
             step(i)
             i += 1
         e1.record()
-        torch.cuda.synchronize()
+        sync()
         per.append(e0.elapsed_time(e1) / n)
         if between is not None:
             between(r)

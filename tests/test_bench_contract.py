@@ -65,3 +65,33 @@ def test_rounds_cover_exactly_the_steps(total):
     """The timed steps are split into at most 5 rounds that together run exactly `total` steps."""
     sizes = bench.round_sizes(total)
     assert sum(sizes) == total and len(sizes) == min(5, total) and max(sizes) - min(sizes) <= 1
+
+
+def test_rounds_rewarm_after_the_cpu_arm_untimed():
+    """With a CPU arm between rounds, each later round is preceded by REWARM untimed calls; the
+    timed calls are exactly `total`, and none of the re-warm calls falls inside a timed round."""
+    log = []
+
+    class Ev:
+        def record(self):
+            log.append("rec")
+
+        def elapsed_time(self, other):
+            return 1.0
+
+    bench.timed_rounds(lambda i: log.append(("step", i)), 23, between=lambda r: log.append("cpu"),
+                       sync=lambda: log.append("sync"), event=Ev)
+    steps = [e for e in log if isinstance(e, tuple)]
+    assert len(steps) == 23 + bench.REWARM * (len(bench.round_sizes(23)) - 1)
+    # inside each timed round (between the two event records) only timed steps run
+    timed, inside, rounds = 0, False, 0
+    for e in log:
+        if e == "rec":
+            inside = not inside
+            rounds += not inside
+        elif isinstance(e, tuple) and inside:
+            timed += 1
+        elif e == "cpu":
+            assert not inside
+    assert timed == 23 and rounds == len(bench.round_sizes(23))
+    assert [i for _, i in steps if True][:5] == list(range(5))
