@@ -227,26 +227,37 @@ def round_sizes(total: int, rounds: int = ROUNDS):
     return [total // r + (1 if i < total % r else 0) for i in range(r)]
 
 
-REWARM = 3  # untimed calls before a round that follows the CPU oracle's arm
+REWARM_MS = 25.0  # untimed device work after each CPU oracle arm (at least REWARM_MIN calls)
+REWARM_MIN = 3
 
 
-def timed_rounds(step, total, between=None, rounds=ROUNDS, sync=None, event=None):
+def rewarm(step, sync, ms=REWARM_MS):
+    """Untimed calls of step(0) until `ms` of wall time (synchronised every 8 calls, so that it
+    tracks device time) and at least REWARM_MIN calls have passed."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < REWARM_MIN or (time.perf_counter() - t0) * 1e3 < ms:
+        step(0)
+        n += 1
+        if n % 8 == 0:
+            sync()
+    sync()
+    return n
+
+
+def timed_rounds(step, total, between=None, rounds=ROUNDS, sync=None, event=None, rewarm_ms=REWARM_MS):
     """Times exactly `total` calls of step(i) in rounds, each bracketed by a device synchronisation
     and timed with events on the current stream; between(r) runs after round r, untimed (the CPU
-    oracle's arm of the same leg), and is followed by REWARM untimed calls of step(0) before the
-    next round: after a second or more of host work the device has dropped its clocks and the
-    host's BLAS threads are still spinning, which would otherwise be charged to the first steps of
-    the round.  Returns the per-round milliseconds per call."""
+    oracle's arm of the same leg), and is followed by untimed calls of step(0) for rewarm_ms: a
+    second or more of host work lets the device drop its clocks, and the ramp back would otherwise
+    be charged to the next round (and to whatever the caller times after the last one).  Returns
+    the per-round milliseconds per call."""
     import torch
     sync = sync or torch.cuda.synchronize
     event = event or (lambda: torch.cuda.Event(enable_timing=True))
     per = []
     i = 0
-    sizes = round_sizes(total, rounds)
-    for r, n in enumerate(sizes):
-        if r > 0 and between is not None:
-            for _ in range(REWARM):
-                step(0)
+    for r, n in enumerate(round_sizes(total, rounds)):
         e0, e1 = event(), event()
         sync()
         e0.record()
@@ -258,6 +269,7 @@ def timed_rounds(step, total, between=None, rounds=ROUNDS, sync=None, event=None
         per.append(e0.elapsed_time(e1) / n)
         if between is not None:
             between(r)
+            rewarm(step, sync, rewarm_ms)
     return per
 
 

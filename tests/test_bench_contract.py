@@ -68,8 +68,9 @@ def test_rounds_cover_exactly_the_steps(total):
 
 
 def test_rounds_rewarm_after_the_cpu_arm_untimed():
-    """With a CPU arm between rounds, each later round is preceded by REWARM untimed calls; the
-    timed calls are exactly `total`, and none of the re-warm calls falls inside a timed round."""
+    """With a CPU arm between rounds, each arm is followed by untimed re-warm calls (at least
+    REWARM_MIN); the timed calls are exactly `total`, numbered 0..total-1, and no re-warm call or
+    CPU arm falls inside a timed round."""
     log = []
 
     class Ev:
@@ -79,19 +80,24 @@ def test_rounds_rewarm_after_the_cpu_arm_untimed():
         def elapsed_time(self, other):
             return 1.0
 
+    nr = len(bench.round_sizes(23))
     bench.timed_rounds(lambda i: log.append(("step", i)), 23, between=lambda r: log.append("cpu"),
-                       sync=lambda: log.append("sync"), event=Ev)
+                       sync=lambda: log.append("sync"), event=Ev, rewarm_ms=0.0)
     steps = [e for e in log if isinstance(e, tuple)]
-    assert len(steps) == 23 + bench.REWARM * (len(bench.round_sizes(23)) - 1)
-    # inside each timed round (between the two event records) only timed steps run
-    timed, inside, rounds = 0, False, 0
+    assert len(steps) == 23 + bench.REWARM_MIN * nr
+    timed, inside, rounds, after_cpu = [], False, 0, None
     for e in log:
         if e == "rec":
             inside = not inside
             rounds += not inside
-        elif isinstance(e, tuple) and inside:
-            timed += 1
+        elif isinstance(e, tuple):
+            if inside:
+                timed.append(e[1])
+            else:
+                assert after_cpu is not None and e[1] == 0, "an untimed call before any CPU arm"
+                after_cpu += 1
         elif e == "cpu":
             assert not inside
-    assert timed == 23 and rounds == len(bench.round_sizes(23))
-    assert [i for _, i in steps if True][:5] == list(range(5))
+            assert after_cpu is None or after_cpu == bench.REWARM_MIN
+            after_cpu = 0
+    assert timed == list(range(23)) and rounds == nr and after_cpu == bench.REWARM_MIN
