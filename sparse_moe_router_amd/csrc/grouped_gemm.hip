@@ -124,7 +124,10 @@ __device__ __forceinline__ void barrier_only() {
 // rounded to nearest even), as an MFMA operand fragment.
 __device__ __forceinline__ u32x4_t dequant8(uint32_t c, uint32_t g) {
   const float s = bf16_lo(g), b = bf16_hi(g);
-  const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;  // elements 0,2,4,6 / 1,3,5,7
+  uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;  // elements 0,2,4,6 / 1,3,5,7
+  // opaque to the compiler: each byte j then converts with one v_cvt_f32_ubyte<j>, instead of
+  // a bit-field extract of the nibble from c and a conversion per element
+  asm("" : "+v"(lo), "+v"(hi));
   u32x4_t r;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
