@@ -121,3 +121,44 @@ def test_small_route_matches_forward():
     torch.cuda.synchronize()
     for k, v in rb.items():
         assert np.array_equal(v.cpu().numpy(), g[k]), k
+
+
+# ------------------------------------------------------------------ batches of 2 to 4 rows
+
+def test_few_row_pieces_match_larger_batch_bitwise():
+    """A 3-row and a 4-row batch equal the same rows of a 16-row batch bit for bit, and each of
+    the 4 rows equals the one-row decode path on it."""
+    w = S.reduced(S.DECODE, E=64, k=8)
+    x, r, ex, sh = device_layer(w, 3, x_rows=16)
+    a = moe.forward(x, r, ex, sh, w.k, flags=GEMV).clone()
+    b3 = moe.forward(x[:3].contiguous(), r, ex, sh, w.k, flags=GEMV).clone()
+    b4 = moe.forward(x[3:7].contiguous(), r, ex, sh, w.k, flags=GEMV).clone()
+    assert torch.equal(b3.view(torch.int16), a[:3].view(torch.int16))
+    assert torch.equal(b4.view(torch.int16), a[3:7].view(torch.int16))
+    for t in range(3, 7):
+        one = moe.forward(x[t:t + 1].contiguous(), r, ex, sh, w.k)
+        assert torch.equal(one.view(torch.int16), b4[t - 3:t - 2].view(torch.int16)), f"row {t}"
+
+
+@pytest.mark.parametrize("M,E,k", [(4, 1000, 8), (4, 64, 32), (3, 1, 1), (2, 300, 8)])
+def test_few_rows_expert_counts_and_top32(M, E, k):
+    """The widest selections (E up to 1000, k = 32) and the smallest union (one expert) on a few rows."""
+    edge_case(M, 128, E, k, 64, 64, flags=GEMV, seed=7 * M + E + k)
+
+
+def test_few_rows_hot_expert_and_ties():
+    g, _ = edge_case(4, 256, 32, 4, 64, 64, flags=GEMV, hot=5, seed=8)
+    assert (g["topk_ids"][:, 0] == 5).all()
+    g, _ = edge_case(3, 256, 16, 4, 64, 0, flags=GEMV, zero_router=True)
+    assert (g["topk_ids"] == np.arange(4)[None, :]).all()
+
+
+def test_few_rows_route_matches_forward():
+    w = S.reduced(S.DECODE, E=64, k=8)
+    x, r, ex, sh = device_layer(w, 0, x_rows=3)
+    g = run_gpu(x, r, ex, sh, w.k, flags=GEMV)
+    rb = {k: torch.empty_like(torch.from_numpy(v)).cuda() for k, v in g.items() if k != "out"}
+    moe.route(x, r, w.k, rb, flags=GEMV, I=w.I, I_shared=w.I_shared)
+    torch.cuda.synchronize()
+    for k, v in rb.items():
+        assert np.array_equal(v.cpu().numpy(), g[k]), k
