@@ -87,13 +87,22 @@ def test_long_prefill_chunk():
     print("long chunk 5, all tokens", st)
 
 
+def _route_all_tokens(hl, M, step, k):
+    """The oracle's routing steps over all M token rows (scores in pieces of `step` rows)."""
+    L = np.concatenate([O.router_logits(hl.x(t, min(step, M - t)), hl.router, hl.bias)
+                        for t in range(0, M, step)])
+    L32 = O.selection_logits(L)
+    return L, L32, O.topk_ids(L32, k), O.near_tie_flags(L32, k)
+
+
 def test_long_prompt_single_call():
     """The 131,072-token prompt in one call (the largest configuration): bit-identical to the
-    same rows in 16 calls of 8,192, and sampled tokens against the oracle."""
+    same rows in 16 calls of 8,192; every token's scores, selection, weights and the
+    histogram / offsets / permutation against the oracle; sampled tokens' outputs against it."""
     w = S.LONG
     big = S.reduced(w, M=w.tokens, chunks=1)
     x, r, ex, sh = device_layer(big)
-    rb = routing_buffers(big.M, w.E, w.k, grouped=False)
+    rb = routing_buffers(big.M, w.E, w.k, grouped=True)
     one = moe.forward(x, r, ex, sh, w.k, routing=rb)
     chunked = torch.empty_like(x)
     for c in range(w.chunks):
@@ -101,11 +110,26 @@ def test_long_prompt_single_call():
     torch.cuda.synchronize()
     assert torch.equal(one.view(torch.int16), chunked.view(torch.int16)), "one call != 16 chunks"
     del ex, chunked
+    hl = HostLayer(big)
+    # routing of all 131,072 tokens: the same rules as check(), over the whole call
+    L, L32, ids_o, flagged = _route_all_tokens(hl, big.M, w.M, w.k)
+    ids_g = rb["topk_ids"].cpu().numpy().astype(np.int64)
+    diff = (ids_g != ids_o).any(axis=1)
+    assert not (diff & ~flagged).any(), f"ids differ on {(diff & ~flagged).sum()} unflagged tokens"
+    assert O.valid_topk(L32[diff], ids_g[diff]).all(), "invalid top-k at flagged tokens"
+    assert np.abs(rb["logits"].cpu().numpy().astype(np.float64) - L).max() < 1e-4, "router scores"
+    werr = np.abs(rb["topk_w"].cpu().numpy().astype(np.float64) - O.topk_weights(L, ids_g)).max()
+    assert werr <= 1e-5, f"routing weights differ by {werr}"
+    counts, offsets, perm, _ = O.route_tables(ids_g, w.E)
+    for name, want in (("counts", counts), ("offsets", offsets), ("perm", perm)):
+        assert np.array_equal(rb[name].cpu().numpy(), want), name
+    print("long prompt one call, routing of all tokens: flagged", int(flagged.sum()), "swapped",
+          int(diff.sum()), "max group", int(counts.max()), "w err", werr)
+    del L, L32
     rng = np.random.default_rng(17)
     sample = sorted(set(rng.choice(big.M, 6, replace=False).tolist()) | {0, big.M - 1})
-    hl = HostLayer(big)
     xs = np.concatenate([hl.x(t, 1) for t in sample])
-    g = {n: t[sample].cpu().numpy() for n, t in rb.items()}
+    g = {n: rb[n][sample].cpu().numpy() for n in ("topk_ids", "topk_w", "logits")}
     g["out"] = one[sample].float().cpu().numpy()
     hl.prefetch(g["topk_ids"].ravel())
     st = check(g, oracle_fn(hl, xs), w.k, w.E, grouped=False, label="long prompt, one call")
