@@ -220,6 +220,13 @@ def test_expert_counts(E):
     _edge(1, 128, E, 8, 64, 64, seed=E + 1)
 
 
+@pytest.mark.parametrize("M", [1, 4, 80])
+def test_max_experts(M):
+    """E at the supported maximum (1024, sixteen scores per lane in the top-k) on the decode,
+    small-batch and grouped paths."""
+    _edge(M, 128, 1024, 8, 64, 64, seed=1024 + M)
+
+
 def test_shared_size_differs():
     _edge(90, 256, 16, 2, 128, 256, seed=5)
     _edge(90, 256, 16, 2, 256, 64, seed=6)

@@ -192,6 +192,12 @@ def test_q4_many_experts_and_top32():
     _edge_q4(20, 128, 64, 32, 64, 64, seed=8)
 
 
+@pytest.mark.parametrize("M", [1, 4, 80])
+def test_q4_max_experts(M):
+    """E at the supported maximum (1024) on the decode, small-batch and grouped paths."""
+    _edge_q4(M, 128, 1024, 8, 64, 64, seed=2048 + M)
+
+
 # ------------------------------------------------------------------ small-batch path (4-bit experts)
 
 def test_q4_small_decode_shape():
