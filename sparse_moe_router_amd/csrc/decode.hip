@@ -59,14 +59,19 @@ __device__ __forceinline__ void wave_dots(const uint16_t* __restrict__ x, const 
   if (TWO) *d2 = wave_sum(a2);
 }
 
-// Router scores: one wave per expert.
+// Router scores: one wave per expert; with ROWS, grid row r works on token row r.
+template <bool ROWS>
 __global__ __launch_bounds__(256) void k_dec_router(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ wr,
                                                     const float* __restrict__ bias,
                                                     float* __restrict__ logits, int32_t* __restrict__ status,
                                                     int H, int E) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (status && blockIdx.x == 0 && threadIdx.x == 0) *status = 0;  // three launches: no waits
+  if (status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;  // three launches: no waits
+  if (ROWS) {
+    x += (int64_t)blockIdx.y * H;
+    logits += (int64_t)blockIdx.y * E;
+  }
   const int e = blockIdx.x * 4 + wave;
   if (e >= E) return;
   float v, unused;
@@ -81,8 +86,9 @@ __global__ __launch_bounds__(256) void k_dec_router(const uint16_t* __restrict__
 // workgroups select: there wave 0 takes the top k of the E scores into LDS,
 // then wave w computes row i = 4*(b % row_blocks) + w of slot j's expert.
 // The first routed workgroup also publishes ids / weights.  With I == 0 only
-// the selection runs.
-template <int EPL, class W>
+// the selection runs.  With ROWS, grid row r works on token row r (h_r:
+// [rows][k][I], h_s: [rows][Is]).
+template <int EPL, class W, bool ROWS>
 __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__ x, const W expert_w,
                                                     const W shared_w, const float* __restrict__ logits,
                                                     int32_t* __restrict__ ids,
@@ -92,6 +98,15 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
   __shared__ int32_t s_ids[kMaxTopK];
   __shared__ uint64_t s_keys[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (ROWS) {
+    const int64_t row = blockIdx.y;
+    x += row * H;
+    logits += row * E;
+    ids += row * k;
+    wts += row * k;
+    h_r += row * k * I;
+    h_s += row * Is;
+  }
   if ((int)blockIdx.x < nshared) {
     const int i = blockIdx.x * 4 + wave;
     if (i >= Is) return;
@@ -135,8 +150,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
 // Workgroup = one wave per expert slot (slot k = shared expert), DR output
 // rows each; every wave loads its DR weight rows and its h slice at once,
 // reduces, and the slot partials are summed in slot order through LDS.
+// With ROWS, grid row r works on token row r.
 constexpr int DR = 4;
-template <class W>
+template <class W, bool ROWS>
 __global__ __launch_bounds__(1024) void k_dec_down(const W expert_w, const W shared_w,
                                                    const int32_t* __restrict__ ids,
                                                    const float* __restrict__ wts,
@@ -148,6 +164,14 @@ __global__ __launch_bounds__(1024) void k_dec_down(const W expert_w, const W sha
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c0 = blockIdx.x * DR;
+  if (ROWS) {
+    const int64_t row = blockIdx.y;
+    ids += row * k;
+    wts += row * k;
+    h_r += row * k * I;
+    h_s += row * Is;
+    out += row * H;
+  }
   // slots wave, wave + nwaves, ... (one pass when k + 1 <= waves per workgroup)
   for (int j = wave; j < nslot; j += blockDim.x >> 6) {
     const bool sh = j == k;  // the shared expert
@@ -427,10 +451,26 @@ __global__ __launch_bounds__(512) void k_dec_experts(const uint16_t* __restrict_
 
 hipError_t launch_decode_router(const uint16_t* x, const uint16_t* wr, const float* bias, float* logits,
                                 int32_t* status, const Plan& p, const Launch& lc) {
-  return launch(lc, k_dec_router, dim3((p.E + 3) / 4), dim3(256), x, wr, bias, logits, status, p.H, p.E);
+  const dim3 g((p.E + 3) / 4, (unsigned)p.M);
+  if (p.M > 1) return launch(lc, k_dec_router<true>, g, dim3(256), x, wr, bias, logits, status, p.H, p.E);
+  return launch(lc, k_dec_router<false>, g, dim3(256), x, wr, bias, logits, status, p.H, p.E);
 }
 
 namespace {
+
+template <class W, bool ROWS>
+hipError_t decode_gateup_launch(dim3 g, dim3 b, const uint16_t* x, const W ew, const W sw, const float* logits,
+                                int32_t* ids, float* w, float* h_dec, float* h_s, int nshared, const Plan& p,
+                                const Launch& lc) {
+#define MOE_DEC_GATEUP(EPL) \
+  launch(lc, k_dec_gateup<EPL, W, ROWS>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared)
+  if (p.E <= 64) return MOE_DEC_GATEUP(1);
+  if (p.E <= 128) return MOE_DEC_GATEUP(2);
+  if (p.E <= 256) return MOE_DEC_GATEUP(4);
+  if (p.E <= 512) return MOE_DEC_GATEUP(8);
+  return MOE_DEC_GATEUP(16);
+#undef MOE_DEC_GATEUP
+}
 
 template <class W>
 hipError_t decode_gateup(const uint16_t* x, const W ew, const W sw, const float* logits, int32_t* ids, float* w,
@@ -438,24 +478,22 @@ hipError_t decode_gateup(const uint16_t* x, const W ew, const W sw, const float*
   // p.I == 0 requests the selection only (routing without expert work)
   const int nshared = p.shared && p.I > 0 ? (p.Is + 3) / 4 : 0;
   const int blocks = nshared + (p.I > 0 ? p.k * ((p.I + 3) / 4) : 1);
-  float* h_s = h_dec + (int64_t)p.k * p.I;
-  const dim3 g(blocks), b(256);
-  if (p.E <= 64) return launch(lc, k_dec_gateup<1, W>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
-  if (p.E <= 128) return launch(lc, k_dec_gateup<2, W>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
-  if (p.E <= 256) return launch(lc, k_dec_gateup<4, W>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
-  if (p.E <= 512) return launch(lc, k_dec_gateup<8, W>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
-  return launch(lc, k_dec_gateup<16, W>, g, b, x, ew, sw, logits, ids, w, h_dec, h_s, p.H, p.E, p.I, p.Is, p.k, nshared);
+  float* h_s = h_dec + p.M * p.k * p.I;
+  const dim3 g(blocks, (unsigned)p.M), b(256);
+  if (p.M > 1) return decode_gateup_launch<W, true>(g, b, x, ew, sw, logits, ids, w, h_dec, h_s, nshared, p, lc);
+  return decode_gateup_launch<W, false>(g, b, x, ew, sw, logits, ids, w, h_dec, h_s, nshared, p, lc);
 }
 
 template <class W>
 hipError_t decode_down(const W ew, const W sw, const int32_t* ids, const float* w, const float* h_dec,
                        uint16_t* out, const Plan& p, const Launch& lc) {
   const float* h_r = h_dec;
-  const float* h_s = h_dec + (int64_t)p.k * p.I;
+  const float* h_s = h_dec + p.M * p.k * p.I;
   const int nslot = p.k + (p.shared ? 1 : 0);
   const int waves = nslot < 16 ? nslot : 16;
-  return launch(lc, k_dec_down<W>, dim3((p.H + DR - 1) / DR), dim3(64 * waves), ew, sw, ids, w, h_r, h_s, out,
-                p.H, p.I, p.Is, p.k, nslot);
+  const dim3 g((p.H + DR - 1) / DR, (unsigned)p.M), b(64 * waves);
+  if (p.M > 1) return launch(lc, k_dec_down<W, true>, g, b, ew, sw, ids, w, h_r, h_s, out, p.H, p.I, p.Is, p.k, nslot);
+  return launch(lc, k_dec_down<W, false>, g, b, ew, sw, ids, w, h_r, h_s, out, p.H, p.I, p.Is, p.k, nslot);
 }
 
 }  // namespace

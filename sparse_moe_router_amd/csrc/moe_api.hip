@@ -380,7 +380,7 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   const uint16_t* xb = (const uint16_t*)x;
   int32_t* status = routing ? routing->wait_status : nullptr;
   hipError_t e;
-  if (gemv && p.M > 1) {
+  if (gemv && p.M > kDecodeRows) {
     float* L = (routing && routing->logits) ? routing->logits : ws_ptr<float>(workspace, p.logits);
     int32_t* ids = (routing && routing->topk_ids) ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
     float* w = (routing && routing->topk_w) ? routing->topk_w : ws_ptr<float>(workspace, p.w);
@@ -410,7 +410,7 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
     int32_t* ids = (routing && routing->topk_ids) ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
     float* w = (routing && routing->topk_w) ? routing->topk_w : ws_ptr<float>(workspace, p.w);
     float* h = ws_ptr<float>(workspace, p.h_r);
-    if ((d->flags & MOE_FLAG_DECODE_TWO_LAUNCH) && decode_two_launch_fits(p)) {
+    if (p.M == 1 && (d->flags & MOE_FLAG_DECODE_TWO_LAUNCH) && decode_two_launch_fits(p)) {
       uint32_t* arr = ws_ptr<uint32_t>(workspace, p.arrive);
       const int probe = (d->flags & MOE_FLAG_WAIT_PROBE) ? 1 : 0;
       if ((e = tr.run(MOE_K_DEC_ROUTE, [&](const Launch& lc) {
@@ -570,7 +570,7 @@ moe_status_t moe_route(const moe_desc_t* d, const void* x, const void* router_w,
     int32_t* ids = routing->topk_ids ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
     float* w = routing->topk_w ? routing->topk_w : ws_ptr<float>(workspace, p.w);
     hipError_t e;
-    if (p.M > 1) {
+    if (p.M > kDecodeRows) {
       if ((e = launch_small_router((const uint16_t*)x, (const uint16_t*)router_w, d->router_bias, L,
                                    routing->wait_status, p, Launch{s, nullptr, nullptr})) != hipSuccess)
         return hip_fail(e);
