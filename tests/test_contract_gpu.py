@@ -49,7 +49,7 @@ def _call(x, r, wts, flags, out, ws, stream=None):
 
 
 @pytest.mark.parametrize("kind", ["bf16", "tiled", "q4"])
-@pytest.mark.parametrize("M", [1, 8, 300, 8200, -1])  # -1: one row on the two-launch decode path
+@pytest.mark.parametrize("M", [1, 3, 8, 300, 8200, -1])  # -1: one row on the two-launch decode path
 def test_graph_replay_matches_eager(kind, M):
     r, wts, flags = _weights(kind)
     if M == -1:
@@ -106,14 +106,15 @@ def test_two_streams_two_workspaces(M):
         assert torch.equal(outs_b[i].view(torch.int16), ref_b.view(torch.int16)), f"stream b call {i}"
 
 
-# moe_kernel_t ids; grouped calls of more than 8192 tokens scan and scatter in two launches
-PATH_KERNELS = {1: [8, 9, 10], 8: [11, 12, 13, 14], 300: [1, 2, 18, 5, 6, 17], 8200: [1, 2, 3, 4, 5, 6, 17],
-                -1: [15, 16]}
+# moe_kernel_t ids; calls of up to 4 rows run the decode kernels; grouped calls of more than
+# 8192 tokens scan and scatter in two launches
+PATH_KERNELS = {1: [8, 9, 10], 3: [8, 9, 10], 8: [11, 12, 13, 14], 300: [1, 2, 18, 5, 6, 17],
+                8200: [1, 2, 3, 4, 5, 6, 17], -1: [15, 16]}
 TWO = moe.FLAG_DECODE_TWO_LAUNCH
 
 
 @pytest.mark.parametrize("kind", ["bf16", "q4"])
-@pytest.mark.parametrize("M", [1, 8, 300, 8200, -1])  # -1: one row on the two-launch decode path
+@pytest.mark.parametrize("M", [1, 3, 8, 300, 8200, -1])  # -1: one row on the two-launch decode path
 def test_traced_call_matches_and_records_kernels(kind, M):
     """With a trace the call gives the bits of the untraced call and records each kernel of its
     path once, in launch order, with a finite duration; with a trace shorter than the path the
