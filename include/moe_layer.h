@@ -88,10 +88,10 @@ typedef enum {
   MOE_ERR_HIP = 5                  /* a HIP launch failed */
 } moe_status_t;
 
-/* Path selection.  1 <= M <= 4: the decode path, each token row through its
- * own selected experts (for M > 1 the decode kernels run one grid row per
- * token row; an expert two rows select is read for each).  5 <= M <= 64: the
- * small-batch path, matrix-vector products over the union of the experts the
+/* Path selection.  1 <= M <= 4 (8 with 4-bit experts): the decode path, each
+ * token row through its own selected experts (for M > 1 the decode kernels
+ * run one grid row per token row; an expert two rows select is read for
+ * each).  Up to M <= 64: the small-batch path, matrix-vector products over the union of the experts the
  * rows select, each expert's weights read once for all rows routed to it
  * (section "Limits of further optimization": few-row batches pick different
  * experts).  Both give every row the bits of a one-row call.  By default the

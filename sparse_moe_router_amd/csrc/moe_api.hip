@@ -380,7 +380,7 @@ moe_status_t forward_impl(const moe_desc_t* d, const void* x, const void* router
   const uint16_t* xb = (const uint16_t*)x;
   int32_t* status = routing ? routing->wait_status : nullptr;
   hipError_t e;
-  if (gemv && p.M > kDecodeRows) {
+  if (gemv && p.M > (wt.q4 ? kDecodeRowsQ4 : kDecodeRows)) {
     float* L = (routing && routing->logits) ? routing->logits : ws_ptr<float>(workspace, p.logits);
     int32_t* ids = (routing && routing->topk_ids) ? routing->topk_ids : ws_ptr<int32_t>(workspace, p.ids);
     float* w = (routing && routing->topk_w) ? routing->topk_w : ws_ptr<float>(workspace, p.w);
