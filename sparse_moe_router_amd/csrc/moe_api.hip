@@ -13,6 +13,11 @@ namespace moe {
 
 namespace {
 
+// Matrix-vector calls of up to kDecodeRows rows (bf16 experts) run the decode
+// kernels, one grid row per token row; with 4-bit experts, whose rows cost a
+// quarter as much to read once per row, up to kDecodeRowsQ4.
+constexpr int kDecodeRowsQ4 = 8;
+
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // place `bytes` at the running offset; false on overflow

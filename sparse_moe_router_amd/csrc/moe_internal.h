@@ -16,10 +16,7 @@ constexpr int kTileM = 256;   // rows per grouped-GEMM tile (block-map granulari
 constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxSmallM = 64;  // most rows the matrix-vector paths take
-// matrix-vector calls of up to this many rows run the decode kernels, one grid row per token row
-// (bf16 experts; 4-bit experts, whose rows are 3.6x cheaper to read twice, up to kDecodeRowsQ4)
-constexpr int kDecodeRows = 4;
-constexpr int kDecodeRowsQ4 = 8;
+constexpr int kDecodeRows = 4;  // matrix-vector calls of up to this many rows run the decode kernels, one grid row per token
 constexpr int kSmallRows = 4;   // small-batch path: assignments per register batch / work unit
 constexpr int kArriveStride = 64;  // decode, two launches: one arrival counter per 256-byte line
 
