@@ -91,14 +91,14 @@ typedef enum {
 /* Path selection.  1 <= M <= 4 (8 with 4-bit experts): the decode path, each
  * token row through its own selected experts (for M > 1 the decode kernels
  * run one grid row per token row; an expert two rows select is read for
- * each).  Up to M <= 64: the small-batch path, matrix-vector products over the union of the experts the
- * rows select, each expert's weights read once for all rows routed to it
- * (section "Limits of further optimization": few-row batches pick different
- * experts).  Both give every row the bits of a one-row call.  By default the
- * matrix-vector paths run when M <= 64 and M * top_k <= 4 * E (at most four
- * assignments per expert on average), the grouped path otherwise; the flags
- * override that choice.  Only the grouped path reports counts / offsets /
- * perm. */
+ * each).  Larger M up to 64: the small-batch path, matrix-vector products
+ * over the union of the experts the rows select, each expert's weights read
+ * once for all rows routed to it (section "Limits of further optimization":
+ * few-row batches pick different experts).  Both give every row the bits of
+ * a one-row call.  By default the matrix-vector paths run when M <= 64 and
+ * M * top_k <= 4 * E (at most four assignments per expert on average), the
+ * grouped path otherwise; the flags override that choice.  Only the grouped
+ * path reports counts / offsets / perm. */
 #define MOE_FLAG_FORCE_GEMV 0x1u /* matrix-vector paths; requires M <= 64 */
 #define MOE_FLAG_FORCE_GEMM 0x2u /* grouped (matrix-matrix) path, also at M == 1 */
 /* expert_w and shared_w are in the tiled layout written by moe_tile_weights
