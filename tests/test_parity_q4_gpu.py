@@ -192,6 +192,24 @@ def test_q4_many_experts_and_top32():
     _edge_q4(20, 128, 64, 32, 64, 64, seed=8)
 
 
+@pytest.mark.parametrize("M", [3, 6, 8])
+def test_q4_few_rows_route_matches_forward(M):
+    """4-bit calls of up to eight rows run the decode kernels (a grid row per token row); their
+    scores, selections and weights equal, bit for bit, those of the routing-only call, which takes
+    the small-batch router and selection above four rows, and each row equals a one-row call."""
+    w = S.reduced(S.DECODE, E=64, k=8)
+    x, r, ec, esb, sc, ssb = SD.layer_tensors_q4(w, 2, x_rows=M)
+    g = run_q4(x, r, ec, esb, sc, ssb, w.k, flags=moe.FLAG_FORCE_GEMV)
+    rb = {k: torch.empty_like(torch.from_numpy(v)).cuda() for k, v in g.items() if k != "out"}
+    moe.route(x, r, w.k, rb, flags=moe.FLAG_FORCE_GEMV, I=w.I, I_shared=w.I_shared)
+    torch.cuda.synchronize()
+    for name, v in rb.items():
+        assert np.array_equal(v.cpu().numpy(), g[name]), name
+    for t in (0, M - 1):
+        one = run_q4(x[t:t + 1].contiguous(), r, ec, esb, sc, ssb, w.k)
+        assert np.array_equal(one["out"], g["out"][t:t + 1]), f"row {t}"
+
+
 @pytest.mark.parametrize("M", [1, 4, 80])
 def test_q4_max_experts(M):
     """E at the supported maximum (1024) on the decode, small-batch and grouped paths."""
