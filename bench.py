@@ -504,7 +504,7 @@ def bench_decode(args, hip, moe, SD, S, peaks, q4=False, cpu=None):
 
 def bench_small(args, hip, moe, S, layers, xpool, Ms=(2, 4, 8, 16, 32, 64)):
     """Small batches of M token rows through the decode workload's layers: the matrix-vector
-    paths (FORCE_GEMV: the decode kernels for up to 4 rows (8 with 4-bit experts), the
+    paths (FORCE_GEMV: the decode kernels for up to 5 rows (8 with 4-bit experts), the
     small-batch kernels over the union of the selected experts above) beside the grouped path (FORCE_GEMM), both HIP-graph
     replayed.  Bytes = the union's expert weights + the shared expert + router + activations,
     from the routing the call itself produced (the minimum any path must read)."""

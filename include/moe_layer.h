@@ -88,7 +88,7 @@ typedef enum {
   MOE_ERR_HIP = 5                  /* a HIP launch failed */
 } moe_status_t;
 
-/* Path selection.  1 <= M <= 4 (8 with 4-bit experts): the decode path, each
+/* Path selection.  1 <= M <= 5 (8 with 4-bit experts): the decode path, each
  * token row through its own selected experts (for M > 1 the decode kernels
  * run one grid row per token row; an expert two rows select is read for
  * each).  Larger M up to 64: the small-batch path, matrix-vector products

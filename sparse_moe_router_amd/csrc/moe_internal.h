@@ -16,7 +16,6 @@ constexpr int kTileM = 256;   // rows per grouped-GEMM tile (block-map granulari
 constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxSmallM = 64;  // most rows the matrix-vector paths take
-constexpr int kDecodeRows = 4;  // matrix-vector calls of up to this many rows run the decode kernels, one grid row per token
 constexpr int kSmallRows = 4;   // small-batch path: assignments per register batch / work unit
 constexpr int kArriveStride = 64;  // decode, two launches: one arrival counter per 256-byte line
 

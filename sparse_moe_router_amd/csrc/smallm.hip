@@ -1,5 +1,5 @@
 // Small-batch path of the sparse MoE layer (up to 64 token rows; calls of up
-// to 4 rows, 8 with 4-bit experts, run the decode kernels instead): matrix-
+// to 5 rows, 8 with 4-bit experts, run the decode kernels instead): matrix-
 // vector work over the union of the experts the rows select (gfx950, wave64).
 //
 // "Optimizing on-device inference for Apple Silicon" (Perplexity 2026),

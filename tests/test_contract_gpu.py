@@ -106,7 +106,7 @@ def test_two_streams_two_workspaces(M):
         assert torch.equal(outs_b[i].view(torch.int16), ref_b.view(torch.int16)), f"stream b call {i}"
 
 
-# moe_kernel_t ids; calls of up to 4 rows (8 with 4-bit experts) run the decode kernels; grouped
+# moe_kernel_t ids; calls of up to 5 rows (8 with 4-bit experts) run the decode kernels; grouped
 # calls of more than 8192 tokens scan and scatter in two launches
 PATH_KERNELS = {1: [8, 9, 10], 3: [8, 9, 10], 8: [11, 12, 13, 14], 300: [1, 2, 18, 5, 6, 17],
                 8200: [1, 2, 3, 4, 5, 6, 17], -1: [15, 16]}
